@@ -1,0 +1,379 @@
+// chain_api.cpp -- the C ABI declared in include/mlp_chain.h: argument
+// checks, tile planning, workspace ownership, epochs and launches.
+//
+// Per-run synchronization state lives in the workspace and is never reset
+// between runs (no memset on the run path, so a run is a single kernel for
+// the fused policies):
+//   * the tile queue counter only grows; the host keeps the number of tickets
+//     all earlier runs drew (each run draws T1 + T2 + grid: every tile once and
+//     one exit ticket per workgroup) and passes it as the run's base;
+//   * tile flags hold the epoch of the run that last published them, and a
+//     consumer waits for (int32)(flag - epoch) >= 0;
+//   * row counters grow by N1t per run; a consumer of run e waits for
+//     (int32)(count - e * N1t) >= 0.
+// All of it is modular 32-bit arithmetic, so wrap-around is harmless.
+#include <hip/hip_runtime.h>
+
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+
+#include "../../include/mlp_chain.h"
+#include "chain_launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+constexpr uint32_t DEFAULT_SPIN_LIMIT = 1u << 20;   // ~1 s of polling with back-off
+constexpr uint32_t GROUP_M = 8;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+uint32_t cdiv(int64_t a, int64_t b) { return (uint32_t)((a + b - 1) / b); }
+
+// Planner: the smallest tiles while M is small (weight streaming wants many
+// workgroups), larger tiles when M grows and the matrix cores bound the run.
+int plan_config(int64_t M) {
+    if (M <= 32) return 0;
+    if (M <= 256) return 1;
+    return 2;
+}
+
+}  // namespace
+
+struct mlp_chain {
+    int64_t M, H, I;
+    int act, dtype, policy, gb;
+    int device;
+    int cus;
+    int cfg;
+    int forced_cfg;
+    CfgInfo ci;
+    uint32_t Mt, N1t, N2t, T1, T2;
+    int occ;        // persistent workgroups per CU
+    uint32_t grid;  // persistent grid
+    // workspace
+    void* ws;
+    size_t ws_bytes;
+    uint16_t* t;
+    uint32_t* flags;
+    uint32_t* rowcnt;
+    uint32_t* ticket;
+    uint32_t* status;
+    // run state
+    uint32_t epoch;
+    uint32_t ticket_base;
+    uint32_t spin_limit;
+    uint32_t skip_producer;
+    hipStream_t last_stream;
+};
+
+namespace {
+
+struct DeviceGuard {
+    int prev = -1;
+    bool ok = true;
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev) != hipSuccess) { ok = false; return; }
+        if (prev != dev && hipSetDevice(dev) != hipSuccess) ok = false;
+    }
+    ~DeviceGuard() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+// (Re)compute the tiling of a handle for configuration `cfg`.
+int apply_plan(mlp_chain* h, int cfg) {
+    const CfgInfo ci = mlpc_config_info(cfg);
+    if (ci.id < 0) return fail(MLP_EINVAL, "unknown tile configuration %d", cfg);
+    h->cfg = cfg;
+    h->ci = ci;
+    h->Mt = cdiv(h->M, ci.BM);
+    h->N1t = cdiv(h->I, ci.BN);
+    h->N2t = cdiv(h->H, ci.BN);
+    h->T1 = h->Mt * h->N1t;
+    h->T2 = h->Mt * h->N2t;
+    h->occ = 0;
+    h->grid = 0;
+    if (h->policy != MLP_POLICY_STREAM_ORDERED) {
+        int occ = 0;
+        hipError_t e = mlpc_persistent_occupancy(cfg, h->dtype, h->gb, h->policy, &occ);
+        if (e != hipSuccess) return fail(MLP_EHIP, "occupancy query failed: %s", hipGetErrorString(e));
+        if (occ < 1) return fail(MLP_EHIP, "persistent kernel of config %d does not fit on a CU", cfg);
+        h->occ = occ;
+        uint64_t g = (uint64_t)occ * (uint64_t)h->cus;
+        const uint64_t tiles = (uint64_t)h->T1 + h->T2;
+        if (g > tiles) g = tiles;
+        h->grid = (uint32_t)g;
+    }
+    return MLP_OK;
+}
+
+int zero_workspace(mlp_chain* h) {
+    hipError_t e = hipMemset(h->flags, 0, h->ws_bytes - ((char*)h->flags - (char*)h->ws));
+    if (e != hipSuccess) return fail(MLP_EHIP, "hipMemset failed: %s", hipGetErrorString(e));
+    e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail(MLP_EHIP, "hipDeviceSynchronize failed: %s", hipGetErrorString(e));
+    h->epoch = 0;
+    h->ticket_base = 0;
+    return MLP_OK;
+}
+
+bool bad_ptr(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) != 0; }
+
+mlpc::ChainArgs make_args(const mlp_chain* h, const void* x, const void* w1, const void* w2, void* out) {
+    mlpc::ChainArgs a{};
+    a.x = static_cast<const uint16_t*>(x);
+    a.w1 = static_cast<const uint16_t*>(w1);
+    a.w2 = static_cast<const uint16_t*>(w2);
+    a.t = h->t;
+    a.y = static_cast<uint16_t*>(out);
+    a.M = (int)h->M;
+    a.H = (int)h->H;
+    a.I = (int)h->I;
+    a.act = h->act;
+    a.Mt = h->Mt;
+    a.N1t = h->N1t;
+    a.N2t = h->N2t;
+    a.T1 = h->T1;
+    a.T2 = h->T2;
+    a.group_m = GROUP_M;
+    a.ticket = h->ticket;
+    a.flags = h->flags;
+    a.rowcnt = h->rowcnt;
+    a.status = h->status;
+    a.ticket_base = h->ticket_base;
+    a.epoch = h->epoch;
+    a.grid = h->grid;
+    a.spin_limit = h->spin_limit;
+    a.skip_producer = h->skip_producer;
+    a.policy = h->policy;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mlp_chain_last_error(void) { return g_err.c_str(); }
+
+mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype, int policy) {
+    g_err.clear();
+    if (M < 1 || H < 8 || I < 8) {
+        fail(MLP_EINVAL, "sizes must be M >= 1, H >= 8, I >= 8 (got M=%lld H=%lld I=%lld)",
+             (long long)M, (long long)H, (long long)I);
+        return nullptr;
+    }
+    if (H % 8 != 0 || I % 8 != 0) {
+        fail(MLP_EINVAL, "H and I must be multiples of 8 (16-byte rows), got H=%lld I=%lld",
+             (long long)H, (long long)I);
+        return nullptr;
+    }
+    const int64_t lim = (int64_t)1 << 30;
+    if (M * H >= lim || M * I >= lim || H * I * 2 >= lim || M >= (1 << 24)) {
+        fail(MLP_EINVAL, "sizes too large for 32-bit tile indexing (M=%lld H=%lld I=%lld)",
+             (long long)M, (long long)H, (long long)I);
+        return nullptr;
+    }
+    if (act < MLP_ACT_NONE || act > MLP_ACT_SWIGLU) {
+        fail(MLP_EINVAL, "unknown activation %d", act);
+        return nullptr;
+    }
+    if (dtype != MLP_DTYPE_F16 && dtype != MLP_DTYPE_BF16) {
+        fail(MLP_EINVAL, "unknown dtype %d", dtype);
+        return nullptr;
+    }
+    if (policy < MLP_POLICY_STREAM_ORDERED || policy > MLP_POLICY_TILE_SYNC) {
+        fail(MLP_EINVAL, "unknown policy %d", policy);
+        return nullptr;
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        fail(MLP_EHIP, "no HIP device: %s", hipGetErrorString(e));
+        return nullptr;
+    }
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) {
+        fail(MLP_EHIP, "hipGetDeviceProperties failed: %s", hipGetErrorString(e));
+        return nullptr;
+    }
+    mlp_chain* h = new (std::nothrow) mlp_chain();
+    if (!h) {
+        fail(MLP_ENOMEM, "out of host memory");
+        return nullptr;
+    }
+    h->M = M;
+    h->H = H;
+    h->I = I;
+    h->act = act;
+    h->dtype = dtype;
+    h->policy = policy;
+    h->gb = act == MLP_ACT_SWIGLU ? 2 : 1;
+    h->device = dev;
+    h->cus = prop.multiProcessorCount;
+    h->forced_cfg = -1;
+    h->spin_limit = DEFAULT_SPIN_LIMIT;
+    h->skip_producer = mlpc::NO_SKIP;
+    h->last_stream = nullptr;
+    if (apply_plan(h, plan_config(M)) != MLP_OK) {
+        delete h;
+        return nullptr;
+    }
+    // flags and row counters sized for the finest tiling any config uses
+    uint32_t max_t1 = 0, max_mt = 0;
+    for (int c = 0; c < mlpc_num_configs(); ++c) {
+        const CfgInfo ci = mlpc_config_info(c);
+        const uint32_t mt = cdiv(M, ci.BM), n1 = cdiv(I, ci.BN);
+        if (mt * n1 > max_t1) max_t1 = mt * n1;
+        if (mt > max_mt) max_mt = mt;
+    }
+    const size_t t_bytes = align_up((size_t)M * (size_t)I * 2, 256);
+    const size_t f_bytes = align_up((size_t)max_t1 * 4, 256);
+    const size_t r_bytes = align_up((size_t)max_mt * 4, 256);
+    h->ws_bytes = t_bytes + f_bytes + r_bytes + 256 + 256;
+    e = hipMalloc(&h->ws, h->ws_bytes);
+    if (e != hipSuccess) {
+        fail(MLP_ENOMEM, "hipMalloc of %zu workspace bytes failed: %s", h->ws_bytes, hipGetErrorString(e));
+        delete h;
+        return nullptr;
+    }
+    char* p = static_cast<char*>(h->ws);
+    h->t = reinterpret_cast<uint16_t*>(p);
+    h->flags = reinterpret_cast<uint32_t*>(p + t_bytes);
+    h->rowcnt = reinterpret_cast<uint32_t*>(p + t_bytes + f_bytes);
+    h->ticket = reinterpret_cast<uint32_t*>(p + t_bytes + f_bytes + r_bytes);
+    h->status = reinterpret_cast<uint32_t*>(p + t_bytes + f_bytes + r_bytes + 256);
+    if (zero_workspace(h) != MLP_OK) {
+        (void)hipFree(h->ws);
+        delete h;
+        return nullptr;
+    }
+    return h;
+}
+
+int mlp_chain_destroy(mlp_chain_t h) {
+    if (!h) return MLP_OK;
+    DeviceGuard g(h->device);
+    hipError_t e1 = hipDeviceSynchronize();
+    hipError_t e2 = hipFree(h->ws);
+    delete h;
+    if (e1 != hipSuccess || e2 != hipSuccess)
+        return fail(MLP_EHIP, "destroy: %s", hipGetErrorString(e1 != hipSuccess ? e1 : e2));
+    return MLP_OK;
+}
+
+static int launch_phase(mlp_chain_t h, int what, const mlpc::ChainArgs& a, hipStream_t s) {
+    hipError_t e = mlpc_launch(a, h->cfg, h->dtype, h->gb, what, (int)h->grid, s);
+    if (e != hipSuccess) return fail(MLP_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return MLP_OK;
+}
+
+int mlp_chain_run(mlp_chain_t h, const void* x, const void* w1, const void* w2, void* out, void* hip_stream) {
+    if (!h) return fail(MLP_EINVAL, "NULL handle");
+    if (bad_ptr(x) || bad_ptr(w1) || bad_ptr(w2) || bad_ptr(out))
+        return fail(MLP_EINVAL, "x, w1, w2 and out must be non-NULL 16-byte aligned device pointers");
+    DeviceGuard g(h->device);
+    if (!g.ok) return fail(MLP_EHIP, "cannot select the handle's device %d", h->device);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    h->last_stream = s;
+    if (h->policy == MLP_POLICY_STREAM_ORDERED) {
+        const mlpc::ChainArgs a = make_args(h, x, w1, w2, out);
+        int rc = launch_phase(h, LAUNCH_GEMM1, a, s);
+        if (rc != MLP_OK) return rc;
+        return launch_phase(h, LAUNCH_GEMM2, a, s);
+    }
+    h->epoch += 1u;
+    const mlpc::ChainArgs a = make_args(h, x, w1, w2, out);
+    int rc = launch_phase(h, h->policy == MLP_POLICY_ROW_SYNC ? LAUNCH_ROW : LAUNCH_TILE, a, s);
+    if (rc != MLP_OK) {
+        h->epoch -= 1u;
+        return rc;
+    }
+    h->ticket_base += h->T1 + h->T2 + h->grid;
+    return MLP_OK;
+}
+
+int mlp_chain_run_phase(mlp_chain_t h, int phase, const void* x, const void* w1, const void* w2, void* out,
+                        void* hip_stream) {
+    if (!h) return fail(MLP_EINVAL, "NULL handle");
+    if (phase != 1 && phase != 2) return fail(MLP_EINVAL, "phase must be 1 or 2, got %d", phase);
+    if (phase == 1 && (bad_ptr(x) || bad_ptr(w1)))
+        return fail(MLP_EINVAL, "phase 1 needs non-NULL 16-byte aligned x and w1");
+    if (phase == 2 && (bad_ptr(w2) || bad_ptr(out)))
+        return fail(MLP_EINVAL, "phase 2 needs non-NULL 16-byte aligned w2 and out");
+    DeviceGuard g(h->device);
+    if (!g.ok) return fail(MLP_EHIP, "cannot select the handle's device %d", h->device);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    h->last_stream = s;
+    const mlpc::ChainArgs a = make_args(h, x, w1, w2, out);
+    return launch_phase(h, phase == 1 ? LAUNCH_GEMM1 : LAUNCH_GEMM2, a, s);
+}
+
+int mlp_chain_status(mlp_chain_t h) {
+    if (!h) return fail(MLP_EINVAL, "NULL handle");
+    DeviceGuard g(h->device);
+    hipError_t e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail(MLP_EHIP, "device error: %s", hipGetErrorString(e));
+    uint32_t st = 0;
+    e = hipMemcpy(&st, h->status, sizeof st, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return fail(MLP_EHIP, "reading status failed: %s", hipGetErrorString(e));
+    if (st != 0) {
+        int rc = zero_workspace(h);
+        if (rc != MLP_OK) return rc;
+        return fail(MLP_ETIMEOUT, "a consumer tile gave up waiting for its producer (watchdog)");
+    }
+    return MLP_OK;
+}
+
+int mlp_chain_info(mlp_chain_t h, int64_t* info, int n) {
+    if (!h || !info || n < 16) return fail(MLP_EINVAL, "mlp_chain_info needs a handle and 16 slots");
+    const int64_t v[16] = {h->ci.BM, h->ci.BN, h->ci.BN, h->ci.BK, h->Mt, h->N1t, h->N2t, h->T1, h->T2,
+                           h->grid, h->occ, h->ci.NT, h->cus, h->epoch, h->cfg, (int64_t)h->ws_bytes};
+    for (int i = 0; i < 16; ++i) info[i] = v[i];
+    return MLP_OK;
+}
+
+int mlp_chain_debug_set_spin_limit(mlp_chain_t h, uint32_t limit) {
+    if (!h) return fail(MLP_EINVAL, "NULL handle");
+    h->spin_limit = limit ? limit : DEFAULT_SPIN_LIMIT;
+    return MLP_OK;
+}
+
+int mlp_chain_debug_skip_producer(mlp_chain_t h, int64_t tile) {
+    if (!h) return fail(MLP_EINVAL, "NULL handle");
+    h->skip_producer = (tile < 0 || tile >= (int64_t)h->T1) ? mlpc::NO_SKIP : (uint32_t)tile;
+    return MLP_OK;
+}
+
+int mlp_chain_debug_set_config(mlp_chain_t h, int config_id) {
+    if (!h) return fail(MLP_EINVAL, "NULL handle");
+    if (config_id < -1 || config_id >= mlpc_num_configs())
+        return fail(MLP_EINVAL, "unknown tile configuration %d", config_id);
+    DeviceGuard g(h->device);
+    const int cfg = config_id < 0 ? plan_config(h->M) : config_id;
+    h->forced_cfg = config_id;
+    int rc = apply_plan(h, cfg);
+    if (rc != MLP_OK) return rc;
+    return zero_workspace(h);
+}
+
+}  // extern "C"

@@ -1,0 +1,211 @@
+// chain_kernels.hip -- the kernels of the MLP GEMM chain and their launchers.
+//
+//   gemm1_act_kernel   one workgroup per GEMM1 tile: X W1 -> act -> T
+//   gemm2_kernel       one workgroup per GEMM2 tile: T W2 -> Y
+//   chain_persistent   one workgroup per CU slot, looping over an atomic tile
+//                      queue that hands out every GEMM1 (producer) tile before
+//                      any GEMM2 (consumer) tile.  A consumer only ever waits
+//                      for producers whose tickets were drawn earlier by
+//                      running workgroups, and producers never wait, so every
+//                      wait ends whatever the grid size.
+//
+// The stream-ordered policy is the first two kernels back to back on one
+// stream (kernel-level dependency); row_sync and tile_sync are the
+// persistent kernel with per-row-block counters or per-tile flags
+// (tile-level dependency, as in the CuSync README's opening paragraph and the
+// megakernel discussion in the Hacker News thread on megakernels vs CUDA
+// graphs, where a consumer task starts as soon as its slice is done).
+#include "chain_device.hpp"
+#include "chain_launch.h"
+
+namespace mlpc {
+
+using Cfg0 = TileCfg<16, 64, 1, 4>;     // small M: narrow tiles, weight streaming
+using Cfg1 = TileCfg<64, 128, 2, 2>;    // medium M
+using Cfg2 = TileCfg<128, 128, 2, 2>;   // large M
+
+template <class C, int DT, int GB>
+__global__ __launch_bounds__(C::NT) void gemm1_act_kernel(ChainArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    uint32_t mb, nb;
+    tile_coords(blockIdx.x, a.Mt, a.N1t, a.group_m, mb, nb);
+    producer_tile<C, DT, GB>(a, mb, nb, smem);
+}
+
+template <class C, int DT>
+__global__ __launch_bounds__(C::NT) void gemm2_kernel(ChainArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    uint32_t mb, nb;
+    tile_coords(blockIdx.x, a.Mt, a.N2t, a.group_m, mb, nb);
+    consumer_tile<C, DT>(a, mb, nb, smem, NoWait{});
+}
+
+// row_sync: wait once, before the first slab, until all N1t producer tiles
+// of the row block have counted themselves in for this epoch.
+struct RowWait {
+    const uint32_t* cnt;
+    uint32_t target;
+    uint32_t* status;
+    uint32_t limit;
+    __device__ __forceinline__ void operator()(int ks) const {
+        if (ks == 0) wave_wait_geq(cnt, target, status, limit);
+    }
+};
+
+// tile_sync: before the first slab of each producer tile's column block,
+// wait for that tile's flag to carry this epoch.  Slabs are taken in
+// ascending K order regardless of which producer finishes first.
+struct TileWait {
+    const uint32_t* flags;   // the row block's N1t flags
+    uint32_t epoch;
+    int per;                 // K slabs per producer tile (BN / BK)
+    uint32_t* status;
+    uint32_t limit;
+    __device__ __forceinline__ void operator()(int ks) const {
+        if (ks % per == 0) wave_wait_geq(flags + ks / per, epoch, status, limit);
+    }
+};
+
+template <class C, int DT, int GB, int POL>
+__global__ __launch_bounds__(C::NT) void chain_persistent_kernel(ChainArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    __shared__ uint32_t s_ticket;
+    const uint32_t total = a.T1 + a.T2;
+    for (;;) {
+        if (threadIdx.x == 0)
+            s_ticket = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
+                       a.ticket_base;
+        __syncthreads();
+        // The ticket is the same for every thread of the workgroup; reading it
+        // through readfirstlane makes that visible to the compiler, so every
+        // branch on it (and the loop exit) is a scalar branch and all lanes of
+        // a wave stay on one path through the barriers below.
+        const uint32_t t = __builtin_amdgcn_readfirstlane(s_ticket);
+        __syncthreads();
+        if (t >= total) break;
+        if (t < a.T1) {
+            if (t != a.skip_producer) {      // test hook: a skipped tile does no work and no release
+                uint32_t mb, nb;
+                tile_coords(t, a.Mt, a.N1t, a.group_m, mb, nb);
+                producer_tile<C, DT, GB>(a, mb, nb, smem);
+                // every thread's T stores are performed at agent scope before the
+                // single release that publishes the tile
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                __syncthreads();
+                if (threadIdx.x == 0) {
+                    if constexpr (POL == POL_TILE)
+                        __hip_atomic_store(a.flags + mb * a.N1t + nb, a.epoch, __ATOMIC_RELEASE,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                    else
+                        __hip_atomic_fetch_add(a.rowcnt + mb, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        } else {
+            uint32_t mb, nb;
+            tile_coords(t - a.T1, a.Mt, a.N2t, a.group_m, mb, nb);
+            if constexpr (POL == POL_TILE) {
+                TileWait w{a.flags + mb * a.N1t, a.epoch, C::BN / BK, a.status, a.spin_limit};
+                consumer_tile<C, DT>(a, mb, nb, smem, w);
+            } else {
+                RowWait w{a.rowcnt + mb, a.epoch * a.N1t, a.status, a.spin_limit};
+                consumer_tile<C, DT>(a, mb, nb, smem, w);
+            }
+        }
+        // Keep this barrier: it separates the thread-0-only release above from
+        // the thread-0-only ticket draw at the top of the loop.  Without it the
+        // compiler may merge the two across the back edge into a loop in which
+        // the other threads re-read the old ticket at the barriers while
+        // thread 0 waits to draw the next one, which never ends.
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------ host side
+
+template <class K>
+static hipError_t prep(K kernel, int lds) {
+    // allow dynamic LDS beyond the default limit (gfx950 has 160 KB per CU)
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+}
+
+template <class C, int DT, int GB>
+static hipError_t launch_t(const ChainArgs& a, int what, int grid, hipStream_t s, int* occ) {
+    constexpr int lds = C::lds_bytes(GB);
+    hipError_t e = hipSuccess;
+    switch (what) {
+    case LAUNCH_GEMM1: {
+        auto k = gemm1_act_kernel<C, DT, GB>;
+        if ((e = prep(k, lds)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k, dim3(a.T1), dim3(C::NT), lds, s, a);
+        return hipGetLastError();
+    }
+    case LAUNCH_GEMM2: {
+        auto k = gemm2_kernel<C, DT>;
+        constexpr int lds2 = C::lds_bytes(1);
+        if ((e = prep(k, lds2)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k, dim3(a.T2), dim3(C::NT), lds2, s, a);
+        return hipGetLastError();
+    }
+    case LAUNCH_ROW:
+    case LAUNCH_TILE: {
+        auto k = (what == LAUNCH_ROW) ? chain_persistent_kernel<C, DT, GB, POL_ROW>
+                                      : chain_persistent_kernel<C, DT, GB, POL_TILE>;
+        if ((e = prep(k, lds)) != hipSuccess) return e;
+        if (occ) {
+            return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, k, C::NT, lds);
+        }
+        hipLaunchKernelGGL(k, dim3(grid), dim3(C::NT), lds, s, a);
+        return hipGetLastError();
+    }
+    default:
+        return hipErrorInvalidValue;
+    }
+}
+
+template <class C>
+static hipError_t launch_c(const ChainArgs& a, int dtype, int gb, int what, int grid, hipStream_t s,
+                           int* occ) {
+    if (dtype == DT_F16)
+        return gb == 2 ? launch_t<C, DT_F16, 2>(a, what, grid, s, occ) : launch_t<C, DT_F16, 1>(a, what, grid, s, occ);
+    return gb == 2 ? launch_t<C, DT_BF16, 2>(a, what, grid, s, occ) : launch_t<C, DT_BF16, 1>(a, what, grid, s, occ);
+}
+
+static hipError_t dispatch(const ChainArgs& a, int cfg, int dtype, int gb, int what, int grid,
+                           hipStream_t s, int* occ) {
+    switch (cfg) {
+    case 0: return launch_c<Cfg0>(a, dtype, gb, what, grid, s, occ);
+    case 1: return launch_c<Cfg1>(a, dtype, gb, what, grid, s, occ);
+    case 2: return launch_c<Cfg2>(a, dtype, gb, what, grid, s, occ);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <class C>
+static CfgInfo info_of(int id) {
+    return CfgInfo{id, C::BM, C::BN, BK, C::NT, C::lds_bytes(1), C::lds_bytes(2)};
+}
+
+}  // namespace mlpc
+
+using namespace mlpc;
+
+int mlpc_num_configs() { return 3; }
+
+CfgInfo mlpc_config_info(int id) {
+    switch (id) {
+    case 0: return info_of<Cfg0>(0);
+    case 1: return info_of<Cfg1>(1);
+    case 2: return info_of<Cfg2>(2);
+    default: return CfgInfo{-1, 0, 0, 0, 0, 0, 0};
+    }
+}
+
+hipError_t mlpc_launch(const ChainArgs& a, int cfg, int dtype, int gb, int what, int grid, hipStream_t s) {
+    return dispatch(a, cfg, dtype, gb, what, grid, s, nullptr);
+}
+
+hipError_t mlpc_persistent_occupancy(int cfg, int dtype, int gb, int policy, int* per_cu) {
+    ChainArgs dummy{};
+    return dispatch(dummy, cfg, dtype, gb, policy == POL_ROW ? LAUNCH_ROW : LAUNCH_TILE, 0, nullptr, per_cu);
+}

@@ -1,0 +1,212 @@
+"""Thin Python binding of the C ABI in include/mlp_chain.h (ctypes).
+
+Only argument marshalling happens here: every step of the chain runs in the
+HIP library libmlp_chain.so.  torch supplies device memory (tensor
+data_ptr()) and streams (torch.cuda.current_stream().cuda_stream, a
+hipStream_t on ROCm).  There is no fallback: if the library is not built,
+loading fails with an error that says how to build it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "lib", "libmlp_chain.so")
+
+MLP_ACT_NONE, MLP_ACT_GELU_TANH, MLP_ACT_SWIGLU = 0, 1, 2
+MLP_DTYPE_F16, MLP_DTYPE_BF16 = 0, 1
+MLP_POLICY_STREAM_ORDERED, MLP_POLICY_ROW_SYNC, MLP_POLICY_TILE_SYNC = 0, 1, 2
+MLP_OK, MLP_EINVAL, MLP_ENOMEM, MLP_EHIP, MLP_ETIMEOUT = 0, -1, -2, -3, -4
+
+ACTS = {"none": MLP_ACT_NONE, "gelu_tanh": MLP_ACT_GELU_TANH, "swiglu": MLP_ACT_SWIGLU}
+DTYPES = {"f16": MLP_DTYPE_F16, "bf16": MLP_DTYPE_BF16}
+POLICIES = {"stream_ordered": MLP_POLICY_STREAM_ORDERED, "row_sync": MLP_POLICY_ROW_SYNC,
+            "tile_sync": MLP_POLICY_TILE_SYNC}
+
+EXPORTS = ("mlp_chain_create", "mlp_chain_run", "mlp_chain_destroy", "mlp_chain_run_phase",
+           "mlp_chain_status", "mlp_chain_last_error", "mlp_chain_info",
+           "mlp_chain_debug_set_spin_limit", "mlp_chain_debug_skip_producer",
+           "mlp_chain_debug_set_config")
+
+INFO_FIELDS = ("BM", "BN1", "BN2", "BK", "Mt", "N1t", "N2t", "T1", "T2", "grid", "wg_per_cu",
+               "threads", "cus", "epoch", "config", "workspace_bytes")
+
+_lib = None
+
+
+class MlpChainError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"mlp_chain error {code}: {msg}")
+        self.code = code
+
+
+def load_library(path: str | None = None):
+    """Load libmlp_chain.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library not found at {path}; build it with "
+                           "`python -m consumer_gemm_chain_amd.build` (needs hipcc)")
+    lib = ctypes.CDLL(path)
+    vp, i64, ci, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint32
+    lib.mlp_chain_create.argtypes = [i64, i64, i64, ci, ci, ci]
+    lib.mlp_chain_create.restype = vp
+    lib.mlp_chain_run.argtypes = [vp, vp, vp, vp, vp, vp]
+    lib.mlp_chain_run.restype = ci
+    lib.mlp_chain_destroy.argtypes = [vp]
+    lib.mlp_chain_destroy.restype = ci
+    lib.mlp_chain_run_phase.argtypes = [vp, ci, vp, vp, vp, vp, vp]
+    lib.mlp_chain_run_phase.restype = ci
+    lib.mlp_chain_status.argtypes = [vp]
+    lib.mlp_chain_status.restype = ci
+    lib.mlp_chain_last_error.argtypes = []
+    lib.mlp_chain_last_error.restype = ctypes.c_char_p
+    lib.mlp_chain_info.argtypes = [vp, ctypes.POINTER(i64), ci]
+    lib.mlp_chain_info.restype = ci
+    lib.mlp_chain_debug_set_spin_limit.argtypes = [vp, u32]
+    lib.mlp_chain_debug_set_spin_limit.restype = ci
+    lib.mlp_chain_debug_skip_producer.argtypes = [vp, i64]
+    lib.mlp_chain_debug_skip_producer.restype = ci
+    lib.mlp_chain_debug_set_config.argtypes = [vp, ci]
+    lib.mlp_chain_debug_set_config.restype = ci
+    _lib = lib
+    return lib
+
+
+# ---- the C ABI, name for name -------------------------------------------------
+
+def mlp_chain_last_error() -> str:
+    return load_library().mlp_chain_last_error().decode()
+
+
+def _check(rc: int) -> int:
+    if rc != MLP_OK:
+        raise MlpChainError(rc, mlp_chain_last_error())
+    return rc
+
+
+def mlp_chain_create(M: int, H: int, I: int, act: int, dtype: int, policy: int) -> int:
+    """Returns the opaque handle (an integer address); raises on failure."""
+    h = load_library().mlp_chain_create(int(M), int(H), int(I), int(act), int(dtype), int(policy))
+    if not h:
+        raise MlpChainError(MLP_EINVAL, mlp_chain_last_error())
+    return h
+
+
+def mlp_chain_run(h: int, x: int, w1: int, w2: int, out: int, hip_stream: int | None) -> int:
+    return _check(load_library().mlp_chain_run(h, x, w1, w2, out, hip_stream or None))
+
+
+def mlp_chain_run_phase(h: int, phase: int, x: int | None, w1: int | None, w2: int | None,
+                        out: int | None, hip_stream: int | None) -> int:
+    return _check(load_library().mlp_chain_run_phase(h, int(phase), x, w1, w2, out, hip_stream or None))
+
+
+def mlp_chain_destroy(h: int | None) -> int:
+    return _check(load_library().mlp_chain_destroy(h))
+
+
+def mlp_chain_status(h: int) -> int:
+    """Returns MLP_OK or MLP_ETIMEOUT (the sticky watchdog status); raises on
+    other errors."""
+    rc = load_library().mlp_chain_status(h)
+    if rc not in (MLP_OK, MLP_ETIMEOUT):
+        raise MlpChainError(rc, mlp_chain_last_error())
+    return rc
+
+
+def mlp_chain_info(h: int) -> dict:
+    arr = (ctypes.c_int64 * 16)()
+    _check(load_library().mlp_chain_info(h, arr, 16))
+    return dict(zip(INFO_FIELDS, (int(v) for v in arr)))
+
+
+def mlp_chain_debug_set_spin_limit(h: int, limit: int) -> int:
+    return _check(load_library().mlp_chain_debug_set_spin_limit(h, int(limit)))
+
+
+def mlp_chain_debug_skip_producer(h: int, tile: int) -> int:
+    return _check(load_library().mlp_chain_debug_skip_producer(h, int(tile)))
+
+
+def mlp_chain_debug_set_config(h: int, config_id: int) -> int:
+    return _check(load_library().mlp_chain_debug_set_config(h, int(config_id)))
+
+
+# ---- convenience wrapper over torch tensors -------------------------------------
+
+class MlpChain:
+    """Owns one handle.  `run(x, w1, w2, out)` takes torch device tensors of
+    dtype float16 / bfloat16 (or int16 / uint16 bit patterns) and enqueues on
+    torch's current stream (or `stream`)."""
+
+    def __init__(self, M: int, H: int, I: int, act: str = "gelu_tanh", dtype: str = "f16",
+                 policy: str = "tile_sync"):
+        self.M, self.H, self.I = int(M), int(H), int(I)
+        self.act, self.dtype, self.policy = act, dtype, policy
+        self.h = mlp_chain_create(M, H, I, ACTS[act], DTYPES[dtype], POLICIES[policy])
+
+    def close(self):
+        if self.h:
+            mlp_chain_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    @staticmethod
+    def _stream(stream):
+        if stream is not None:
+            return int(getattr(stream, "cuda_stream", stream))
+        import torch
+        return int(torch.cuda.current_stream().cuda_stream)
+
+    def _shapes(self, x, w1, w2, out):
+        g = 2 if self.act == "swiglu" else 1
+        want = {"x": (self.M, self.H), "w1": (self.H, g * self.I), "w2": (self.I, self.H),
+                "out": (self.M, self.H)}
+        for name, t in (("x", x), ("w1", w1), ("w2", w2), ("out", out)):
+            if t is None:
+                continue
+            if tuple(t.shape) != want[name]:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want[name]}")
+            if not t.is_cuda or not t.is_contiguous() or t.element_size() != 2:
+                raise ValueError(f"{name} must be a contiguous 2-byte device tensor")
+
+    def run(self, x, w1, w2, out, stream=None):
+        self._shapes(x, w1, w2, out)
+        mlp_chain_run(self.h, x.data_ptr(), w1.data_ptr(), w2.data_ptr(), out.data_ptr(),
+                      self._stream(stream))
+        return out
+
+    def run_phase(self, phase, x=None, w1=None, w2=None, out=None, stream=None):
+        self._shapes(x, w1, w2, out)
+        p = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
+        mlp_chain_run_phase(self.h, phase, p(x), p(w1), p(w2), p(out), self._stream(stream))
+
+    def status(self) -> int:
+        return mlp_chain_status(self.h)
+
+    def info(self) -> dict:
+        return mlp_chain_info(self.h)
+
+    def set_config(self, cfg: int):
+        mlp_chain_debug_set_config(self.h, cfg)
+
+    def set_spin_limit(self, limit: int):
+        mlp_chain_debug_set_spin_limit(self.h, limit)
+
+    def skip_producer(self, tile: int):
+        mlp_chain_debug_skip_producer(self.h, tile)

@@ -1,0 +1,143 @@
+/*
+ * mlp_chain.h -- C ABI of the tile-synchronized MLP GEMM chain for MI355X (gfx950).
+ *
+ * The operation is the transformer MLP as a chain of two dependent GEMMs:
+ *
+ *     T = act(X * W1)      (first GEMM, activation fused into its epilogue)
+ *     Y = T * W2           (second GEMM, consumes T)
+ *
+ * which the CuSync README (github.com/microsoft/cusync, opening paragraph)
+ * describes as a producer kernel and a consumer kernel whose dependent tiles
+ * (thread blocks) are synchronized by policies instead of whole-kernel
+ * ordering, so that independent tiles run concurrently and fill the last
+ * wave of thread blocks; the same README's paragraph on the GPT-3 / LLaMA MLP
+ * graphs fuses GeLU into the first GeMM.  The policies here are:
+ *
+ *   MLP_POLICY_STREAM_ORDERED  two kernels on one stream (GEMM1+act, then
+ *                              GEMM2): kernel-level dependency, the baseline.
+ *   MLP_POLICY_ROW_SYNC        one persistent kernel; a GEMM2 tile waits until
+ *                              every GEMM1 tile of its row block is done.
+ *   MLP_POLICY_TILE_SYNC       one persistent kernel; a GEMM2 tile waits, K
+ *                              chunk by K chunk, only for the GEMM1 tile that
+ *                              produced that chunk.
+ *
+ * All three compute bit-identical outputs (same tiles, same accumulation
+ * order); they differ only in when tiles run.
+ *
+ * Numerics: inputs and outputs are fp16 or bf16; products accumulate in fp32
+ * on the matrix cores; the activation is applied to the fp32 accumulator(s);
+ * T is rounded to the storage dtype once (round to nearest even), then the
+ * second GEMM accumulates in fp32 and rounds Y the same way.
+ *
+ * Layouts (all row-major, contiguous, same dtype, 16-byte aligned base):
+ *   x   [M, H]
+ *   w1  [H, I]      for gelu_tanh / none
+ *       [H, 2I]     for swiglu: gate = w1[:, 0:I], up = w1[:, I:2I]
+ *   w2  [I, H]
+ *   out [M, H]
+ * H and I must be multiples of 8 (16-byte rows); M is any value >= 1.
+ *
+ * Activations:
+ *   none       a = h
+ *   gelu_tanh  a = 0.5 h (1 + tanh(sqrt(2/pi) (h + 0.044715 h^3)))
+ *   swiglu     a = silu(g) * u,  silu(g) = g / (1 + exp(-g))
+ *
+ * Pointers: x, w1, w2 and out are DEVICE pointers owned by the caller.  The
+ * stream argument is a hipStream_t passed as void* (NULL = default stream).
+ * The handle owns a device workspace (the intermediate T [M, I], per-tile
+ * ready flags, per-row-block counters, a ticket counter, a status word),
+ * allocated by create and freed by destroy.
+ *
+ * Concurrency: runs on one handle must be ordered on one stream (they share
+ * the workspace); separate handles are independent.  All entry points are
+ * thread-safe with respect to different handles.
+ *
+ * Errors: functions return MLP_OK (0) or a negative code; the message of the
+ * last failure on the calling thread is available from mlp_chain_last_error.
+ */
+#ifndef MLP_CHAIN_H
+#define MLP_CHAIN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct mlp_chain* mlp_chain_t;
+
+enum { MLP_ACT_NONE = 0, MLP_ACT_GELU_TANH = 1, MLP_ACT_SWIGLU = 2 };
+enum { MLP_DTYPE_F16 = 0, MLP_DTYPE_BF16 = 1 };
+enum { MLP_POLICY_STREAM_ORDERED = 0, MLP_POLICY_ROW_SYNC = 1, MLP_POLICY_TILE_SYNC = 2 };
+enum { MLP_OK = 0, MLP_EINVAL = -1, MLP_ENOMEM = -2, MLP_EHIP = -3, MLP_ETIMEOUT = -4 };
+
+/* Create a chain for fixed sizes on the current HIP device.
+ * M >= 1, H >= 8 and I >= 8 with H % 8 == 0 and I % 8 == 0; act, dtype and
+ * policy from the enums above.  Picks the tile configuration, allocates and
+ * zeroes the workspace.  Returns NULL on error (bad argument, out of device
+ * memory, HIP failure) with mlp_chain_last_error() set.
+ * (CuSync README, opening paragraph: policies over a producer/consumer chain.) */
+mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype, int policy);
+
+/* Enqueue one chain pass Y = act(X W1) W2 on `hip_stream` with the handle's
+ * policy.  Asynchronous: never synchronizes the host.  Returns MLP_EINVAL for
+ * a NULL handle or a NULL / non-16-byte-aligned pointer, MLP_EHIP if a launch
+ * fails.  A consumer tile that waits longer than the spin limit for its
+ * producer gives up and records MLP_ETIMEOUT in the handle's status word
+ * (see mlp_chain_status); its output is then undefined.
+ * (CuSync README, opening and MLP paragraphs.) */
+int mlp_chain_run(mlp_chain_t h, const void* x, const void* w1, const void* w2, void* out,
+                  void* hip_stream);
+
+/* Release the handle and its workspace (waits for the device first).
+ * NULL-safe; returns MLP_OK, or MLP_EHIP if freeing failed. */
+int mlp_chain_destroy(mlp_chain_t h);
+
+/* Enqueue one phase alone, with the same kernels and tiles as the
+ * stream-ordered policy: phase 1 = GEMM1 + activation, writing the handle's
+ * intermediate T; phase 2 = GEMM2, reading the handle's T and writing out.
+ * Unused pointers may be NULL (phase 1 ignores w2/out, phase 2 ignores x/w1).
+ * It times the best unsplit GEMMs for an overhead figure in the style of the
+ * FLUX summary card's Effective Communication Time (Interesting ideas, I2:
+ * total time minus the best unsplit GEMM time).  Returns as mlp_chain_run,
+ * and MLP_EINVAL for a phase other than 1 or 2. */
+int mlp_chain_run_phase(mlp_chain_t h, int phase, const void* x, const void* w1, const void* w2,
+                        void* out, void* hip_stream);
+
+/* Wait for the device to finish the handle's work, then return the sticky
+ * device status: MLP_OK, or MLP_ETIMEOUT if a consumer tile gave up waiting
+ * since the last call.  Reading an error also clears it and re-zeroes the
+ * handle's flags and counters so that the next run starts clean.  Returns
+ * MLP_EINVAL for a NULL handle and MLP_EHIP if the device reports an error. */
+int mlp_chain_status(mlp_chain_t h);
+
+/* Message describing the last failed call on this thread ("" if none).  The
+ * string is owned by the library and valid until the next call on the thread. */
+const char* mlp_chain_last_error(void);
+
+/* Plan and launch facts of a handle, for tests and measurement:
+ * info[0..15] = { BM, BN1, BN2, BK, Mt, N1t, N2t, T1, T2, persistent grid,
+ *                 workgroups per CU, threads per workgroup, CUs, epoch,
+ *                 config id, workspace bytes }.
+ * Returns MLP_EINVAL for a NULL handle or array, or n < 16. */
+int mlp_chain_info(mlp_chain_t h, int64_t* info, int n);
+
+/* Test hooks (never needed for normal use):
+ * set the consumer spin limit (iterations of the back-off loop before a
+ * consumer gives up; 0 restores the default), and make producer tile
+ * `tile` (ticket order, -1 = none) skip its work and its release, which
+ * forces the watchdog path without any kernel faulting or hanging.
+ * Return MLP_EINVAL for a NULL handle. */
+int mlp_chain_debug_set_spin_limit(mlp_chain_t h, uint32_t limit);
+int mlp_chain_debug_skip_producer(mlp_chain_t h, int64_t tile);
+
+/* Force a tile configuration by id for the next runs (-1 = planner's
+ * choice); used by tests that sweep configurations.  The workspace is kept.
+ * Returns MLP_EINVAL for a NULL handle or an unknown id. */
+int mlp_chain_debug_set_config(mlp_chain_t h, int config_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLP_CHAIN_H */

@@ -1,0 +1,100 @@
+"""GPU-side behaviour of the C ABI: argument errors, the phase entry point,
+the watchdog path (forced from the host, so every kernel still exits
+normally), and handle lifetime."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from consumer_gemm_chain_amd import gen
+from consumer_gemm_chain_amd import mlp_chain as mc
+from tests._helpers import empty_dev, from_dev, run_chain, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(M=96, H=256, I=384, act="gelu_tanh", dtype="f16", seed=1):
+    x, w1, w2 = gen.random_case(M, H, I, act, dtype, seed, w_std=1.0 / np.sqrt(H))
+    return x, w1, w2, (to_dev(x, dtype), to_dev(w1, dtype), to_dev(w2, dtype))
+
+
+def test_misaligned_and_null_pointers_rejected():
+    import torch
+    x, w1, w2, (dx, dw1, dw2) = _inputs()
+    out = empty_dev((96, 256), "f16")
+    lib = mc.load_library()
+    h = mc.mlp_chain_create(96, 256, 384, mc.MLP_ACT_GELU_TANH, mc.MLP_DTYPE_F16, mc.MLP_POLICY_TILE_SYNC)
+    try:
+        s = torch.cuda.current_stream().cuda_stream
+        rc = lib.mlp_chain_run(h, dx.data_ptr() + 2, dw1.data_ptr(), dw2.data_ptr(), out.data_ptr(), s)
+        assert rc == mc.MLP_EINVAL and "aligned" in mc.mlp_chain_last_error()
+        rc = lib.mlp_chain_run(h, dx.data_ptr(), None, dw2.data_ptr(), out.data_ptr(), s)
+        assert rc == mc.MLP_EINVAL
+        rc = lib.mlp_chain_run_phase(h, 3, dx.data_ptr(), dw1.data_ptr(), None, None, s)
+        assert rc == mc.MLP_EINVAL
+        assert mc.mlp_chain_status(h) == mc.MLP_OK
+        info = mc.mlp_chain_info(h)
+        assert info["epoch"] == 0          # rejected runs do not advance the epoch
+    finally:
+        mc.mlp_chain_destroy(h)
+
+
+@pytest.mark.parametrize("policy", ["stream_ordered", "tile_sync"])
+def test_phases_compose_to_the_chain(policy):
+    import torch
+    x, w1, w2, dev = _inputs()
+    ref = run_chain(x, w1, w2, "gelu_tanh", "f16", "stream_ordered", dev=dev)
+    with mc.MlpChain(96, 256, 384, "gelu_tanh", "f16", policy) as ch:
+        out = empty_dev((96, 256), "f16")
+        ch.run_phase(1, x=dev[0], w1=dev[1])
+        ch.run_phase(2, w2=dev[2], out=out)
+        torch.cuda.synchronize()
+        assert np.array_equal(from_dev(out), ref)
+
+
+@pytest.mark.parametrize("policy", ["row_sync", "tile_sync"])
+def test_watchdog_reports_timeout_and_recovers(policy):
+    """Producer tile 0 is told (from the host) to skip its work and its
+    release; the consumers that need it give up after a short spin limit,
+    the handle reports MLP_ETIMEOUT, and the next run is correct again."""
+    import torch
+    x, w1, w2, dev = _inputs()
+    ref = run_chain(x, w1, w2, "gelu_tanh", "f16", "stream_ordered", dev=dev)
+    with mc.MlpChain(96, 256, 384, "gelu_tanh", "f16", policy) as ch:
+        out = empty_dev((96, 256), "f16")
+        ch.run(*dev, out)
+        torch.cuda.synchronize()
+        assert ch.status() == mc.MLP_OK
+        ch.set_spin_limit(2000)
+        ch.skip_producer(0)
+        ch.run(*dev, out)
+        torch.cuda.synchronize()
+        assert ch.status() == mc.MLP_ETIMEOUT
+        assert "gave up" in mc.mlp_chain_last_error()
+        ch.skip_producer(-1)
+        ch.set_spin_limit(0)
+        out.fill_(0)
+        ch.run(*dev, out)
+        torch.cuda.synchronize()
+        assert ch.status() == mc.MLP_OK
+        assert np.array_equal(from_dev(out), ref)
+
+
+def test_create_destroy_does_not_leak():
+    import torch
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    for _ in range(30):
+        h = mc.mlp_chain_create(2048, 4096, 4096, mc.MLP_ACT_SWIGLU, mc.MLP_DTYPE_BF16,
+                                mc.MLP_POLICY_TILE_SYNC)
+        mc.mlp_chain_destroy(h)
+    free1, _ = torch.cuda.mem_get_info()
+    assert free0 - free1 < 64 << 20
+
+
+def test_info_reports_plan():
+    with mc.MlpChain(2048, 12288, 6144, "gelu_tanh", "f16", "tile_sync") as ch:
+        info = ch.info()
+        assert info["cus"] >= 1 and info["grid"] >= 1 and info["wg_per_cu"] >= 1
+        assert info["T1"] == info["Mt"] * info["N1t"] and info["T2"] == info["Mt"] * info["N2t"]
+        assert info["grid"] <= info["wg_per_cu"] * info["cus"]

@@ -1,0 +1,53 @@
+"""Regression check on the compiled gfx950 code of the persistent kernel
+(no GPU needed: hipcc cross-compiles).
+
+The persistent kernel's loop draws a ticket on thread 0, publishes it through
+LDS, and every thread reads it back between two barriers.  An earlier build
+let the compiler merge the thread-0-only flag release at the end of an
+iteration with the thread-0-only ticket draw at the top, producing an inner
+loop in which the other threads re-read the old ticket forever.  This test
+asserts that, in every instantiation, the ticket atomic and the LDS read of
+the ticket sit at the same (outermost) loop depth."""
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from consumer_gemm_chain_amd import build as b
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    if not os.path.exists(b.hipcc()):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("isa") / "kernels.s"
+    src = os.path.join(b.CSRC, "chain_kernels.hip")
+    cmd = [b.hipcc(), "-x", "hip", *b.FLAGS, "--cuda-device-only", "-S", src, "-o", str(out)]
+    subprocess.run(cmd, check=True, stderr=subprocess.DEVNULL)
+    return out.read_text()
+
+
+def _functions(text, prefix):
+    for m in re.finditer(rf"^({prefix}\w*):", text, flags=re.M):
+        start = m.end()
+        end = text.index("s_endpgm", start)
+        yield m.group(1), text[start:end]
+
+
+def test_ticket_draw_and_read_at_same_loop_depth(asm):
+    kernels = list(_functions(asm, "_ZN4mlpc23chain_persistent_kernel"))
+    assert len(kernels) == 24
+    for name, body in kernels:
+        depth = None
+        d_atomic = d_read = None
+        for line in body.split("\n"):
+            m = re.search(r"Depth=(\d+)", line)
+            if m:
+                depth = int(m.group(1))
+            if d_atomic is None and "global_atomic_add" in line and " sc0" in line:
+                d_atomic = depth
+            if d_atomic is not None and d_read is None and "ds_read_b32" in line:
+                d_read = depth
+        assert d_atomic == 1 and d_read == 1, (name, d_atomic, d_read)

@@ -1,0 +1,183 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, and
+bit-exactness across the three policies.
+
+Small cases span several tiles and ragged tails in every dimension and run
+the whole output through the oracle; the five workloads run at full size in
+the planner's launch configuration (the one the benchmark times), with the
+oracle on sampled rows and the policies compared on the whole output.
+"""
+import numpy as np
+import pytest
+
+from consumer_gemm_chain_amd import gen
+from tests._helpers import (POLICIES, check_against_oracle, run_chain, to_dev, widen)
+
+pytestmark = pytest.mark.gpu
+
+ACTS = ("none", "gelu_tanh", "swiglu")
+DTYPES = ("f16", "bf16")
+
+
+def _case(M, H, I, act, dtype, seed):
+    # weight scale keeps the intermediate O(1) for any H
+    return gen.random_case(M, H, I, act, dtype, seed, x_std=1.0, w_std=1.0 / np.sqrt(H))
+
+
+@pytest.mark.parametrize("act", ACTS)
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+def test_small_all_policies_match_oracle(oracle_mod, act, dtype, cfg):
+    # several tiles in M, N1, N2 and K for every config, ragged everywhere
+    M, H, I = 200, 328, 456
+    x, w1, w2 = _case(M, H, I, act, dtype, seed=100 + cfg)
+    print(f"case M={M} H={H} I={I} act={act} dtype={dtype} cfg={cfg}", flush=True)
+    y_ref = oracle_mod.mlp_chain(x, w1, w2, act, dtype)
+    outs = {}
+    for pol in POLICIES:
+        outs[pol] = run_chain(x, w1, w2, act, dtype, pol, cfg=cfg)
+        check_against_oracle(outs[pol], y_ref, dtype, f"{pol} cfg{cfg}")
+    assert np.array_equal(outs["row_sync"], outs["stream_ordered"])
+    assert np.array_equal(outs["tile_sync"], outs["stream_ordered"])
+
+
+@pytest.mark.parametrize("M", [1, 15, 16, 17, 127, 129])
+@pytest.mark.parametrize("act,dtype", [("gelu_tanh", "f16"), ("swiglu", "bf16")])
+def test_edge_rows_and_ragged_inner(oracle_mod, M, act, dtype):
+    # I = 2752 = 43 * 64: the LLaMA-65 shard's ragged inner width
+    H, I = 256, 2752
+    x, w1, w2 = _case(M, H, I, act, dtype, seed=M)
+    print(f"case M={M} H={H} I={I} act={act} dtype={dtype}", flush=True)
+    y_ref = oracle_mod.mlp_chain(x, w1, w2, act, dtype)
+    outs = {pol: run_chain(x, w1, w2, act, dtype, pol) for pol in POLICIES}
+    for pol, y in outs.items():
+        check_against_oracle(y, y_ref, dtype, pol)
+    assert np.array_equal(outs["tile_sync"], outs["stream_ordered"])
+    assert np.array_equal(outs["row_sync"], outs["stream_ordered"])
+
+
+def test_tiny_workload(oracle_mod):
+    """Workload 0: X[64,512], W1[512,2048], W2[2048,512], fp16, GeLU."""
+    w = gen.WORKLOADS[0]
+    x, w1, w2 = gen.workload_inputs(w)
+    y_ref = oracle_mod.mlp_chain(x, w1, w2, w.act, w.dtype)
+    outs = {pol: run_chain(x, w1, w2, w.act, w.dtype, pol) for pol in POLICIES}
+    for pol, y in outs.items():
+        check_against_oracle(y, y_ref, w.dtype, pol)
+        assert np.array_equal(y, outs["stream_ordered"])
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+def test_exact_integer_pin_on_gpu(oracle_mod, dtype, cfg):
+    """Integer inputs whose partial sums are exact in fp32 in any order (also
+    inside the matrix cores): every policy, the oracle and exact int64
+    products followed by the library's rounding agree bit for bit."""
+    M, H, I = 96, 512, 384
+    r = np.random.Generator(np.random.PCG64(cfg * 7 + (dtype == "bf16")))
+    def ints(shape, lo, hi, dens):
+        v = r.integers(lo, hi + 1, size=shape).astype(np.float32)
+        v[r.random(shape) >= dens] = 0
+        return v
+    xv = ints((M, H), -3, 3, 0.7)
+    w1v = ints((H, I), -3, 3, 0.7)
+    w2v = ints((I, H), -1, 1, 0.1 if dtype == "f16" else 0.05)
+    x, w1, w2 = gen.to_bits(xv, dtype), gen.to_bits(w1v, dtype), gen.to_bits(w2v, dtype)
+    h = xv.astype(np.int64) @ w1v.astype(np.int64)
+    t_bits = gen.to_bits(h.astype(np.float32), dtype)
+    t_int = widen(t_bits, dtype).astype(np.int64)
+    y_bits = gen.to_bits((t_int @ w2v.astype(np.int64)).astype(np.float32), dtype)
+    y_or = oracle_mod.mlp_chain(x, w1, w2, "none", dtype)
+    assert np.array_equal(y_or, y_bits)
+    for pol in POLICIES:
+        y = run_chain(x, w1, w2, "none", dtype, pol, cfg=cfg)
+        assert np.array_equal(y, y_bits), pol
+
+
+@pytest.mark.parametrize("act", ACTS)
+def test_identity_w2_and_zero_x(oracle_mod, act):
+    """Invariants on the GPU: identity W2 gives act(X W1) (bitwise equal to
+    the oracle's intermediate where the GPU's fp32 sum rounds the same way,
+    within tolerance everywhere); zero X gives exactly zero."""
+    M, H, I = 70, 128, 320
+    dtype = "f16"
+    x, w1, _ = _case(M, H, I, act, dtype, seed=5)
+    eye = np.zeros((I, H), np.float32)
+    eye[np.arange(H), np.arange(H)] = 1.0
+    w2 = gen.to_bits(eye, dtype)
+    _, t_ref = oracle_mod.mlp_chain(x, w1, w2, act, dtype, want_t=True)
+    for pol in POLICIES:
+        y = run_chain(x, w1, w2, act, dtype, pol)
+        check_against_oracle(y, t_ref[:, :H], dtype, f"identity {pol}")
+        z = run_chain(np.zeros_like(x), w1, w2, act, dtype, pol)
+        assert np.all(widen(z, dtype) == 0)
+
+
+def test_linear_in_w2_on_gpu():
+    """Y(4 W2) == 4 Y(W2) bit for bit on the GPU (power-of-two scaling is
+    exact through the fp32 accumulation and the rounding)."""
+    M, H, I, dtype = 64, 256, 512, "f16"
+    x, w1, w2 = _case(M, H, I, "gelu_tanh", dtype, seed=6)
+    w2s = gen.to_bits(widen(w2, dtype).astype(np.float32) * 4, dtype)
+    for pol in POLICIES:
+        y1 = widen(run_chain(x, w1, w2, "gelu_tanh", dtype, pol), dtype)
+        y4 = widen(run_chain(x, w1, w2s, "gelu_tanh", dtype, pol), dtype)
+        normal = np.abs(y1) >= 2.0 ** -14
+        assert np.array_equal(y4[normal], 4 * y1[normal])
+
+
+def test_repeated_runs_are_bit_identical():
+    """Any data race on the intermediate or the flags would show up as
+    run-to-run differences; 40 back-to-back runs of each fused policy on one
+    handle (epochs advance) must match the stream-ordered output exactly."""
+    import torch
+    from consumer_gemm_chain_amd.mlp_chain import MlpChain
+    from tests._helpers import empty_dev, from_dev
+    M, H, I, act, dtype = 512, 1024, 1536, "gelu_tanh", "f16"
+    x, w1, w2 = _case(M, H, I, act, dtype, seed=9)
+    dev = (to_dev(x, dtype), to_dev(w1, dtype), to_dev(w2, dtype))
+    ref = run_chain(x, w1, w2, act, dtype, "stream_ordered", dev=dev)
+    for pol in ("row_sync", "tile_sync"):
+        with MlpChain(M, H, I, act, dtype, pol) as ch:
+            out = empty_dev((M, H), dtype)
+            for i in range(40):
+                out.fill_(float("nan"))
+                ch.run(*dev, out)
+                torch.cuda.synchronize()
+                assert np.array_equal(from_dev(out), ref), f"{pol} run {i}"
+            assert ch.status() == 0
+            assert ch.info()["epoch"] == 40
+
+
+def _sample_rows(M, k=6, seed=0):
+    r = np.random.Generator(np.random.PCG64(seed))
+    rows = {0, M - 1, M // 2}
+    while len(rows) < min(k, M):
+        rows.add(int(r.integers(0, M)))
+    return sorted(rows)
+
+
+FULL = [(1, 1), (1, 64), (1, 512), (1, 2048),
+        (2, 1), (2, 256), (2, 2048),
+        (3, 128), (3, 2048), (3, 8192),
+        (4, 8192)]
+
+
+@pytest.mark.parametrize("wl,M", FULL)
+def test_full_size_workloads(oracle_mod, wl, M):
+    """Full-size workloads in the planner's launch configuration: the three
+    policies agree bit for bit on the whole output, and sampled rows agree
+    with the oracle within tolerance."""
+    import torch
+    w = gen.WORKLOADS[wl]
+    print(f"workload {w.name} M={M}", flush=True)
+    w1, w2 = gen.weights(w)
+    x = gen.x_rows(w, M)
+    dev = (to_dev(x, w.dtype), to_dev(w1, w.dtype), to_dev(w2, w.dtype))
+    outs = {pol: run_chain(x, w1, w2, w.act, w.dtype, pol, dev=dev) for pol in POLICIES}
+    del dev
+    torch.cuda.empty_cache()
+    assert np.array_equal(outs["row_sync"], outs["stream_ordered"])
+    assert np.array_equal(outs["tile_sync"], outs["stream_ordered"])
+    rows = _sample_rows(M, seed=wl * 10000 + M)
+    y_ref = oracle_mod.mlp_chain(x[rows], w1, w2, w.act, w.dtype)
+    check_against_oracle(outs["tile_sync"][rows], y_ref, w.dtype, f"{w.name} M={M}")
