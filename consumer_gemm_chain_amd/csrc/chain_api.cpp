@@ -376,4 +376,13 @@ int mlp_chain_debug_set_config(mlp_chain_t h, int config_id) {
     return zero_workspace(h);
 }
 
+int mlp_chain_debug_read_intermediate(mlp_chain_t h, void* dst, void* hip_stream) {
+    if (!h || !dst) return fail(MLP_EINVAL, "mlp_chain_debug_read_intermediate needs a handle and a buffer");
+    DeviceGuard g(h->device);
+    hipError_t e = hipMemcpyAsync(dst, h->t, (size_t)h->M * (size_t)h->I * 2, hipMemcpyDeviceToDevice,
+                                  static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(MLP_EHIP, "copy of the intermediate failed: %s", hipGetErrorString(e));
+    return MLP_OK;
+}
+
 }  // extern "C"

@@ -102,8 +102,14 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
     }
 }
 
+// fp32 -> storage dtype, round to nearest even, from a value that has been
+// rounded to fp32 first.  The empty asm pins `v` as an fp32 register value:
+// without it the compiler may fuse the multiply that produced `v` with the
+// conversion (v_fma_mixlo_f16), which rounds once instead of twice and makes
+// the result depend on how the epilogue was inlined into each kernel.
 template <int DT>
 __device__ __forceinline__ uint16_t to_storage(float v) {
+    asm volatile("" : "+v"(v));
     if constexpr (DT == DT_F16) {
         return __builtin_bit_cast(uint16_t, (_Float16)v);
     } else {

@@ -27,7 +27,7 @@ POLICIES = {"stream_ordered": MLP_POLICY_STREAM_ORDERED, "row_sync": MLP_POLICY_
 EXPORTS = ("mlp_chain_create", "mlp_chain_run", "mlp_chain_destroy", "mlp_chain_run_phase",
            "mlp_chain_status", "mlp_chain_last_error", "mlp_chain_info",
            "mlp_chain_debug_set_spin_limit", "mlp_chain_debug_skip_producer",
-           "mlp_chain_debug_set_config")
+           "mlp_chain_debug_set_config", "mlp_chain_debug_read_intermediate")
 
 INFO_FIELDS = ("BM", "BN1", "BN2", "BK", "Mt", "N1t", "N2t", "T1", "T2", "grid", "wg_per_cu",
                "threads", "cus", "epoch", "config", "workspace_bytes")
@@ -72,6 +72,8 @@ def load_library(path: str | None = None):
     lib.mlp_chain_debug_skip_producer.restype = ci
     lib.mlp_chain_debug_set_config.argtypes = [vp, ci]
     lib.mlp_chain_debug_set_config.restype = ci
+    lib.mlp_chain_debug_read_intermediate.argtypes = [vp, vp, vp]
+    lib.mlp_chain_debug_read_intermediate.restype = ci
     _lib = lib
     return lib
 
@@ -134,6 +136,10 @@ def mlp_chain_debug_skip_producer(h: int, tile: int) -> int:
 
 def mlp_chain_debug_set_config(h: int, config_id: int) -> int:
     return _check(load_library().mlp_chain_debug_set_config(h, int(config_id)))
+
+
+def mlp_chain_debug_read_intermediate(h: int, dst: int, hip_stream: int | None) -> int:
+    return _check(load_library().mlp_chain_debug_read_intermediate(h, dst, hip_stream or None))
 
 
 # ---- convenience wrapper over torch tensors -------------------------------------
@@ -210,3 +216,11 @@ class MlpChain:
 
     def skip_producer(self, tile: int):
         mlp_chain_debug_skip_producer(self.h, tile)
+
+    def read_intermediate(self, stream=None):
+        """Copy of the intermediate T [M, I] left by the last run (a device tensor)."""
+        import torch
+        dt = torch.float16 if self.dtype == "f16" else torch.bfloat16
+        t = torch.empty((self.M, self.I), dtype=dt, device="cuda")
+        mlp_chain_debug_read_intermediate(self.h, t.data_ptr(), self._stream(stream))
+        return t

@@ -136,6 +136,13 @@ int mlp_chain_debug_skip_producer(mlp_chain_t h, int64_t tile);
  * Returns MLP_EINVAL for a NULL handle or an unknown id. */
 int mlp_chain_debug_set_config(mlp_chain_t h, int config_id);
 
+/* Copy the handle's intermediate T [M, I] (as left by the last run on the
+ * handle) into the caller's device buffer `dst` (M * I elements of the
+ * storage dtype), enqueued on `hip_stream` after the handle's work.  For
+ * tests that check the intermediate itself.  Returns MLP_EINVAL for a NULL
+ * handle or buffer, MLP_EHIP if the copy cannot be enqueued. */
+int mlp_chain_debug_read_intermediate(mlp_chain_t h, void* dst, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -51,3 +51,14 @@ def test_ticket_draw_and_read_at_same_loop_depth(asm):
             if d_atomic is not None and d_read is None and "ds_read_b32" in line:
                 d_read = depth
         assert d_atomic == 1 and d_read == 1, (name, d_atomic, d_read)
+
+
+def test_no_mixed_precision_fma_in_epilogues(asm):
+    """The activation is rounded to fp32 before the conversion to the
+    storage dtype; a fused multiply-add with conversion (v_fma_mix*/v_mad_mix*)
+    would round once instead, and differently in different kernels."""
+    assert "v_fma_mix" not in asm and "v_mad_mix" not in asm
+
+
+def test_no_packed_fp32_arithmetic(asm):
+    assert not re.search(r"v_pk_(add|mul|fma)_f32", asm)
