@@ -1,0 +1,267 @@
+"""Benchmark of the tile-synchronized MLP GEMM chain on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1] [--M 2048]
+                    [--policy tile_sync] [--no-sweep] [--no-cpu]
+
+A step is one chain pass (GEMM1 + activation, then GEMM2) over one batch of
+M tokens, enqueued through the C ABI (mlp_chain_run) with inputs already
+resident in HBM.  The headline is the GPT-3 175B MLP shard (H=12288,
+I=6144, fp16, GeLU; the pages' GPT-3 MLP under 8-way model parallelism) at
+M=2048 tokens with the tile_sync policy.  Next to it the script reports the
+stream-ordered two-kernel baseline, a sweep over M = 1..2048 for the three
+policies (time, TFLOP/s, fraction of the MFMA / HBM roofline, speedup over
+stream-ordered, and an overhead in the style of the FLUX summary card's
+Effective Communication Time: policy time minus the best isolated GEMM1 and
+GEMM2 times), the dominant kernel's roofline position measured with HIP
+events, and the CPU oracle timed on a bounded sample of rows.
+
+Prints ONE JSON line.  Inputs are seeded synthetic data of the workload's
+shapes (no trained weights).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}   # MI355X dense fp16 / bf16 matrix peak
+PEAK_HBM_GBS = 8000.0                                  # MI355X HBM3E bandwidth
+POLICIES = ("stream_ordered", "row_sync", "tile_sync")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def roofline_time_us(w, M, dtype):
+    f = w.flops(M)
+    b = w.bytes(M)
+    t_mfma = f / (PEAK_MFMA_TFLOPS[dtype] * 1e12) * 1e6
+    t_hbm = b / (PEAK_HBM_GBS * 1e9) * 1e6
+    return max(t_mfma, t_hbm), ("mfma" if t_mfma >= t_hbm else "hbm")
+
+
+class Runner:
+    """Device inputs for one workload at its largest M; runs slice X rows."""
+
+    def __init__(self, w, max_M):
+        import torch
+        from consumer_gemm_chain_amd import gen
+        from consumer_gemm_chain_amd.tensors import to_dev
+        self.w = w
+        t0 = time.time()
+        w1, w2 = gen.weights(w)
+        x = gen.x_rows(w, max_M, max_M=max(max_M, w.max_M))
+        self.host = (x, w1, w2)
+        self.x = to_dev(x, w.dtype)
+        self.w1 = to_dev(w1, w.dtype)
+        self.w2 = to_dev(w2, w.dtype)
+        dt = self.x.dtype
+        self.out = torch.empty((max_M, w.H), dtype=dt, device="cuda")
+        torch.cuda.synchronize()
+        log(f"inputs for {w.name} (M<={max_M}) ready in {time.time() - t0:.1f}s")
+
+    def chain(self, M, policy):
+        from consumer_gemm_chain_amd.mlp_chain import MlpChain
+        return MlpChain(M, self.w.H, self.w.I, self.w.act, self.w.dtype, policy)
+
+    def args(self, M):
+        return self.x[:M], self.w1, self.w2, self.out[:M]
+
+
+def event_times(fn, n, stream, flush=None):
+    """Per-call device times (us) from HIP events recorded on `stream`."""
+    import torch
+    ts = []
+    for _ in range(n):
+        if flush is not None:
+            flush()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        ts.append(a.elapsed_time(b) * 1e3)
+    return np.array(ts)
+
+
+def sweep(runner, Ms, reps, stream, flush_buf):
+    """Per (M, policy): median event time, TFLOP/s, roofline fraction, speedup,
+    ECT-style overhead against the best isolated GEMM1 + GEMM2 times."""
+    import torch
+    w = runner.w
+    flush = (lambda: flush_buf.add_(1)) if flush_buf is not None else None
+    rows = []
+    for M in Ms:
+        x, w1, w2, out = runner.args(M)
+        res = {}
+        with runner.chain(M, "stream_ordered") as so:
+            for _ in range(3):
+                so.run_phase(1, x=x, w1=w1)
+                so.run_phase(2, w2=w2, out=out)
+            torch.cuda.synchronize()
+            g1 = np.median(event_times(lambda: so.run_phase(1, x=x, w1=w1), reps, stream, flush))
+            g2 = np.median(event_times(lambda: so.run_phase(2, w2=w2, out=out), reps, stream, flush))
+        for pol in POLICIES:
+            with runner.chain(M, pol) as ch:
+                for _ in range(3):
+                    ch.run(x, w1, w2, out)
+                torch.cuda.synchronize()
+                ts = event_times(lambda: ch.run(x, w1, w2, out), reps, stream, flush)
+                assert ch.status() == 0
+                info = ch.info()
+            res[pol] = (float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90)), info)
+        t_roof, bound = roofline_time_us(w, M, w.dtype)
+        t_so = res["stream_ordered"][0]
+        for pol in POLICIES:
+            t, p10, p90, info = res[pol]
+            rows.append({
+                "M": M, "policy": pol, "us": round(t, 2), "p10_us": round(p10, 2), "p90_us": round(p90, 2),
+                "tflops": round(w.flops(M) / (t * 1e-6) / 1e12, 2),
+                "gbs": round(w.bytes(M) / (t * 1e-6) / 1e9, 1),
+                "roofline_frac": round(t_roof / t, 4), "bound": bound,
+                "speedup_vs_stream_ordered": round(t_so / t, 4),
+                "overhead_vs_best_unsplit_us": round(t - (g1 + g2), 2),
+                "tiles": [info["T1"], info["T2"]], "tile": [info["BM"], info["BN1"]],
+            })
+        log(f"M={M:5d} g1={g1:8.1f}us g2={g2:8.1f}us  " + "  ".join(
+            f"{p}={res[p][0]:8.1f}us" for p in POLICIES))
+    return rows
+
+
+def cpu_baseline(runner, M, budget_s=12.0):
+    """The oracle as it stands, on a bounded sample of the workload's rows."""
+    from oracle import oracle
+    w = runner.w
+    x, w1, w2 = runner.host
+    threads = oracle.max_threads()
+    R = max(1, min(M, threads))
+    while True:
+        t0 = time.perf_counter()
+        oracle.mlp_chain(x[:R], w1, w2, w.act, w.dtype)
+        dt = time.perf_counter() - t0
+        if dt >= budget_s / 3 or R >= M:
+            break
+        R = min(M, R * 2)
+    tflops = w.flops(R) / dt / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{w.name}: first {R} of {M} rows in one call ({dt:.2f} s, weights widened "
+                      f"inside the call), throughput scaled per row"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=1)
+    ap.add_argument("--M", type=int, default=2048)
+    ap.add_argument("--policy", default="tile_sync", choices=POLICIES)
+    ap.add_argument("--sweep-reps", type=int, default=20)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--flush", action="store_true", help="flush the MALL between sweep runs")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the chain runs on one MI355X; no sharding); "
+              f"got --gpus {args.gpus}", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from consumer_gemm_chain_amd import gen
+    from consumer_gemm_chain_amd.mlp_chain import load_library
+    load_library()   # fails loudly if the HIP library is not built
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    w = gen.WORKLOADS[args.workload]
+    M = args.M
+    sweep_Ms = [m for m in w.Ms if m <= M] if not args.no_sweep else []
+    runner = Runner(w, max(M, max(sweep_Ms) if sweep_Ms else M))
+    stream = torch.cuda.current_stream()
+    x, w1, w2, out = runner.args(M)
+
+    def timed_loop(ch, steps):
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        t0 = time.perf_counter()
+        for a, b in ev:
+            a.record(stream)
+            ch.run(x, w1, w2, out)
+            b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+        return wall, kern
+
+    # headline: the chosen policy, K timed steps after W warmup steps
+    with runner.chain(M, args.policy) as ch:
+        for _ in range(args.warmup):
+            ch.run(x, w1, w2, out)
+        wall, kern = timed_loop(ch, args.steps)
+        assert ch.status() == 0, "device watchdog fired during the timed steps"
+        info = ch.info()
+    ms_per_step = wall / args.steps * 1e3
+    F = w.flops(M)
+    value = F / (ms_per_step * 1e-3) / 1e12
+
+    # the stream-ordered two-kernel baseline at the same M
+    with runner.chain(M, "stream_ordered") as so:
+        for _ in range(args.warmup):
+            so.run(x, w1, w2, out)
+        wall_so, kern_so = timed_loop(so, args.steps)
+    so_tflops = F / (wall_so / args.steps) / 1e12
+
+    t_roof, bound = roofline_time_us(w, M, w.dtype)
+    kern_us = float(np.mean(kern))
+    achieved = F / (kern_us * 1e-6) / 1e12
+    roofline = {"bound": "mfma" if bound == "mfma" else "hbm",
+                "kernel": f"chain_persistent_kernel ({args.policy})" if args.policy != "stream_ordered"
+                else "gemm1_act_kernel + gemm2_kernel",
+                "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS[w.dtype], "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_MFMA_TFLOPS[w.dtype], 4),
+                "kernel_us": round(kern_us, 2), "traffic": None,
+                "algorithmic_flops_per_launch": F, "algorithmic_bytes_per_launch": w.bytes(M),
+                "roofline_time_us": round(t_roof, 2), "frac_of_roofline_time": round(t_roof / kern_us, 4)}
+    if bound == "hbm":
+        gbs = w.bytes(M) / (kern_us * 1e-6) / 1e9
+        roofline.update({"achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4)})
+
+    rows = []
+    if sweep_Ms:
+        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.flush else None
+        rows = sweep(runner, sweep_Ms, args.sweep_reps, stream, flush_buf)
+        del flush_buf
+
+    cpu = None if args.no_cpu else cpu_baseline(runner, M)
+
+    line = {
+        "metric": "MLP-chain TFLOP/s and % roofline vs stream-ordered 2-kernel, M=1..2048",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "M": M, "H": w.H, "I": w.I, "act": w.act, "policy": args.policy,
+                   "tile": [info["BM"], info["BN1"], info["BK"]], "tiles": [info["T1"], info["T2"]],
+                   "grid": info["grid"], "parallelism": "single GPU"},
+        "stream_ordered": {"value": round(so_tflops, 2), "ms_per_step": round(wall_so / args.steps * 1e3, 4),
+                           "kernel_pair_us": round(float(np.mean(kern_so)), 2)},
+        "speedup_vs_stream_ordered": round(value / so_tflops, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "sweep": rows,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

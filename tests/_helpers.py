@@ -6,6 +6,7 @@ import numpy as np
 
 from consumer_gemm_chain_amd import gen
 from consumer_gemm_chain_amd.mlp_chain import MLP_OK, MlpChain
+from consumer_gemm_chain_amd.tensors import empty_dev, from_dev, to_dev, torch_dtype  # noqa: F401
 
 POLICIES = ("stream_ordered", "row_sync", "tile_sync")
 
@@ -13,27 +14,6 @@ POLICIES = ("stream_ordered", "row_sync", "tile_sync")
 TOL = {"f16": (1e-2, 1e-2), "bf16": (2e-2, 2e-2)}
 # supplementary normwise bound ||gpu - oracle||_F / ||oracle||_F
 NORMWISE = {"f16": 2.0 ** -8, "bf16": 2.0 ** -5}
-
-
-def torch_dtype(dtype):
-    import torch
-    return torch.float16 if dtype == "f16" else torch.bfloat16
-
-
-def to_dev(bits: np.ndarray, dtype: str):
-    import torch
-    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda")
-    return t.view(torch_dtype(dtype))
-
-
-def from_dev(t) -> np.ndarray:
-    import torch
-    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-
-
-def empty_dev(shape, dtype):
-    import torch
-    return torch.empty(shape, dtype=torch_dtype(dtype), device="cuda")
 
 
 def run_chain(x, w1, w2, act, dtype, policy, cfg=None, reps=1, dev=None, chain=None):
