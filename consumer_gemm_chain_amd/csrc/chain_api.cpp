@@ -106,7 +106,7 @@ int apply_plan(mlp_chain* h, int cfg) {
     h->cfg = cfg;
     h->ci = ci;
     h->Mt = cdiv(h->M, ci.BM);
-    h->N1t = cdiv(h->I, ci.BN);
+    h->N1t = cdiv(h->I, h->act == MLP_ACT_SWIGLU ? ci.BN / 2 : ci.BN);
     h->N2t = cdiv(h->H, ci.BN);
     h->T1 = h->Mt * h->N1t;
     h->T2 = h->Mt * h->N2t;
@@ -114,7 +114,7 @@ int apply_plan(mlp_chain* h, int cfg) {
     h->grid = 0;
     if (h->policy != MLP_POLICY_STREAM_ORDERED) {
         int occ = 0;
-        hipError_t e = mlpc_persistent_occupancy(cfg, h->dtype, h->gb, h->policy, &occ);
+        hipError_t e = mlpc_persistent_occupancy(cfg, h->dtype, h->policy, &occ);
         if (e != hipSuccess) return fail(MLP_EHIP, "occupancy query failed: %s", hipGetErrorString(e));
         if (occ < 1) return fail(MLP_EHIP, "persistent kernel of config %d does not fit on a CU", cfg);
         h->occ = occ;
@@ -242,7 +242,7 @@ mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype
     uint32_t max_t1 = 0, max_mt = 0;
     for (int c = 0; c < mlpc_num_configs(); ++c) {
         const CfgInfo ci = mlpc_config_info(c);
-        const uint32_t mt = cdiv(M, ci.BM), n1 = cdiv(I, ci.BN);
+        const uint32_t mt = cdiv(M, ci.BM), n1 = cdiv(I, act == MLP_ACT_SWIGLU ? ci.BN / 2 : ci.BN);
         if (mt * n1 > max_t1) max_t1 = mt * n1;
         if (mt > max_mt) max_mt = mt;
     }
@@ -282,7 +282,7 @@ int mlp_chain_destroy(mlp_chain_t h) {
 }
 
 static int launch_phase(mlp_chain_t h, int what, const mlpc::ChainArgs& a, hipStream_t s) {
-    hipError_t e = mlpc_launch(a, h->cfg, h->dtype, h->gb, what, (int)h->grid, s);
+    hipError_t e = mlpc_launch(a, h->cfg, h->dtype, what, (int)h->grid, s);
     if (e != hipSuccess) return fail(MLP_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
     return MLP_OK;
 }
@@ -346,7 +346,8 @@ int mlp_chain_status(mlp_chain_t h) {
 
 int mlp_chain_info(mlp_chain_t h, int64_t* info, int n) {
     if (!h || !info || n < 16) return fail(MLP_EINVAL, "mlp_chain_info needs a handle and 16 slots");
-    const int64_t v[16] = {h->ci.BM, h->ci.BN, h->ci.BN, h->ci.BK, h->Mt, h->N1t, h->N2t, h->T1, h->T2,
+    const int64_t bn1 = h->act == MLP_ACT_SWIGLU ? h->ci.BN / 2 : h->ci.BN;
+    const int64_t v[16] = {h->ci.BM, bn1, h->ci.BN, h->ci.BK, h->Mt, h->N1t, h->N2t, h->T1, h->T2,
                            h->grid, h->occ, h->ci.NT, h->cus, h->epoch, h->cfg, (int64_t)h->ws_bytes};
     for (int i = 0; i < 16; ++i) info[i] = v[i];
     return MLP_OK;

@@ -66,19 +66,25 @@ struct ChainArgs {
     int policy;
 };
 
-// Tile configuration.  BN is the output width of a tile; a SwiGLU producer
-// tile holds 2*BN weight columns (gate and up) and two accumulator sets.
-template <int BM_, int BN_, int WM_, int WN_>
+// Tile configuration: BM x BN tile, WM x WN waves of (BM/WM) x (BN/WN).  BN
+// is the number of B (weight) columns of a tile: its output width, except
+// for SwiGLU producer tiles, whose BN columns are gate/up pairs of BN/2
+// output columns.
+template <int BM_, int BN_, int WM_, int WN_, int OCC_>
 struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    // waves per SIMD the persistent kernel is register-limited to (the
+    // occupancy of the standalone GEMM2 kernel of the same tile)
+    static constexpr int OCC = OCC_;
     static constexpr int NT = 64 * WM * WN;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int FM = WTM / 16, FN = WTN / 16;
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16x16");
-    // bytes of one LDS stage for a B tile of gb*BN columns
-    static constexpr int stage_bytes(int gb) { return (BM + gb * BN) * BK * 2; }
-    static constexpr int lds_bytes(int gb) {
-        int ml = 2 * stage_bytes(gb);
+    static_assert(FN % 2 == 0, "SwiGLU tiles pair gate/up fragments within a wave");
+    // bytes of one LDS stage (A tile and B tile of one BK slab)
+    static constexpr int stage_bytes() { return (BM + BN) * BK * 2; }
+    static constexpr int lds_bytes() {
+        int ml = 2 * stage_bytes();
         int ep = BM * (BN + 8) * 2;
         return ml > ep ? ml : ep;
     }
@@ -162,110 +168,165 @@ __device__ __forceinline__ uint32_t atomic_load_relaxed(const uint32_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wave-level wait: lane 0 polls `*p` until (int)(*p - target) >= 0, with
-// s_sleep back-off, giving up after `limit` polls or when another consumer
-// has already given up (status != 0).  Afterwards the whole wave takes an
-// agent-scope acquire fence so its later loads see the producer's data.
-// Returns true if the condition was met.
-__device__ __forceinline__ bool wave_wait_geq(const uint32_t* p, uint32_t target, uint32_t* status,
-                                              uint32_t limit) {
-    const int lane = threadIdx.x & 63;
-    uint32_t ok = 1;
-    if (lane == 0) {
-        uint32_t v = atomic_load_relaxed(p);
-        if ((int32_t)(v - target) < 0) {
-            uint32_t n = 0;
-            for (;;) {
-                __builtin_amdgcn_s_sleep(2);
-                v = atomic_load_relaxed(p);
-                if ((int32_t)(v - target) >= 0) break;
-                if (++n >= limit || atomic_load_relaxed(status) != 0) {
-                    __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    ok = 0;
-                    break;
-                }
-            }
+// Number of consecutive ready flags starting at index `from` (of `n`),
+// polled by one whole wave: lane i reads flag from+i with a relaxed
+// agent-scope load, and a ballot counts the leading run of flags that carry
+// `epoch`.  Windows of 64 flags are scanned until one is not full.
+__device__ __forceinline__ uint32_t wave_count_ready(const uint32_t* flags, uint32_t from, uint32_t n,
+                                                     uint32_t epoch) {
+    const uint32_t lane = threadIdx.x & 63;
+    uint32_t r = from;
+    while (r < n) {
+        const uint32_t idx = r + lane;
+        bool ok = false;
+        if (idx < n) ok = (int32_t)(atomic_load_relaxed(flags + idx) - epoch) >= 0;
+        const uint64_t b = __ballot(ok);
+        const uint32_t lead = (~b == 0) ? 64u : (uint32_t)__builtin_ctzll(~b);
+        r += lead;
+        if (lead < 64) break;
+    }
+    return r < n ? r : n;
+}
+
+// Called by ONE whole wave: flags [0, from) are already acquired; wait
+// until flags from..need are all ready (polling from `from`, s_sleep
+// back-off), then take an agent-scope acquire fence so that the workgroup's
+// later loads see the producers' data.  Returns the first flag index not
+// known ready (> need), or n if the wait gave up (status records it).
+__device__ __forceinline__ uint32_t wave_acquire_flags(const uint32_t* flags, uint32_t from, uint32_t need,
+                                                       uint32_t n, uint32_t epoch, uint32_t* status,
+                                                       uint32_t limit) {
+    uint32_t r = wave_count_ready(flags, from, n, epoch);
+    uint32_t polls = 0;
+    while (r <= need) {
+        __builtin_amdgcn_s_sleep(2);
+        r = wave_count_ready(flags, r, n, epoch);
+        if (r <= need && (++polls >= limit || atomic_load_relaxed(status) != 0)) {
+            if ((threadIdx.x & 63) == 0)
+                __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            r = n;
+            break;
         }
     }
-    ok = __builtin_amdgcn_readfirstlane(ok);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    return ok != 0;
+    return r;
+}
+
+// Called by ONE whole wave: wait until the counter reaches `target`
+// ((int32)(count - target) >= 0), then acquire.  Returns false on timeout.
+__device__ __forceinline__ bool wave_acquire_count(const uint32_t* cnt, uint32_t target, uint32_t* status,
+                                                   uint32_t limit) {
+    bool ok = true;
+    uint32_t polls = 0;
+    while ((int32_t)(atomic_load_relaxed(cnt) - target) < 0) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++polls >= limit || atomic_load_relaxed(status) != 0) {
+            if ((threadIdx.x & 63) == 0)
+                __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ok = false;
+            break;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return ok;
 }
 
 // ---------------------------------------------------------------- main loop
 
-// Loads of one BK slab into registers.
-//  A: [rows, K] row-major, tile rows m0..m0+BM-1 (rows >= a_rows read as 0)
-//  B: [K, ldb] row-major; tile column block n0..n0+BN-1 (and, for GB == 2, the
-//     up block at column b_up + n0...), columns >= b_cols (per half) read as 0.
-template <class C, int GB>
+// One tile's operands.  The same main loop serves both GEMMs, so producer
+// and consumer tiles of the persistent kernel share one copy of the code.
+//   A: [a_rows, K] row-major (lda), tile rows m0..m0+BM-1; rows >= a_rows read as 0
+//   B: [K, ldb] row-major.  The tile's BN B-columns are, for a plain tile,
+//      the output columns n0..n0+BN-1; for an interleaved (SwiGLU) tile the
+//      16-column fragments alternate gate / up: fragment 2j is output
+//      columns n0+16j..n0+16j+15 of the gate half, fragment 2j+1 the same
+//      output columns of the up half (global column + up).  Output columns
+//      >= b_cols read as 0.
+struct TileJob {
+    const uint16_t* A;
+    const uint16_t* B;
+    int lda, a_rows, m0;
+    int ldb, b_cols, n0, up;
+    int K;
+    bool inter;
+};
+
+template <class C>
 struct SlabRegs {
     static constexpr int A_CHUNKS = C::BM * 8;                          // 16-byte chunks
     static constexpr int A_IT = (A_CHUNKS + C::NT - 1) / C::NT;
-    static constexpr int B_UNITS = 8 * (GB * C::BN / 8);                // 8x8 blocks
+    static constexpr int B_UNITS = C::BN;                              // 8x8 blocks: BN/8 columns x 8 k-rows
     static constexpr int B_IT = (B_UNITS + C::NT - 1) / C::NT;
     u32x4 a[A_IT];
     u32x4 b[B_IT][8];
 };
 
-template <class C, int GB>
-__device__ __forceinline__ void load_a(SlabRegs<C, GB>& r, const uint16_t* A, int lda, int a_rows,
-                                       int m0, int K, int k0) {
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < SlabRegs<C, GB>::A_IT; ++i) {
-        const int j = tid + i * C::NT;
-        const int row = j >> 3, c = j & 7;
-        const int gm = m0 + row, gk = k0 + c * 8;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (j < SlabRegs<C, GB>::A_CHUNKS && gm < a_rows && gk < K)
-            v = ld16(A + (size_t)gm * lda + gk);
-        r.a[i] = v;
+// Global column of B-tile column block nb (8 columns) and whether it is in range.
+__device__ __forceinline__ int b_column(const TileJob& j, int nb, bool& ok) {
+    if (j.inter) {
+        const int f = nb >> 1;                                   // 16-column fragment
+        const int oc = j.n0 + (f >> 1) * 16 + (nb & 1) * 8;       // output column
+        ok = oc < j.b_cols;
+        return oc + (f & 1) * j.up;
     }
+    const int oc = j.n0 + nb * 8;
+    ok = oc < j.b_cols;
+    return oc;
 }
 
-template <class C, int GB>
-__device__ __forceinline__ void load_b(SlabRegs<C, GB>& r, const uint16_t* B, int ldb, int b_cols,
-                                       int n0, int b_up, int K, int k0) {
+template <class C>
+__device__ __forceinline__ void load_slab(SlabRegs<C>& r, const TileJob& j, int k0, bool do_a, bool do_b) {
     const int tid = threadIdx.x;
-    constexpr int NB = GB * C::BN / 8;       // 8-column blocks across the (gate|up) tile
+    if (do_b) {
+        constexpr int NB = C::BN / 8;
 #pragma unroll
-    for (int i = 0; i < SlabRegs<C, GB>::B_IT; ++i) {
-        const int u = tid + i * C::NT;
-        const int nb = u % NB, kb = u / NB;
-        const int half = (GB == 2 && nb >= NB / 2) ? 1 : 0;
-        const int nloc = (nb - half * (NB / 2)) * 8;          // column within the half
-        const int gn = n0 + nloc;
-        const int gcol = gn + half * b_up;
-        const bool colok = (u < SlabRegs<C, GB>::B_UNITS) && gn < b_cols;
+        for (int i = 0; i < SlabRegs<C>::B_IT; ++i) {
+            const int u = tid + i * C::NT;
+            const int nb = u % NB, kb = u / NB;
+            bool ok;
+            const int gcol = b_column(j, nb, ok);
+            ok = ok && (u < SlabRegs<C>::B_UNITS);
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr) {
-            const int gk = k0 + kb * 8 + rr;
+            for (int rr = 0; rr < 8; ++rr) {
+                const int gk = k0 + kb * 8 + rr;
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (ok && gk < j.K) v = ld16(j.B + (size_t)gk * j.ldb + gcol);
+                r.b[i][rr] = v;
+            }
+        }
+    }
+    if (do_a) {
+#pragma unroll
+        for (int i = 0; i < SlabRegs<C>::A_IT; ++i) {
+            const int q = tid + i * C::NT;
+            const int row = q >> 3, c = q & 7;
+            const int gm = j.m0 + row, gk = k0 + c * 8;
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (colok && gk < K) v = ld16(B + (size_t)gk * ldb + gcol);
-            r.b[i][rr] = v;
+            if (q < SlabRegs<C>::A_CHUNKS && gm < j.a_rows && gk < j.K)
+                v = ld16(j.A + (size_t)gm * j.lda + gk);
+            r.a[i] = v;
         }
     }
 }
 
-template <class C, int GB>
-__device__ __forceinline__ void store_slab(const SlabRegs<C, GB>& r, char* stage) {
+template <class C>
+__device__ __forceinline__ void store_slab(const SlabRegs<C>& r, char* stage) {
     const int tid = threadIdx.x;
     char* sa = stage;
     char* sb = stage + C::BM * BK * 2;
 #pragma unroll
-    for (int i = 0; i < SlabRegs<C, GB>::A_IT; ++i) {
-        const int j = tid + i * C::NT;
-        if (j < SlabRegs<C, GB>::A_CHUNKS) lds_st16(sa, lds_off(j >> 3, j & 7), r.a[i]);
+    for (int i = 0; i < SlabRegs<C>::A_IT; ++i) {
+        const int q = tid + i * C::NT;
+        if (q < SlabRegs<C>::A_CHUNKS) lds_st16(sa, lds_off(q >> 3, q & 7), r.a[i]);
     }
-    constexpr int NB = GB * C::BN / 8;
+    constexpr int NB = C::BN / 8;
 #pragma unroll
-    for (int i = 0; i < SlabRegs<C, GB>::B_IT; ++i) {
+    for (int i = 0; i < SlabRegs<C>::B_IT; ++i) {
         const int u = tid + i * C::NT;
-        if (u < SlabRegs<C, GB>::B_UNITS) {
+        if (u < SlabRegs<C>::B_UNITS) {
             const int nb = u % NB, kb = u / NB;
-            // r.b[i][k] holds B[k][n0..n0+7] as 4 dwords, dword q = (col 2q | col 2q+1 << 16).
-            // Output row n (= 2q + s) needs B[0..7][n] packed as dwords (k 2p | k 2p+1 << 16).
+            // r.b[i][k] holds B[k][8 columns] as 4 dwords, dword q = (col 2q | col 2q+1 << 16).
+            // LDS row n (= 2q + s) needs B[0..7][n] packed as dwords (k 2p | k 2p+1 << 16).
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 u32x4 lo, hi;
@@ -283,8 +344,8 @@ __device__ __forceinline__ void store_slab(const SlabRegs<C, GB>& r, char* stage
     }
 }
 
-template <class C, int DT, int GB>
-__device__ __forceinline__ void compute_slab(const char* stage, f32x4 (&acc)[GB][C::FM][C::FN]) {
+template <class C, int DT>
+__device__ __forceinline__ void compute_slab(const char* stage, f32x4 (&acc)[C::FM][C::FN]) {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave / C::WN, wn = wave % C::WN;
@@ -294,67 +355,61 @@ __device__ __forceinline__ void compute_slab(const char* stage, f32x4 (&acc)[GB]
     for (int kk = 0; kk < 2; ++kk) {
         const int chunk = kk * 4 + (lane >> 4);
         u32x4 af[C::FM];
-        u32x4 bf[GB][C::FN];
+        u32x4 bf[C::FN];
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm)
             af[fm] = lds_ld16(sa, lds_off(wm * C::WTM + fm * 16 + (lane & 15), chunk));
 #pragma unroll
-        for (int g = 0; g < GB; ++g)
-#pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn)
-                bf[g][fn] = lds_ld16(sb, lds_off(g * C::BN + wn * C::WTN + fn * 16 + (lane & 15), chunk));
-#pragma unroll
-        for (int g = 0; g < GB; ++g)
-#pragma unroll
-            for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-                for (int fn = 0; fn < C::FN; ++fn)
-                    acc[g][fm][fn] = mfma16x16x32<DT>(af[fm], bf[g][fn], acc[g][fm][fn]);
-    }
-}
-
-// The K loop of one tile.  `wait(ks)` is called by every wave before the
-// A-operand loads of slab ks (the consumer's dependency on the producer);
-// the B-operand (weight) loads of that slab are issued before the wait.
-template <class C, int DT, int GB, class Wait>
-__device__ __forceinline__ void tile_mainloop(const uint16_t* A, int lda, int a_rows, int m0,
-                                              const uint16_t* B, int ldb, int b_cols, int n0, int b_up,
-                                              int K, f32x4 (&acc)[GB][C::FM][C::FN], char* smem,
-                                              Wait&& wait) {
-#pragma unroll
-    for (int g = 0; g < GB; ++g)
+        for (int fn = 0; fn < C::FN; ++fn)
+            bf[fn] = lds_ld16(sb, lds_off(wn * C::WTN + fn * 16 + (lane & 15), chunk));
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn) acc[g][fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int fn = 0; fn < C::FN; ++fn)
+                acc[fm][fn] = mfma16x16x32<DT>(af[fm], bf[fn], acc[fm][fn]);
+    }
+}
 
-    constexpr int SB = C::stage_bytes(GB);
-    const int nks = (K + BK - 1) / BK;
-    SlabRegs<C, GB> r;
-    load_b<C, GB>(r, B, ldb, b_cols, n0, b_up, K, 0);
+// The K loop of one tile.  `wait(ks)` is called (uniformly) before the
+// A-operand loads of slab ks -- the consumer's dependency on its producers;
+// the B-operand (weight) loads of that slab are issued before the wait.
+template <class C, int DT, class Wait>
+__device__ __forceinline__ void tile_mainloop(const TileJob& j, f32x4 (&acc)[C::FM][C::FN], char* smem,
+                                              Wait&& wait) {
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    constexpr int SB = C::stage_bytes();
+    const int nks = (j.K + BK - 1) / BK;
+    SlabRegs<C> r;
+    load_slab<C>(r, j, 0, false, true);
     wait(0);
-    load_a<C, GB>(r, A, lda, a_rows, m0, K, 0);
-    store_slab<C, GB>(r, smem);
+    load_slab<C>(r, j, 0, true, false);
+    store_slab<C>(r, smem);
     __syncthreads();
     for (int ks = 0; ks < nks; ++ks) {
         char* cur = smem + (ks & 1) * SB;
         char* nxt = smem + ((ks + 1) & 1) * SB;
         const bool more = ks + 1 < nks;
         if (more) {
-            load_b<C, GB>(r, B, ldb, b_cols, n0, b_up, K, (ks + 1) * BK);
+            load_slab<C>(r, j, (ks + 1) * BK, false, true);
             wait(ks + 1);
-            load_a<C, GB>(r, A, lda, a_rows, m0, K, (ks + 1) * BK);
+            load_slab<C>(r, j, (ks + 1) * BK, true, false);
         }
-        compute_slab<C, DT, GB>(cur, acc);
-        if (more) store_slab<C, GB>(r, nxt);
+        compute_slab<C, DT>(cur, acc);
+        if (more) store_slab<C>(r, nxt);
         __syncthreads();
     }
 }
 
 // Epilogue: activation on the fp32 accumulators, RNE to the storage dtype,
 // staged through LDS, 16-byte stores of rows < rows and columns < cols.
-template <class C, int DT, int GB>
-__device__ __forceinline__ void tile_epilogue(const f32x4 (&acc)[GB][C::FM][C::FN], int act,
+// For an interleaved (SwiGLU) tile, fragment pairs (2j, 2j+1) hold gate and
+// up of the same output columns and the tile is BN/2 columns wide.
+template <class C, int DT>
+__device__ __forceinline__ void tile_epilogue(const f32x4 (&acc)[C::FM][C::FN], int act, bool inter,
                                               uint16_t* D, int ldd, int rows, int cols, int m0, int n0,
                                               char* smem) {
     const int lane = threadIdx.x & 63;
@@ -362,27 +417,37 @@ __device__ __forceinline__ void tile_epilogue(const f32x4 (&acc)[GB][C::FM][C::F
     const int wm = wave / C::WN, wn = wave % C::WN;
     constexpr int LD = C::BN + 8;     // padded LDS row (elements)
     uint16_t* s = reinterpret_cast<uint16_t*>(smem);
+    if (inter) {
 #pragma unroll
-    for (int fm = 0; fm < C::FM; ++fm)
+        for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
+            for (int fn = 0; fn < C::FN; fn += 2)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float v;
-                if constexpr (GB == 2) {
-                    v = silu(acc[0][fm][fn][i]) * acc[1][fm][fn][i];
-                } else {
-                    v = acc[0][fm][fn][i];
-                    if (act == ACT_GELU_TANH) v = gelu_tanh(v);
+                for (int i = 0; i < 4; ++i) {
+                    const float v = silu(acc[fm][fn][i]) * acc[fm][fn + 1][i];
+                    const int row = wm * C::WTM + fm * 16 + (lane >> 4) * 4 + i;
+                    const int col = (wn * C::WTN + fn * 16) / 2 + (lane & 15);
+                    s[row * LD + col] = to_storage<DT>(v);
                 }
-                const int row = wm * C::WTM + fm * 16 + (lane >> 4) * 4 + i;
-                const int col = wn * C::WTN + fn * 16 + (lane & 15);
-                s[row * LD + col] = to_storage<DT>(v);
-            }
+    } else {
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v = acc[fm][fn][i];
+                    if (act == ACT_GELU_TANH) v = gelu_tanh(v);
+                    const int row = wm * C::WTM + fm * 16 + (lane >> 4) * 4 + i;
+                    const int col = wn * C::WTN + fn * 16 + (lane & 15);
+                    s[row * LD + col] = to_storage<DT>(v);
+                }
+    }
     __syncthreads();
-    constexpr int CHUNKS = C::BM * C::BN / 8;
-    for (int j = threadIdx.x; j < CHUNKS; j += C::NT) {
-        const int row = j / (C::BN / 8), c = j % (C::BN / 8);
+    const int width = inter ? C::BN / 2 : C::BN;
+    const int cpr = width / 8;                    // 16-byte chunks per row
+    for (int q = threadIdx.x; q < C::BM * cpr; q += C::NT) {
+        const int row = q / cpr, c = q % cpr;
         const int gm = m0 + row, gn = n0 + c * 8;
         if (gm < rows && gn < cols) {
             const u32x4 v = *reinterpret_cast<const u32x4*>(s + row * LD + c * 8);
@@ -396,23 +461,37 @@ struct NoWait {
     __device__ __forceinline__ void operator()(int) const {}
 };
 
-// Producer tile (GEMM1 + activation) writing T; returns after the stores.
-template <class C, int DT, int GB>
-__device__ __forceinline__ void producer_tile(const ChainArgs& a, uint32_t mb, uint32_t nb, char* smem) {
-    f32x4 acc[GB][C::FM][C::FN];
-    const int m0 = (int)mb * C::BM, n0 = (int)nb * C::BN;
-    tile_mainloop<C, DT, GB>(a.x, a.H, a.M, m0, a.w1, GB * a.I, a.I, n0, a.I, a.H, acc, smem, NoWait{});
-    tile_epilogue<C, DT, GB>(acc, a.act, a.t, a.I, a.M, a.I, m0, n0, smem);
+// Output width of a GEMM1 (producer) tile: BN, or BN/2 for SwiGLU.
+template <class C>
+__device__ __forceinline__ int producer_width(const ChainArgs& a) {
+    return a.act == ACT_SWIGLU ? C::BN / 2 : C::BN;
 }
 
-// Consumer tile (GEMM2) reading T, writing Y.
+template <class C>
+__device__ __forceinline__ TileJob producer_job(const ChainArgs& a, uint32_t mb, uint32_t nb) {
+    const bool inter = a.act == ACT_SWIGLU;
+    return TileJob{a.x, a.w1, a.H, a.M, (int)mb * C::BM,
+                   (inter ? 2 : 1) * a.I, a.I, (int)nb * producer_width<C>(a), inter ? a.I : 0,
+                   a.H, inter};
+}
+
+template <class C>
+__device__ __forceinline__ TileJob consumer_job(const ChainArgs& a, uint32_t mb, uint32_t nb) {
+    return TileJob{a.t, a.w2, a.I, a.M, (int)mb * C::BM, a.H, a.H, (int)nb * C::BN, 0, a.I, false};
+}
+
+// One tile of either GEMM.  `role` 1 = producer (X W1 -> act -> T),
+// 2 = consumer (T W2 -> Y); `wait` is only exercised by consumers.
 template <class C, int DT, class Wait>
-__device__ __forceinline__ void consumer_tile(const ChainArgs& a, uint32_t mb, uint32_t nb, char* smem,
-                                              Wait&& wait) {
-    f32x4 acc[1][C::FM][C::FN];
-    const int m0 = (int)mb * C::BM, n0 = (int)nb * C::BN;
-    tile_mainloop<C, DT, 1>(a.t, a.I, a.M, m0, a.w2, a.H, a.H, n0, 0, a.I, acc, smem, wait);
-    tile_epilogue<C, DT, 1>(acc, ACT_NONE, a.y, a.H, a.M, a.H, m0, n0, smem);
+__device__ __forceinline__ void run_tile(const ChainArgs& a, int role, uint32_t mb, uint32_t nb, char* smem,
+                                         Wait&& wait) {
+    f32x4 acc[C::FM][C::FN];
+    const TileJob j = role == 1 ? producer_job<C>(a, mb, nb) : consumer_job<C>(a, mb, nb);
+    tile_mainloop<C, DT>(j, acc, smem, wait);
+    if (role == 1)
+        tile_epilogue<C, DT>(acc, a.act, j.inter, a.t, a.I, a.M, a.I, j.m0, j.n0, smem);
+    else
+        tile_epilogue<C, DT>(acc, ACT_NONE, false, a.y, a.H, a.M, a.H, j.m0, j.n0, smem);
 }
 
 }  // namespace mlpc

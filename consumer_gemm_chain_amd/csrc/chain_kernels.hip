@@ -20,16 +20,16 @@
 
 namespace mlpc {
 
-using Cfg0 = TileCfg<16, 64, 1, 4>;     // small M: narrow tiles, weight streaming
-using Cfg1 = TileCfg<64, 128, 2, 2>;    // medium M
-using Cfg2 = TileCfg<128, 128, 2, 2>;   // large M
+using Cfg0 = TileCfg<16, 64, 1, 2, 3>;     // small M: narrow tiles, weight streaming
+using Cfg1 = TileCfg<64, 128, 2, 2, 2>;    // medium M
+using Cfg2 = TileCfg<128, 128, 2, 2, 2>;   // large M
 
-template <class C, int DT, int GB>
+template <class C, int DT>
 __global__ __launch_bounds__(C::NT) void gemm1_act_kernel(ChainArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     uint32_t mb, nb;
     tile_coords(blockIdx.x, a.Mt, a.N1t, a.group_m, mb, nb);
-    producer_tile<C, DT, GB>(a, mb, nb, smem);
+    run_tile<C, DT>(a, 1, mb, nb, smem, NoWait{});
 }
 
 template <class C, int DT>
@@ -37,40 +37,60 @@ __global__ __launch_bounds__(C::NT) void gemm2_kernel(ChainArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     uint32_t mb, nb;
     tile_coords(blockIdx.x, a.Mt, a.N2t, a.group_m, mb, nb);
-    consumer_tile<C, DT>(a, mb, nb, smem, NoWait{});
+    run_tile<C, DT>(a, 2, mb, nb, smem, NoWait{});
 }
 
-// row_sync: wait once, before the first slab, until all N1t producer tiles
-// of the row block have counted themselves in for this epoch.
-struct RowWait {
-    const uint32_t* cnt;
-    uint32_t target;
+// Consumer-side wait of the persistent kernel.  One functor type serves
+// producer tiles (inactive) and consumer tiles, so the kernel holds a single
+// inlined copy of the tile main loop.  Only wave 0 polls and takes the
+// acquire fence; the result reaches the other waves through LDS behind a
+// barrier, so one L2 invalidation covers the whole workgroup.
+//   row_sync:  before slab 0, wait until all N1t producer tiles of the row
+//              block have counted themselves in for this epoch;
+//   tile_sync: before slab ks, make sure every producer column block that
+//              slab reads has been acquired; if not, wave 0 waits for it and
+//              acquires every block that is ready by then in one go.  Slabs
+//              are still taken in ascending K order.
+template <int POL>
+struct ChainWait {
+    bool active;             // consumer tile (uniform)
+    const uint32_t* flags;   // tile_sync: the row block's N1t flags
+    const uint32_t* cnt;     // row_sync: the row block's counter
+    uint32_t n1t;
+    uint32_t target;         // tile_sync: epoch; row_sync: epoch * N1t
+    int bn1;                 // output columns per producer tile
     uint32_t* status;
     uint32_t limit;
-    __device__ __forceinline__ void operator()(int ks) const {
-        if (ks == 0) wave_wait_geq(cnt, target, status, limit);
+    uint32_t* s_ready;       // LDS broadcast slot
+    uint32_t ready;          // producer blocks acquired so far (uniform)
+    __device__ __forceinline__ void operator()(int ks) {
+        if (!active) return;
+        if constexpr (POL == POL_ROW) {
+            if (ks != 0) return;
+            if ((threadIdx.x >> 6) == 0) wave_acquire_count(cnt, target, status, limit);
+            __syncthreads();
+        } else {
+            uint32_t need = (uint32_t)((ks * BK + BK - 1) / bn1);    // last block slab ks reads
+            if (need > n1t - 1) need = n1t - 1;
+            if (need < ready) return;
+            if ((threadIdx.x >> 6) == 0) {
+                const uint32_t r = wave_acquire_flags(flags, ready, need, n1t, target, status, limit);
+                if (threadIdx.x == 0) *s_ready = r;
+            }
+            __syncthreads();
+            ready = __builtin_amdgcn_readfirstlane(*s_ready);
+        }
     }
 };
 
-// tile_sync: before the first slab of each producer tile's column block,
-// wait for that tile's flag to carry this epoch.  Slabs are taken in
-// ascending K order regardless of which producer finishes first.
-struct TileWait {
-    const uint32_t* flags;   // the row block's N1t flags
-    uint32_t epoch;
-    int per;                 // K slabs per producer tile (BN / BK)
-    uint32_t* status;
-    uint32_t limit;
-    __device__ __forceinline__ void operator()(int ks) const {
-        if (ks % per == 0) wave_wait_geq(flags + ks / per, epoch, status, limit);
-    }
-};
-
-template <class C, int DT, int GB, int POL>
-__global__ __launch_bounds__(C::NT) void chain_persistent_kernel(ChainArgs a) {
+template <class C, int DT, int POL>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
+void chain_persistent_kernel(ChainArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem[];
     __shared__ uint32_t s_ticket;
+    __shared__ uint32_t s_ready;
     const uint32_t total = a.T1 + a.T2;
+    const int bn1 = a.act == ACT_SWIGLU ? C::BN / 2 : C::BN;
     for (;;) {
         if (threadIdx.x == 0)
             s_ticket = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
@@ -83,14 +103,22 @@ __global__ __launch_bounds__(C::NT) void chain_persistent_kernel(ChainArgs a) {
         const uint32_t t = __builtin_amdgcn_readfirstlane(s_ticket);
         __syncthreads();
         if (t >= total) break;
-        if (t < a.T1) {
-            if (t != a.skip_producer) {      // test hook: a skipped tile does no work and no release
-                uint32_t mb, nb;
+        const bool prod = t < a.T1;
+        // test hook: a skipped producer tile does no work and no release
+        if (!(prod && t == a.skip_producer)) {
+            uint32_t mb, nb;
+            if (prod)
                 tile_coords(t, a.Mt, a.N1t, a.group_m, mb, nb);
-                producer_tile<C, DT, GB>(a, mb, nb, smem);
-                // every thread's T stores are performed at agent scope before the
-                // single release that publishes the tile
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            else
+                tile_coords(t - a.T1, a.Mt, a.N2t, a.group_m, mb, nb);
+            ChainWait<POL> w{!prod, a.flags + mb * a.N1t, a.rowcnt + mb, a.N1t,
+                             POL == POL_ROW ? a.epoch * a.N1t : a.epoch, bn1, a.status, a.spin_limit,
+                             &s_ready, 0u};
+            run_tile<C, DT>(a, prod ? 1 : 2, mb, nb, smem, w);
+            if (prod) {
+                // every thread's T stores happen before thread 0's agent-scope
+                // release (workgroup release + barrier), which publishes the tile
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
                 __syncthreads();
                 if (threadIdx.x == 0) {
                     if constexpr (POL == POL_TILE)
@@ -99,16 +127,6 @@ __global__ __launch_bounds__(C::NT) void chain_persistent_kernel(ChainArgs a) {
                     else
                         __hip_atomic_fetch_add(a.rowcnt + mb, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
                 }
-            }
-        } else {
-            uint32_t mb, nb;
-            tile_coords(t - a.T1, a.Mt, a.N2t, a.group_m, mb, nb);
-            if constexpr (POL == POL_TILE) {
-                TileWait w{a.flags + mb * a.N1t, a.epoch, C::BN / BK, a.status, a.spin_limit};
-                consumer_tile<C, DT>(a, mb, nb, smem, w);
-            } else {
-                RowWait w{a.rowcnt + mb, a.epoch * a.N1t, a.status, a.spin_limit};
-                consumer_tile<C, DT>(a, mb, nb, smem, w);
             }
         }
         // Keep this barrier: it separates the thread-0-only release above from
@@ -129,32 +147,29 @@ static hipError_t prep(K kernel, int lds) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, lds);
 }
 
-template <class C, int DT, int GB>
+template <class C, int DT>
 static hipError_t launch_t(const ChainArgs& a, int what, int grid, hipStream_t s, int* occ) {
-    constexpr int lds = C::lds_bytes(GB);
+    constexpr int lds = C::lds_bytes();
     hipError_t e = hipSuccess;
     switch (what) {
     case LAUNCH_GEMM1: {
-        auto k = gemm1_act_kernel<C, DT, GB>;
+        auto k = gemm1_act_kernel<C, DT>;
         if ((e = prep(k, lds)) != hipSuccess) return e;
         hipLaunchKernelGGL(k, dim3(a.T1), dim3(C::NT), lds, s, a);
         return hipGetLastError();
     }
     case LAUNCH_GEMM2: {
         auto k = gemm2_kernel<C, DT>;
-        constexpr int lds2 = C::lds_bytes(1);
-        if ((e = prep(k, lds2)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k, dim3(a.T2), dim3(C::NT), lds2, s, a);
+        if ((e = prep(k, lds)) != hipSuccess) return e;
+        hipLaunchKernelGGL(k, dim3(a.T2), dim3(C::NT), lds, s, a);
         return hipGetLastError();
     }
     case LAUNCH_ROW:
     case LAUNCH_TILE: {
-        auto k = (what == LAUNCH_ROW) ? chain_persistent_kernel<C, DT, GB, POL_ROW>
-                                      : chain_persistent_kernel<C, DT, GB, POL_TILE>;
+        auto k = (what == LAUNCH_ROW) ? chain_persistent_kernel<C, DT, POL_ROW>
+                                      : chain_persistent_kernel<C, DT, POL_TILE>;
         if ((e = prep(k, lds)) != hipSuccess) return e;
-        if (occ) {
-            return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, k, C::NT, lds);
-        }
+        if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, k, C::NT, lds);
         hipLaunchKernelGGL(k, dim3(grid), dim3(C::NT), lds, s, a);
         return hipGetLastError();
     }
@@ -164,26 +179,24 @@ static hipError_t launch_t(const ChainArgs& a, int what, int grid, hipStream_t s
 }
 
 template <class C>
-static hipError_t launch_c(const ChainArgs& a, int dtype, int gb, int what, int grid, hipStream_t s,
-                           int* occ) {
-    if (dtype == DT_F16)
-        return gb == 2 ? launch_t<C, DT_F16, 2>(a, what, grid, s, occ) : launch_t<C, DT_F16, 1>(a, what, grid, s, occ);
-    return gb == 2 ? launch_t<C, DT_BF16, 2>(a, what, grid, s, occ) : launch_t<C, DT_BF16, 1>(a, what, grid, s, occ);
+static hipError_t launch_c(const ChainArgs& a, int dtype, int what, int grid, hipStream_t s, int* occ) {
+    return dtype == DT_F16 ? launch_t<C, DT_F16>(a, what, grid, s, occ)
+                           : launch_t<C, DT_BF16>(a, what, grid, s, occ);
 }
 
-static hipError_t dispatch(const ChainArgs& a, int cfg, int dtype, int gb, int what, int grid,
-                           hipStream_t s, int* occ) {
+static hipError_t dispatch(const ChainArgs& a, int cfg, int dtype, int what, int grid, hipStream_t s,
+                           int* occ) {
     switch (cfg) {
-    case 0: return launch_c<Cfg0>(a, dtype, gb, what, grid, s, occ);
-    case 1: return launch_c<Cfg1>(a, dtype, gb, what, grid, s, occ);
-    case 2: return launch_c<Cfg2>(a, dtype, gb, what, grid, s, occ);
+    case 0: return launch_c<Cfg0>(a, dtype, what, grid, s, occ);
+    case 1: return launch_c<Cfg1>(a, dtype, what, grid, s, occ);
+    case 2: return launch_c<Cfg2>(a, dtype, what, grid, s, occ);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <class C>
 static CfgInfo info_of(int id) {
-    return CfgInfo{id, C::BM, C::BN, BK, C::NT, C::lds_bytes(1), C::lds_bytes(2)};
+    return CfgInfo{id, C::BM, C::BN, BK, C::NT, C::lds_bytes()};
 }
 
 }  // namespace mlpc
@@ -197,15 +210,15 @@ CfgInfo mlpc_config_info(int id) {
     case 0: return info_of<Cfg0>(0);
     case 1: return info_of<Cfg1>(1);
     case 2: return info_of<Cfg2>(2);
-    default: return CfgInfo{-1, 0, 0, 0, 0, 0, 0};
+    default: return CfgInfo{-1, 0, 0, 0, 0, 0};
     }
 }
 
-hipError_t mlpc_launch(const ChainArgs& a, int cfg, int dtype, int gb, int what, int grid, hipStream_t s) {
-    return dispatch(a, cfg, dtype, gb, what, grid, s, nullptr);
+hipError_t mlpc_launch(const ChainArgs& a, int cfg, int dtype, int what, int grid, hipStream_t s) {
+    return dispatch(a, cfg, dtype, what, grid, s, nullptr);
 }
 
-hipError_t mlpc_persistent_occupancy(int cfg, int dtype, int gb, int policy, int* per_cu) {
+hipError_t mlpc_persistent_occupancy(int cfg, int dtype, int policy, int* per_cu) {
     ChainArgs dummy{};
-    return dispatch(dummy, cfg, dtype, gb, policy == POL_ROW ? LAUNCH_ROW : LAUNCH_TILE, 0, nullptr, per_cu);
+    return dispatch(dummy, cfg, dtype, policy == POL_ROW ? LAUNCH_ROW : LAUNCH_TILE, 0, nullptr, per_cu);
 }

@@ -10,9 +10,8 @@ enum { LAUNCH_GEMM1 = 1, LAUNCH_GEMM2 = 2, LAUNCH_ROW = 3, LAUNCH_TILE = 4 };
 
 struct CfgInfo {
     int id;
-    int BM, BN, BK, NT;
-    int lds_g1;   // LDS bytes with one B column block (GeLU / none producers, all consumers)
-    int lds_g2;   // LDS bytes with gate + up column blocks (SwiGLU producers)
+    int BM, BN, BK, NT;   // BN: weight columns per tile (SwiGLU producers: BN/2 output columns)
+    int lds;              // dynamic LDS bytes per workgroup
 };
 
 int mlpc_num_configs();
@@ -20,8 +19,7 @@ CfgInfo mlpc_config_info(int id);
 
 // Launch one kernel of the chain.  `what` is LAUNCH_GEMM1 (grid a.T1),
 // LAUNCH_GEMM2 (grid a.T2) or a persistent kernel (grid `grid`).
-hipError_t mlpc_launch(const mlpc::ChainArgs& a, int cfg, int dtype, int gb, int what, int grid,
-                       hipStream_t s);
+hipError_t mlpc_launch(const mlpc::ChainArgs& a, int cfg, int dtype, int what, int grid, hipStream_t s);
 
 // Resident workgroups per CU of the persistent kernel for a configuration.
-hipError_t mlpc_persistent_occupancy(int cfg, int dtype, int gb, int policy, int* per_cu);
+hipError_t mlpc_persistent_occupancy(int cfg, int dtype, int policy, int* per_cu);

@@ -125,25 +125,33 @@ def test_linear_in_w2_on_gpu():
         assert np.array_equal(y4[normal], 4 * y1[normal])
 
 
-def test_repeated_runs_are_bit_identical():
-    """Any data race on the intermediate or the flags would show up as
-    run-to-run differences; 40 back-to-back runs of each fused policy on one
-    handle (epochs advance) must match the stream-ordered output exactly."""
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+def test_repeated_runs_alternating_inputs(cfg):
+    """Race check: 40 back-to-back runs of each fused policy on one handle,
+    alternating between two inputs, must each equal the stream-ordered output
+    for their input exactly.  A consumer that read the intermediate before its
+    producer published it would see the other input's intermediate (left by
+    the previous run) and differ."""
     import torch
     from consumer_gemm_chain_amd.mlp_chain import MlpChain
     from tests._helpers import empty_dev, from_dev
     M, H, I, act, dtype = 512, 1024, 1536, "gelu_tanh", "f16"
-    x, w1, w2 = _case(M, H, I, act, dtype, seed=9)
-    dev = (to_dev(x, dtype), to_dev(w1, dtype), to_dev(w2, dtype))
-    ref = run_chain(x, w1, w2, act, dtype, "stream_ordered", dev=dev)
+    xa, w1, w2 = _case(M, H, I, act, dtype, seed=9)
+    xb = gen.normal_bits((M, H), 99, 1.0, dtype)
+    dw1, dw2 = to_dev(w1, dtype), to_dev(w2, dtype)
+    dxs = [to_dev(xa, dtype), to_dev(xb, dtype)]
+    refs = [run_chain(x, w1, w2, act, dtype, "stream_ordered", cfg=cfg, dev=(dx, dw1, dw2))
+            for x, dx in zip((xa, xb), dxs)]
+    assert not np.array_equal(refs[0], refs[1])
     for pol in ("row_sync", "tile_sync"):
         with MlpChain(M, H, I, act, dtype, pol) as ch:
+            ch.set_config(cfg)
             out = empty_dev((M, H), dtype)
             for i in range(40):
                 out.fill_(float("nan"))
-                ch.run(*dev, out)
+                ch.run(dxs[i % 2], dw1, dw2, out)
                 torch.cuda.synchronize()
-                assert np.array_equal(from_dev(out), ref), f"{pol} run {i}"
+                assert np.array_equal(from_dev(out), refs[i % 2]), f"{pol} cfg{cfg} run {i}"
             assert ch.status() == 0
             assert ch.info()["epoch"] == 40
 
@@ -166,15 +174,29 @@ FULL = [(1, 1), (1, 64), (1, 512), (1, 2048),
 def test_full_size_workloads(oracle_mod, wl, M):
     """Full-size workloads in the planner's launch configuration: the three
     policies agree bit for bit on the whole output, and sampled rows agree
-    with the oracle within tolerance."""
+    with the oracle within tolerance.  Each fused handle first runs once on a
+    decoy input (X with its rows reversed), so a consumer that read a stale
+    intermediate would read the decoy's and differ."""
     import torch
+    from consumer_gemm_chain_amd.mlp_chain import MlpChain
+    from tests._helpers import empty_dev, from_dev
     w = gen.WORKLOADS[wl]
     print(f"workload {w.name} M={M}", flush=True)
     w1, w2 = gen.weights(w)
     x = gen.x_rows(w, M)
-    dev = (to_dev(x, w.dtype), to_dev(w1, w.dtype), to_dev(w2, w.dtype))
-    outs = {pol: run_chain(x, w1, w2, w.act, w.dtype, pol, dev=dev) for pol in POLICIES}
-    del dev
+    dx, dw1, dw2 = to_dev(x, w.dtype), to_dev(w1, w.dtype), to_dev(w2, w.dtype)
+    decoy = torch.flip(dx, dims=[0]).contiguous() if M > 1 else torch.zeros_like(dx)
+    outs = {}
+    for pol in POLICIES:
+        with MlpChain(M, w.H, w.I, w.act, w.dtype, pol) as ch:
+            out = empty_dev((M, w.H), w.dtype)
+            ch.run(decoy, dw1, dw2, out)
+            out.fill_(float("nan"))
+            ch.run(dx, dw1, dw2, out)
+            torch.cuda.synchronize()
+            assert ch.status() == 0
+            outs[pol] = from_dev(out)
+    del dx, dw1, dw2, decoy
     torch.cuda.empty_cache()
     assert np.array_equal(outs["row_sync"], outs["stream_ordered"])
     assert np.array_equal(outs["tile_sync"], outs["stream_ordered"])
