@@ -22,7 +22,14 @@ LIB = os.path.join(LIBDIR, "libmlp_chain.so")
 BUILD = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["chain_kernels.hip", "chain_api.cpp"]
+SOURCES = ["chain_api.cpp", "chain_dispatch.cpp"]
+KERNELS = "chain_kernels.hip"     # compiled once per tile configuration
+
+
+def num_configs() -> int:
+    text = open(os.path.join(CSRC, "chain_configs.h")).read()
+    import re
+    return len(re.findall(r"^\s*X\(\d+,", text, flags=re.M))
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -40,9 +47,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the HIP library)")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-x", "hip", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job, verbose: bool) -> str:
+    src, cfg = job
+    tag = os.path.basename(src) + ("" if cfg is None else f".cfg{cfg}")
+    obj = os.path.join(BUILD, tag + ".o")
+    defs = [] if cfg is None else [f"-DMLPC_CFG={cfg}"]
+    cmd = [hipcc(), "-x", "hip", *FLAGS, *defs, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -52,8 +62,10 @@ def _compile(src: str, verbose: bool) -> str:
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    jobs = [(KERNELS, c) for c in range(num_configs())] + [(src, None) for src in SOURCES]
+    workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = list(ex.map(lambda j: _compile(j, verbose), jobs))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

@@ -47,11 +47,12 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 uint32_t cdiv(int64_t a, int64_t b) { return (uint32_t)((a + b - 1) / b); }
 
-// Planner: the smallest tiles while M is small (weight streaming wants many
-// workgroups), larger tiles when M grows and the matrix cores bound the run.
+// Planner: the narrow 16-row tiles while M is small (weight streaming wants
+// many workgroups), 128 x 128 tiles with two LDS stages (two workgroups per
+// CU) once M grows and the matrix cores bound the run.  The crossover was
+// measured on the GPT-3 shard (H=12288, I=6144) for M in 1..2048.
 int plan_config(int64_t M) {
-    if (M <= 32) return 0;
-    if (M <= 256) return 1;
+    if (M <= 96) return 0;
     return 2;
 }
 
@@ -76,6 +77,7 @@ struct mlp_chain {
     uint32_t* rowcnt;
     uint32_t* ticket;
     uint32_t* status;
+    uint16_t* zero;
     // run state
     uint32_t epoch;
     uint32_t ticket_base;
@@ -159,6 +161,7 @@ mlpc::ChainArgs make_args(const mlp_chain* h, const void* x, const void* w1, con
     a.flags = h->flags;
     a.rowcnt = h->rowcnt;
     a.status = h->status;
+    a.zero = h->zero;
     a.ticket_base = h->ticket_base;
     a.epoch = h->epoch;
     a.grid = h->grid;
@@ -249,7 +252,7 @@ mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype
     const size_t t_bytes = align_up((size_t)M * (size_t)I * 2, 256);
     const size_t f_bytes = align_up((size_t)max_t1 * 4, 256);
     const size_t r_bytes = align_up((size_t)max_mt * 4, 256);
-    h->ws_bytes = t_bytes + f_bytes + r_bytes + 256 + 256;
+    h->ws_bytes = t_bytes + f_bytes + r_bytes + 256 + 256 + 256;
     e = hipMalloc(&h->ws, h->ws_bytes);
     if (e != hipSuccess) {
         fail(MLP_ENOMEM, "hipMalloc of %zu workspace bytes failed: %s", h->ws_bytes, hipGetErrorString(e));
@@ -262,6 +265,7 @@ mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype
     h->rowcnt = reinterpret_cast<uint32_t*>(p + t_bytes + f_bytes);
     h->ticket = reinterpret_cast<uint32_t*>(p + t_bytes + f_bytes + r_bytes);
     h->status = reinterpret_cast<uint32_t*>(p + t_bytes + f_bytes + r_bytes + 256);
+    h->zero = reinterpret_cast<uint16_t*>(p + t_bytes + f_bytes + r_bytes + 512);
     if (zero_workspace(h) != MLP_OK) {
         (void)hipFree(h->ws);
         delete h;

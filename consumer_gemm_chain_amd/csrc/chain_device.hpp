@@ -4,18 +4,23 @@
 // stream-ordered pair and the persistent kernel), so all policies produce
 // bit-identical results:
 //   * MFMA main loop: v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulators,
-//     BK = 64 K-slab per step, K steps in ascending order, two LDS stages with
-//     register prefetch of the next slab.
-//   * LDS layout: every operand is stored K-contiguous, 8 chunks of 16 bytes
-//     per row, with the chunk index XOR-swizzled by the row so that both the
-//     16-byte fragment reads and the transposed writes avoid bank conflicts
-//     (the bank-conflict motivation for swizzling is the jonahsamost bearblog
-//     post on swizzling; the tile depth / staging discussion is its post on
-//     adding depth to a GEMM).
-//   * The weights are [K, N] row-major (N contiguous) while the matrix cores
-//     want K-contiguous fragments, so each thread loads an 8x8 block of
-//     16-bit values (eight 16-byte rows) and transposes it in registers with
-//     byte permutes before the LDS store.
+//     BK = 64 K-slab per step, K steps in ascending order.
+//   * Operand staging: both operands go from global memory straight into
+//     LDS (global_load_lds_dwordx4, no registers) through an NS-deep ring
+//     of LDS stages, so NS-1 slabs are in flight while one is computed (the
+//     pipeline depth of the jonahsamost bearblog post on adding depth to a
+//     GEMM).  Every stage is a separate LDS object so the compiler can tell
+//     the stages apart and does not drain the ring before each LDS read; the
+//     ring is synchronized by explicit vmcnt waits and bare barriers.
+//   * LDS layouts: the activation tile A is stored K-contiguous (8 chunks of
+//     16 bytes per row) and read as MFMA fragments with ds_read_b128; the
+//     weight tile B keeps the weights' [K, N] row-major layout and is read
+//     with the gfx950 transpose read ds_read_b64_tr_b16 (each 16-lane group
+//     reads a 4 x 16 block and receives it transposed).  Both use XOR chunk
+//     swizzles, applied by choosing which global chunk each lane fetches,
+//     against LDS bank conflicts (the bearblog post on swizzling).
+//   * Edges: chunks outside the matrices are fetched from a zero page, so
+//     the ring always holds zeros beyond M, N and K.
 //   * Epilogue: activation on the fp32 accumulators, one round-to-nearest-even
 //     conversion, staged through LDS and written with 16-byte stores (the
 //     registers -> shared memory -> global (M, N) epilogue of the bearblog
@@ -58,6 +63,7 @@ struct ChainArgs {
     uint32_t* flags;        // [Mt * N1t] ready epochs (tile_sync)
     uint32_t* rowcnt;       // [Mt] producer completions (row_sync)
     uint32_t* status;       // sticky watchdog status (nonzero = a consumer gave up)
+    const uint16_t* zero;   // >= 16 zero bytes: the source of every out-of-range chunk
     uint32_t ticket_base;   // tickets drawn by earlier runs (mod 2^32)
     uint32_t epoch;         // this run's epoch (mod 2^32)
     uint32_t grid;          // persistent workgroups
@@ -66,36 +72,40 @@ struct ChainArgs {
     int policy;
 };
 
-// Tile configuration: BM x BN tile, WM x WN waves of (BM/WM) x (BN/WN).  BN
-// is the number of B (weight) columns of a tile: its output width, except
-// for SwiGLU producer tiles, whose BN columns are gate/up pairs of BN/2
-// output columns.
-template <int BM_, int BN_, int WM_, int WN_, int OCC_>
+// Tile configuration: BM x BN tile, WM x WN waves of (BM/WM) x (BN/WN), NS
+// LDS stages.  BN is the number of B (weight) columns of a tile: its output
+// width, except for SwiGLU producer tiles, whose BN columns are gate/up
+// pairs of BN/2 output columns.
+template <int BM_, int BN_, int WM_, int WN_, int NS_, int OCC_>
 struct TileCfg {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-    // waves per SIMD the persistent kernel is register-limited to (the
-    // occupancy of the standalone GEMM2 kernel of the same tile)
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NS = NS_;
+    // waves per SIMD the persistent kernel is register-limited to
     static constexpr int OCC = OCC_;
-    static constexpr int NT = 64 * WM * WN;
+    static constexpr int NW = WM * WN;
+    static constexpr int NT = 64 * NW;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int FM = WTM / 16, FN = WTN / 16;
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16x16");
     static_assert(FN % 2 == 0, "SwiGLU tiles pair gate/up fragments within a wave");
-    // bytes of one LDS stage (A tile and B tile of one BK slab)
-    static constexpr int stage_bytes() { return (BM + BN) * BK * 2; }
-    static constexpr int lds_bytes() {
-        int ml = 2 * stage_bytes();
-        int ep = BM * (BN + 8) * 2;
-        return ml > ep ? ml : ep;
-    }
+    static_assert(NS >= 2 && NS <= 4, "2 to 4 LDS stages");
+    static constexpr int A_BYTES = BM * BK * 2;          // A slab: BM rows x 128 bytes
+    static constexpr int B_BYTES = BK * BN * 2;          // B slab: 64 k-rows x BN columns
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    // epilogue staging (padded rows) in EPI_PASSES row passes that each fit a stage
+    static constexpr int EPI_PASSES = BM * (BN + 8) * 2 <= STAGE ? 1 : BM * (BN + 8) * 2 <= 2 * STAGE ? 2 : 4;
+    static constexpr int EPI_ROWS = BM / EPI_PASSES;
+    static_assert(EPI_ROWS * (BN + 8) * 2 <= STAGE, "epilogue pass must fit one stage");
+    static constexpr int STAGE0 = STAGE;
+    static constexpr int CPR = BN / 8;                   // 16-byte chunks per B row
+    static constexpr int A_PER_WAVE = BM / 8 / NW;       // 1 KB DMA instructions per wave per slab
+    static constexpr int B_PER_WAVE = CPR / NW;
+    static_assert(A_PER_WAVE * NW * 8 == BM && B_PER_WAVE * NW == CPR, "DMA split across waves");
+    static constexpr int LPS = A_PER_WAVE + B_PER_WAVE;  // DMA instructions per wave per slab
+    static_assert(LPS * (NS - 2) <= 63, "vmcnt range");
+    static constexpr int lds_bytes() { return STAGE0 + (NS - 1) * STAGE; }
 };
 
 // ------------------------------------------------------------------ helpers
-
-// Byte offset of 16-byte chunk `c` (0..7) of LDS row `r` (rows of 64 elements).
-__device__ __forceinline__ int lds_off(int r, int c) {
-    return (r * 8 + (c ^ ((r ^ (r >> 3)) & 7))) * 16;
-}
 
 template <int DT>
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
@@ -144,9 +154,6 @@ __device__ __forceinline__ u32x4 lds_ld16(const char* smem, int off) {
     return *reinterpret_cast<const u32x4*>(smem + off);
 }
 
-__device__ __forceinline__ void lds_st16(char* smem, int off, u32x4 v) {
-    *reinterpret_cast<u32x4*>(smem + off) = v;
-}
 
 // Grouped tile order: walk GROUP row blocks down one column block before
 // moving to the next column block, so tiles that run together share weight
@@ -242,23 +249,15 @@ __device__ __forceinline__ bool wave_acquire_count(const uint32_t* cnt, uint32_t
 //      columns n0+16j..n0+16j+15 of the gate half, fragment 2j+1 the same
 //      output columns of the up half (global column + up).  Output columns
 //      >= b_cols read as 0.
+//   K slabs ks0..ks1-1 (BK = 64 each) are accumulated, in ascending order.
 struct TileJob {
     const uint16_t* A;
     const uint16_t* B;
+    const uint16_t* zero;
     int lda, a_rows, m0;
     int ldb, b_cols, n0, up;
-    int K;
+    int K, ks0, ks1;
     bool inter;
-};
-
-template <class C>
-struct SlabRegs {
-    static constexpr int A_CHUNKS = C::BM * 8;                          // 16-byte chunks
-    static constexpr int A_IT = (A_CHUNKS + C::NT - 1) / C::NT;
-    static constexpr int B_UNITS = C::BN;                              // 8x8 blocks: BN/8 columns x 8 k-rows
-    static constexpr int B_IT = (B_UNITS + C::NT - 1) / C::NT;
-    u32x4 a[A_IT];
-    u32x4 b[B_IT][8];
 };
 
 // Global column of B-tile column block nb (8 columns) and whether it is in range.
@@ -274,94 +273,109 @@ __device__ __forceinline__ int b_column(const TileJob& j, int nb, bool& ok) {
     return oc;
 }
 
+// The LDS stages of configuration C: one LDS object per stage (stage 0 also
+// holds the epilogue staging area).
+template <class C, int S>
+__device__ __forceinline__ char* lds_stage() {
+    __shared__ __attribute__((aligned(16))) char buf[S == 0 ? C::STAGE0 : C::STAGE];
+    return buf;
+}
+
+// Physical 16-byte chunk of logical chunk c in A row r (8 chunks per row).
+__device__ __forceinline__ int a_chunk(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+
+// Physical chunk of logical chunk c in B row k.  A transpose read covers,
+// per 32 lanes, rows 8g + (0..3) for g in {0,1} (or {2,3}) and two adjacent
+// chunks per row; the XOR term 2*((k & 3) | ((k >> 3) & 1) << 2) gives those
+// 8 rows 8 distinct chunk pairs, so the 32 lanes hit 64 distinct banks when
+// a row has at least 16 chunks.
 template <class C>
-__device__ __forceinline__ void load_slab(SlabRegs<C>& r, const TileJob& j, int k0, bool do_a, bool do_b) {
-    const int tid = threadIdx.x;
-    if (do_b) {
-        constexpr int NB = C::BN / 8;
+__device__ __forceinline__ int b_chunk(int k, int c) {
+    return c ^ ((2 * ((k & 3) | (((k >> 3) & 1) << 2))) & (C::CPR - 1));
+}
+
+__device__ __forceinline__ void dma16(const uint16_t* src, char* lds) {
+    // (a C-style cast is the way to change the address space to LDS)
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                     (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
+}
+
+// Issue the DMA of slab ks (B part and/or A part) into stage S.  Every wave
+// issues B_PER_WAVE B instructions and A_PER_WAVE A instructions; lane i of
+// an instruction fills LDS chunk L0 + i, and picks the global chunk that
+// belongs there under the swizzle (or the zero page).
+template <class C, int S>
+__device__ __forceinline__ void issue_b(const TileJob& j, int ks) {
+    char* st = lds_stage<C, S>() + C::A_BYTES;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int k0 = ks * BK;
 #pragma unroll
-        for (int i = 0; i < SlabRegs<C>::B_IT; ++i) {
-            const int u = tid + i * C::NT;
-            const int nb = u % NB, kb = u / NB;
-            bool ok;
-            const int gcol = b_column(j, nb, ok);
-            ok = ok && (u < SlabRegs<C>::B_UNITS);
-#pragma unroll
-            for (int rr = 0; rr < 8; ++rr) {
-                const int gk = k0 + kb * 8 + rr;
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (ok && gk < j.K) v = ld16(j.B + (size_t)gk * j.ldb + gcol);
-                r.b[i][rr] = v;
-            }
-        }
-    }
-    if (do_a) {
-#pragma unroll
-        for (int i = 0; i < SlabRegs<C>::A_IT; ++i) {
-            const int q = tid + i * C::NT;
-            const int row = q >> 3, c = q & 7;
-            const int gm = j.m0 + row, gk = k0 + c * 8;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (q < SlabRegs<C>::A_CHUNKS && gm < j.a_rows && gk < j.K)
-                v = ld16(j.A + (size_t)gm * j.lda + gk);
-            r.a[i] = v;
-        }
+    for (int q = 0; q < C::B_PER_WAVE; ++q) {
+        const int L0 = (wave * C::B_PER_WAVE + q) * 64;
+        const int L = L0 + lane;
+        const int k = L / C::CPR, p = L % C::CPR;
+        const int c = b_chunk<C>(k, p);
+        bool ok;
+        const int gcol = b_column(j, c, ok);
+        const int gk = k0 + k;
+        const uint16_t* src = (ok && gk < j.K) ? j.B + (size_t)gk * j.ldb + gcol : j.zero;
+        dma16(src, st + L0 * 16);
     }
 }
 
-template <class C>
-__device__ __forceinline__ void store_slab(const SlabRegs<C>& r, char* stage) {
-    const int tid = threadIdx.x;
-    char* sa = stage;
-    char* sb = stage + C::BM * BK * 2;
+template <class C, int S>
+__device__ __forceinline__ void issue_a(const TileJob& j, int ks) {
+    char* st = lds_stage<C, S>();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int k0 = ks * BK;
 #pragma unroll
-    for (int i = 0; i < SlabRegs<C>::A_IT; ++i) {
-        const int q = tid + i * C::NT;
-        if (q < SlabRegs<C>::A_CHUNKS) lds_st16(sa, lds_off(q >> 3, q & 7), r.a[i]);
-    }
-    constexpr int NB = C::BN / 8;
-#pragma unroll
-    for (int i = 0; i < SlabRegs<C>::B_IT; ++i) {
-        const int u = tid + i * C::NT;
-        if (u < SlabRegs<C>::B_UNITS) {
-            const int nb = u % NB, kb = u / NB;
-            // r.b[i][k] holds B[k][8 columns] as 4 dwords, dword q = (col 2q | col 2q+1 << 16).
-            // LDS row n (= 2q + s) needs B[0..7][n] packed as dwords (k 2p | k 2p+1 << 16).
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                u32x4 lo, hi;
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const uint32_t e = r.b[i][2 * p][q];
-                    const uint32_t o = r.b[i][2 * p + 1][q];
-                    lo[p] = __builtin_amdgcn_perm(o, e, 0x05040100u);   // low halves
-                    hi[p] = __builtin_amdgcn_perm(o, e, 0x07060302u);   // high halves
-                }
-                lds_st16(sb, lds_off(nb * 8 + 2 * q, kb), lo);
-                lds_st16(sb, lds_off(nb * 8 + 2 * q + 1, kb), hi);
-            }
-        }
+    for (int q = 0; q < C::A_PER_WAVE; ++q) {
+        const int L0 = (wave * C::A_PER_WAVE + q) * 64;
+        const int L = L0 + lane;
+        const int r = L >> 3, c = a_chunk(r, L & 7);
+        const int gm = j.m0 + r, gk = k0 + c * 8;
+        const uint16_t* src = (gm < j.a_rows && gk < j.K) ? j.A + (size_t)gm * j.lda + gk : j.zero;
+        dma16(src, st + L0 * 16);
     }
 }
 
-template <class C, int DT>
-__device__ __forceinline__ void compute_slab(const char* stage, f32x4 (&acc)[C::FM][C::FN]) {
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x2 lds_read_tr(const char* p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(const_cast<char*>(p))));
+}
+
+// MFMA over the slab in stage S.
+template <class C, int DT, int S>
+__device__ __forceinline__ void compute_stage(f32x4 (&acc)[C::FM][C::FN]) {
+    const char* sa = lds_stage<C, S>();
+    const char* sb = sa + C::A_BYTES;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave / C::WN, wn = wave % C::WN;
-    const char* sa = stage;
-    const char* sb = stage + C::BM * BK * 2;
+    const int g = lane >> 4, jj = lane & 15;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-        const int chunk = kk * 4 + (lane >> 4);
         u32x4 af[C::FM];
         u32x4 bf[C::FN];
 #pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
-            af[fm] = lds_ld16(sa, lds_off(wm * C::WTM + fm * 16 + (lane & 15), chunk));
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int r = wm * C::WTM + fm * 16 + jj;
+            af[fm] = lds_ld16(sa, (r * 8 + a_chunk(r, kk * 4 + g)) * 16);
+        }
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn)
-            bf[fn] = lds_ld16(sb, lds_off(wn * C::WTN + fn * 16 + (lane & 15), chunk));
+        for (int fn = 0; fn < C::FN; ++fn) {
+            // lane (g, jj): rows k = 32kk + 8g + 4h + jj/4, columns (jj%4)*4..+3 of the fragment
+            const int col = wn * C::WTN + fn * 16 + (jj & 3) * 4;
+            const int c = col >> 3, half = (col & 7) * 2;
+            const int k_lo = kk * 32 + g * 8 + (jj >> 2);
+            const int k_hi = k_lo + 4;
+            const u32x2 lo = lds_read_tr(sb + (k_lo * C::CPR + b_chunk<C>(k_lo, c)) * 16 + half);
+            const u32x2 hi = lds_read_tr(sb + (k_hi * C::CPR + b_chunk<C>(k_hi, c)) * 16 + half);
+            bf[fn] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
@@ -370,91 +384,134 @@ __device__ __forceinline__ void compute_slab(const char* stage, f32x4 (&acc)[C::
     }
 }
 
+// Wait until at most `n` DMA instructions of this wave are outstanding and
+// every LDS access of this wave has completed, then meet the other waves.
+// (A bare s_barrier: __syncthreads() would also wait for all DMA.)
+// The empty asm statements with a memory clobber and the scheduling
+// barriers keep the compiler from moving any memory access (in particular
+// LDS reads of the next stage) across the barrier.
+template <int N>
+__device__ __forceinline__ void ring_barrier() {
+    static_assert(N >= 0 && N <= 63, "vmcnt");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+
+// LDS-visible barrier that leaves the DMA ring in flight.
+__device__ __forceinline__ void lds_barrier() { ring_barrier<63>(); }
+
+template <class C, class Wait, int S>
+__device__ __forceinline__ void issue_slab(const TileJob& j, int ks, Wait& wait) {
+    issue_b<C, S>(j, ks);
+    wait(ks);
+    issue_a<C, S>(j, ks);
+}
+
+// One pipeline step: slab ks (in stage S) is computed while slabs ks+1 ..
+// ks+NS-1 are in flight.
+template <class C, int DT, int S, class Wait>
+__device__ __forceinline__ void pipe_step(const TileJob& j, int ks, f32x4 (&acc)[C::FM][C::FN], Wait& wait) {
+    // slab ks has landed once only the slabs issued after it remain in flight
+    if (ks + C::NS - 2 < j.ks1) ring_barrier<C::LPS * (C::NS - 2)>();
+    else ring_barrier<0>();
+    constexpr int SN = (S + C::NS - 1) % C::NS;
+    if (ks + C::NS - 1 < j.ks1) issue_slab<C, Wait, SN>(j, ks + C::NS - 1, wait);
+    compute_stage<C, DT, S>(acc);
+}
+
 // The K loop of one tile.  `wait(ks)` is called (uniformly) before the
-// A-operand loads of slab ks -- the consumer's dependency on its producers;
-// the B-operand (weight) loads of that slab are issued before the wait.
+// A-operand DMA of slab ks -- the consumer's dependency on its producers;
+// the B-operand (weight) DMA of that slab is issued before the wait.
+// Slab ks0 + i lives in stage i % NS.
 template <class C, int DT, class Wait>
-__device__ __forceinline__ void tile_mainloop(const TileJob& j, f32x4 (&acc)[C::FM][C::FN], char* smem,
-                                              Wait&& wait) {
+__device__ __forceinline__ void tile_mainloop(const TileJob& j, f32x4 (&acc)[C::FM][C::FN], Wait& wait) {
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    constexpr int SB = C::stage_bytes();
-    const int nks = (j.K + BK - 1) / BK;
-    SlabRegs<C> r;
-    load_slab<C>(r, j, 0, false, true);
-    wait(0);
-    load_slab<C>(r, j, 0, true, false);
-    store_slab<C>(r, smem);
-    __syncthreads();
-    for (int ks = 0; ks < nks; ++ks) {
-        char* cur = smem + (ks & 1) * SB;
-        char* nxt = smem + ((ks + 1) & 1) * SB;
-        const bool more = ks + 1 < nks;
-        if (more) {
-            load_slab<C>(r, j, (ks + 1) * BK, false, true);
-            wait(ks + 1);
-            load_slab<C>(r, j, (ks + 1) * BK, true, false);
-        }
-        compute_slab<C, DT>(cur, acc);
-        if (more) store_slab<C>(r, nxt);
-        __syncthreads();
+    const int n = j.ks1 - j.ks0;
+    // prologue: slabs ks0 .. ks0+NS-2 into stages 0 .. NS-2
+    if (n > 0) issue_slab<C, Wait, 0>(j, j.ks0, wait);
+    if constexpr (C::NS > 2) if (n > 1) issue_slab<C, Wait, 1>(j, j.ks0 + 1, wait);
+    if constexpr (C::NS > 3) if (n > 2) issue_slab<C, Wait, 2>(j, j.ks0 + 2, wait);
+    // whole rounds of NS steps, then the remaining steps (no exits mid-round,
+    // so the accumulators stay in place across the loop)
+    int ks = j.ks0;
+    for (; ks + C::NS <= j.ks1; ks += C::NS) {
+        pipe_step<C, DT, 0>(j, ks, acc, wait);
+        pipe_step<C, DT, 1>(j, ks + 1, acc, wait);
+        if constexpr (C::NS > 2) pipe_step<C, DT, 2>(j, ks + 2, acc, wait);
+        if constexpr (C::NS > 3) pipe_step<C, DT, 3>(j, ks + 3, acc, wait);
     }
+    const int rem = j.ks1 - ks;
+    if (rem > 0) pipe_step<C, DT, 0>(j, ks, acc, wait);
+    if constexpr (C::NS > 2) if (rem > 1) pipe_step<C, DT, 1>(j, ks + 1, acc, wait);
+    if constexpr (C::NS > 3) if (rem > 2) pipe_step<C, DT, 2>(j, ks + 2, acc, wait);
+    // every wave is done reading the ring before the epilogue reuses stage 0
+    ring_barrier<0>();
 }
 
 // Epilogue: activation on the fp32 accumulators, RNE to the storage dtype,
-// staged through LDS, 16-byte stores of rows < rows and columns < cols.
-// For an interleaved (SwiGLU) tile, fragment pairs (2j, 2j+1) hold gate and
-// up of the same output columns and the tile is BN/2 columns wide.
+// staged through LDS (stage 0, in EPI_PASSES passes of EPI_ROWS rows), and
+// 16-byte stores of rows < rows and columns < cols.  For an interleaved
+// (SwiGLU) tile, fragment pairs (2j, 2j+1) hold gate and up of the same
+// output columns and the tile is BN/2 columns wide.
 template <class C, int DT>
 __device__ __forceinline__ void tile_epilogue(const f32x4 (&acc)[C::FM][C::FN], int act, bool inter,
-                                              uint16_t* D, int ldd, int rows, int cols, int m0, int n0,
-                                              char* smem) {
+                                              uint16_t* D, int ldd, int rows, int cols, int m0, int n0) {
+    char* smem = lds_stage<C, 0>();
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave / C::WN, wn = wave % C::WN;
     constexpr int LD = C::BN + 8;     // padded LDS row (elements)
     uint16_t* s = reinterpret_cast<uint16_t*>(smem);
-    if (inter) {
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-            for (int fn = 0; fn < C::FN; fn += 2)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float v = silu(acc[fm][fn][i]) * acc[fm][fn + 1][i];
-                    const int row = wm * C::WTM + fm * 16 + (lane >> 4) * 4 + i;
-                    const int col = (wn * C::WTN + fn * 16) / 2 + (lane & 15);
-                    s[row * LD + col] = to_storage<DT>(v);
-                }
-    } else {
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float v = acc[fm][fn][i];
-                    if (act == ACT_GELU_TANH) v = gelu_tanh(v);
-                    const int row = wm * C::WTM + fm * 16 + (lane >> 4) * 4 + i;
-                    const int col = wn * C::WTN + fn * 16 + (lane & 15);
-                    s[row * LD + col] = to_storage<DT>(v);
-                }
-    }
-    __syncthreads();
     const int width = inter ? C::BN / 2 : C::BN;
     const int cpr = width / 8;                    // 16-byte chunks per row
-    for (int q = threadIdx.x; q < C::BM * cpr; q += C::NT) {
-        const int row = q / cpr, c = q % cpr;
-        const int gm = m0 + row, gn = n0 + c * 8;
-        if (gm < rows && gn < cols) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(s + row * LD + c * 8);
-            st16(D + (size_t)gm * ldd + gn, v);
+#pragma unroll
+    for (int pass = 0; pass < C::EPI_PASSES; ++pass) {
+        const int r0 = pass * C::EPI_ROWS;
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm) {
+            const int rbase = wm * C::WTM + fm * 16;          // wave-uniform
+            if (rbase < r0 || rbase >= r0 + C::EPI_ROWS) continue;
+            if (inter) {
+#pragma unroll
+                for (int fn = 0; fn < C::FN; fn += 2)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float v = silu(acc[fm][fn][i]) * acc[fm][fn + 1][i];
+                        const int row = rbase - r0 + (lane >> 4) * 4 + i;
+                        const int col = (wn * C::WTN + fn * 16) / 2 + (lane & 15);
+                        s[row * LD + col] = to_storage<DT>(v);
+                    }
+            } else {
+#pragma unroll
+                for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float v = acc[fm][fn][i];
+                        if (act == ACT_GELU_TANH) v = gelu_tanh(v);
+                        const int row = rbase - r0 + (lane >> 4) * 4 + i;
+                        const int col = wn * C::WTN + fn * 16 + (lane & 15);
+                        s[row * LD + col] = to_storage<DT>(v);
+                    }
+            }
         }
+        lds_barrier();
+        for (int q = threadIdx.x; q < C::EPI_ROWS * cpr; q += C::NT) {
+            const int row = q / cpr, c = q % cpr;
+            const int gm = m0 + r0 + row, gn = n0 + c * 8;
+            if (gm < rows && gn < cols) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(s + row * LD + c * 8);
+                st16(D + (size_t)gm * ldd + gn, v);
+            }
+        }
+        lds_barrier();     // the staging area is free again
     }
-    __syncthreads();   // the staging area is free again for the next tile
 }
 
 struct NoWait {
@@ -470,28 +527,28 @@ __device__ __forceinline__ int producer_width(const ChainArgs& a) {
 template <class C>
 __device__ __forceinline__ TileJob producer_job(const ChainArgs& a, uint32_t mb, uint32_t nb) {
     const bool inter = a.act == ACT_SWIGLU;
-    return TileJob{a.x, a.w1, a.H, a.M, (int)mb * C::BM,
+    return TileJob{a.x, a.w1, a.zero, a.H, a.M, (int)mb * C::BM,
                    (inter ? 2 : 1) * a.I, a.I, (int)nb * producer_width<C>(a), inter ? a.I : 0,
-                   a.H, inter};
+                   a.H, 0, (a.H + BK - 1) / BK, inter};
 }
 
 template <class C>
 __device__ __forceinline__ TileJob consumer_job(const ChainArgs& a, uint32_t mb, uint32_t nb) {
-    return TileJob{a.t, a.w2, a.I, a.M, (int)mb * C::BM, a.H, a.H, (int)nb * C::BN, 0, a.I, false};
+    return TileJob{a.t, a.w2, a.zero, a.I, a.M, (int)mb * C::BM, a.H, a.H, (int)nb * C::BN, 0,
+                   a.I, 0, (a.I + BK - 1) / BK, false};
 }
 
 // One tile of either GEMM.  `role` 1 = producer (X W1 -> act -> T),
 // 2 = consumer (T W2 -> Y); `wait` is only exercised by consumers.
 template <class C, int DT, class Wait>
-__device__ __forceinline__ void run_tile(const ChainArgs& a, int role, uint32_t mb, uint32_t nb, char* smem,
-                                         Wait&& wait) {
+__device__ __forceinline__ void run_tile(const ChainArgs& a, int role, uint32_t mb, uint32_t nb, Wait& wait) {
     f32x4 acc[C::FM][C::FN];
     const TileJob j = role == 1 ? producer_job<C>(a, mb, nb) : consumer_job<C>(a, mb, nb);
-    tile_mainloop<C, DT>(j, acc, smem, wait);
+    tile_mainloop<C, DT>(j, acc, wait);
     if (role == 1)
-        tile_epilogue<C, DT>(acc, a.act, j.inter, a.t, a.I, a.M, a.I, j.m0, j.n0, smem);
+        tile_epilogue<C, DT>(acc, a.act, j.inter, a.t, a.I, a.M, a.I, j.m0, j.n0);
     else
-        tile_epilogue<C, DT>(acc, ACT_NONE, false, a.y, a.H, a.M, a.H, j.m0, j.n0, smem);
+        tile_epilogue<C, DT>(acc, ACT_NONE, false, a.y, a.H, a.M, a.H, j.m0, j.n0);
 }
 
 }  // namespace mlpc

@@ -15,36 +15,41 @@
 // (tile-level dependency, as in the CuSync README's opening paragraph and the
 // megakernel discussion in the Hacker News thread on megakernels vs CUDA
 // graphs, where a consumer task starts as soon as its slice is done).
+//
+// This file is compiled once per tile configuration (MLPC_CFG = the id in
+// chain_configs.h); each object defines the launchers of that configuration.
+#include "chain_configs.h"
 #include "chain_device.hpp"
 #include "chain_launch.h"
 
-namespace mlpc {
+#ifndef MLPC_CFG
+#error "compile with -DMLPC_CFG=<configuration id>"
+#endif
 
-using Cfg0 = TileCfg<16, 64, 1, 2, 3>;     // small M: narrow tiles, weight streaming
-using Cfg1 = TileCfg<64, 128, 2, 2, 2>;    // medium M
-using Cfg2 = TileCfg<128, 128, 2, 2, 2>;   // large M
+namespace mlpc {
 
 template <class C, int DT>
 __global__ __launch_bounds__(C::NT) void gemm1_act_kernel(ChainArgs a) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
     uint32_t mb, nb;
     tile_coords(blockIdx.x, a.Mt, a.N1t, a.group_m, mb, nb);
-    run_tile<C, DT>(a, 1, mb, nb, smem, NoWait{});
+    NoWait w;
+    run_tile<C, DT>(a, 1, mb, nb, w);
 }
 
 template <class C, int DT>
 __global__ __launch_bounds__(C::NT) void gemm2_kernel(ChainArgs a) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
     uint32_t mb, nb;
     tile_coords(blockIdx.x, a.Mt, a.N2t, a.group_m, mb, nb);
-    run_tile<C, DT>(a, 2, mb, nb, smem, NoWait{});
+    NoWait w;
+    run_tile<C, DT>(a, 2, mb, nb, w);
 }
 
 // Consumer-side wait of the persistent kernel.  One functor type serves
 // producer tiles (inactive) and consumer tiles, so the kernel holds a single
 // inlined copy of the tile main loop.  Only wave 0 polls and takes the
 // acquire fence; the result reaches the other waves through LDS behind a
-// barrier, so one L2 invalidation covers the whole workgroup.
+// barrier that leaves the DMA ring in flight, so one L2 invalidation covers
+// the whole workgroup.
 //   row_sync:  before slab 0, wait until all N1t producer tiles of the row
 //              block have counted themselves in for this epoch;
 //   tile_sync: before slab ks, make sure every producer column block that
@@ -68,7 +73,7 @@ struct ChainWait {
         if constexpr (POL == POL_ROW) {
             if (ks != 0) return;
             if ((threadIdx.x >> 6) == 0) wave_acquire_count(cnt, target, status, limit);
-            __syncthreads();
+            lds_barrier();
         } else {
             uint32_t need = (uint32_t)((ks * BK + BK - 1) / bn1);    // last block slab ks reads
             if (need > n1t - 1) need = n1t - 1;
@@ -77,7 +82,7 @@ struct ChainWait {
                 const uint32_t r = wave_acquire_flags(flags, ready, need, n1t, target, status, limit);
                 if (threadIdx.x == 0) *s_ready = r;
             }
-            __syncthreads();
+            lds_barrier();
             ready = __builtin_amdgcn_readfirstlane(*s_ready);
         }
     }
@@ -86,7 +91,6 @@ struct ChainWait {
 template <class C, int DT, int POL>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
 void chain_persistent_kernel(ChainArgs a) {
-    extern __shared__ __attribute__((aligned(16))) char smem[];
     __shared__ uint32_t s_ticket;
     __shared__ uint32_t s_ready;
     const uint32_t total = a.T1 + a.T2;
@@ -114,7 +118,7 @@ void chain_persistent_kernel(ChainArgs a) {
             ChainWait<POL> w{!prod, a.flags + mb * a.N1t, a.rowcnt + mb, a.N1t,
                              POL == POL_ROW ? a.epoch * a.N1t : a.epoch, bn1, a.status, a.spin_limit,
                              &s_ready, 0u};
-            run_tile<C, DT>(a, prod ? 1 : 2, mb, nb, smem, w);
+            run_tile<C, DT>(a, prod ? 1 : 2, mb, nb, w);
             if (prod) {
                 // every thread's T stores happen before thread 0's agent-scope
                 // release (workgroup release + barrier), which publishes the tile
@@ -140,37 +144,22 @@ void chain_persistent_kernel(ChainArgs a) {
 
 // ------------------------------------------------------------------ host side
 
-template <class K>
-static hipError_t prep(K kernel, int lds) {
-    // allow dynamic LDS beyond the default limit (gfx950 has 160 KB per CU)
-    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-}
-
 template <class C, int DT>
 static hipError_t launch_t(const ChainArgs& a, int what, int grid, hipStream_t s, int* occ) {
-    constexpr int lds = C::lds_bytes();
-    hipError_t e = hipSuccess;
+    // all LDS is static (one object per pipeline stage)
     switch (what) {
-    case LAUNCH_GEMM1: {
-        auto k = gemm1_act_kernel<C, DT>;
-        if ((e = prep(k, lds)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k, dim3(a.T1), dim3(C::NT), lds, s, a);
+    case LAUNCH_GEMM1:
+        hipLaunchKernelGGL((gemm1_act_kernel<C, DT>), dim3(a.T1), dim3(C::NT), 0, s, a);
         return hipGetLastError();
-    }
-    case LAUNCH_GEMM2: {
-        auto k = gemm2_kernel<C, DT>;
-        if ((e = prep(k, lds)) != hipSuccess) return e;
-        hipLaunchKernelGGL(k, dim3(a.T2), dim3(C::NT), lds, s, a);
+    case LAUNCH_GEMM2:
+        hipLaunchKernelGGL((gemm2_kernel<C, DT>), dim3(a.T2), dim3(C::NT), 0, s, a);
         return hipGetLastError();
-    }
     case LAUNCH_ROW:
     case LAUNCH_TILE: {
         auto k = (what == LAUNCH_ROW) ? chain_persistent_kernel<C, DT, POL_ROW>
                                       : chain_persistent_kernel<C, DT, POL_TILE>;
-        if ((e = prep(k, lds)) != hipSuccess) return e;
-        if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, k, C::NT, lds);
-        hipLaunchKernelGGL(k, dim3(grid), dim3(C::NT), lds, s, a);
+        if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, k, C::NT, 0);
+        hipLaunchKernelGGL(k, dim3(grid), dim3(C::NT), 0, s, a);
         return hipGetLastError();
     }
     default:
@@ -184,41 +173,28 @@ static hipError_t launch_c(const ChainArgs& a, int dtype, int what, int grid, hi
                            : launch_t<C, DT_BF16>(a, what, grid, s, occ);
 }
 
-static hipError_t dispatch(const ChainArgs& a, int cfg, int dtype, int what, int grid, hipStream_t s,
-                           int* occ) {
-    switch (cfg) {
-    case 0: return launch_c<Cfg0>(a, dtype, what, grid, s, occ);
-    case 1: return launch_c<Cfg1>(a, dtype, what, grid, s, occ);
-    case 2: return launch_c<Cfg2>(a, dtype, what, grid, s, occ);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-template <class C>
-static CfgInfo info_of(int id) {
-    return CfgInfo{id, C::BM, C::BN, BK, C::NT, C::lds_bytes()};
-}
+#define MLPC_PICK(id, bm, bn, wm, wn, ns, occ) \
+    if constexpr (id == MLPC_CFG) return TileCfg<bm, bn, wm, wn, ns, occ>{};
+static constexpr auto this_cfg() { MLPC_CONFIGS(MLPC_PICK) }
+#undef MLPC_PICK
+using Cfg = decltype(this_cfg());
 
 }  // namespace mlpc
 
 using namespace mlpc;
 
-int mlpc_num_configs() { return 3; }
+#define MLPC_CAT2(a, b) a##b
+#define MLPC_CAT(a, b) MLPC_CAT2(a, b)
 
-CfgInfo mlpc_config_info(int id) {
-    switch (id) {
-    case 0: return info_of<Cfg0>(0);
-    case 1: return info_of<Cfg1>(1);
-    case 2: return info_of<Cfg2>(2);
-    default: return CfgInfo{-1, 0, 0, 0, 0, 0};
-    }
+hipError_t MLPC_CAT(mlpc_launch_cfg, MLPC_CFG)(const ChainArgs& a, int dtype, int what, int grid, hipStream_t s) {
+    return launch_c<Cfg>(a, dtype, what, grid, s, nullptr);
 }
 
-hipError_t mlpc_launch(const ChainArgs& a, int cfg, int dtype, int what, int grid, hipStream_t s) {
-    return dispatch(a, cfg, dtype, what, grid, s, nullptr);
-}
-
-hipError_t mlpc_persistent_occupancy(int cfg, int dtype, int policy, int* per_cu) {
+hipError_t MLPC_CAT(mlpc_occupancy_cfg, MLPC_CFG)(int dtype, int policy, int* per_cu) {
     ChainArgs dummy{};
-    return dispatch(dummy, cfg, dtype, policy == POL_ROW ? LAUNCH_ROW : LAUNCH_TILE, 0, nullptr, per_cu);
+    return launch_c<Cfg>(dummy, dtype, policy == POL_ROW ? LAUNCH_ROW : LAUNCH_TILE, 0, nullptr, per_cu);
+}
+
+CfgInfo MLPC_CAT(mlpc_info_cfg, MLPC_CFG)() {
+    return CfgInfo{MLPC_CFG, Cfg::BM, Cfg::BN, BK, Cfg::NT, Cfg::lds_bytes()};
 }

@@ -20,13 +20,22 @@ from consumer_gemm_chain_amd import build as b
 
 @pytest.fixture(scope="module")
 def asm(tmp_path_factory):
+    """gfx950 assembly of every tile configuration's kernels (compiled in parallel)."""
+    import concurrent.futures as cf
     if not os.path.exists(b.hipcc()):
         pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("isa") / "kernels.s"
+    d = tmp_path_factory.mktemp("isa")
     src = os.path.join(b.CSRC, "chain_kernels.hip")
-    cmd = [b.hipcc(), "-x", "hip", *b.FLAGS, "--cuda-device-only", "-S", src, "-o", str(out)]
-    subprocess.run(cmd, check=True, stderr=subprocess.DEVNULL)
-    return out.read_text()
+
+    def one(cfg):
+        out = d / f"kernels_cfg{cfg}.s"
+        cmd = [b.hipcc(), "-x", "hip", *b.FLAGS, f"-DMLPC_CFG={cfg}", "--cuda-device-only", "-S", src,
+               "-o", str(out)]
+        subprocess.run(cmd, check=True, stderr=subprocess.DEVNULL)
+        return out.read_text()
+
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        return "\n".join(ex.map(one, range(b.num_configs())))
 
 
 def _functions(text, prefix):
@@ -38,7 +47,7 @@ def _functions(text, prefix):
 
 def test_ticket_draw_and_read_at_same_loop_depth(asm):
     kernels = list(_functions(asm, "_ZN4mlpc23chain_persistent_kernel"))
-    assert len(kernels) == 12   # 3 tile configs x 2 dtypes x 2 policies
+    assert len(kernels) == 4 * b.num_configs()   # configs x 2 dtypes x 2 policies
     for name, body in kernels:
         depth = None
         d_atomic = d_read = None
