@@ -60,26 +60,34 @@ int plan_config(int64_t M) {
 
 struct mlp_chain {
     int64_t M, H, I;
-    int act, dtype, policy, gb;
+    int act, dtype, policy;
     int device;
     int cus;
     int cfg;
     int forced_cfg;
+    int forced_s1, forced_s2;   // 0 = planner's split
     CfgInfo ci;
     uint32_t Mt, N1t, N2t, T1, T2;
+    uint32_t S1, S2, ksp1, ksp2;  // K split of GEMM1 / GEMM2 tiles
     int occ;        // persistent workgroups per CU
     uint32_t grid;  // persistent grid
-    // workspace
+    // workspace (one allocation, rebuilt when the plan changes)
     void* ws;
     size_t ws_bytes;
+    size_t sync_bytes;          // the zeroed region: flags .. zero page
     uint16_t* t;
     uint32_t* flags;
     uint32_t* rowcnt;
+    uint32_t* cnt1;
+    uint32_t* cnt2;
     uint32_t* ticket;
     uint32_t* status;
     uint16_t* zero;
+    float* part1;
+    float* part2;
     // run state
-    uint32_t epoch;
+    uint32_t epoch;             // fused runs
+    uint32_t gen1, gen2;        // GEMM1 / GEMM2 executions (split arrival targets)
     uint32_t ticket_base;
     uint32_t spin_limit;
     uint32_t skip_producer;
@@ -101,7 +109,26 @@ struct DeviceGuard {
     }
 };
 
-// (Re)compute the tiling of a handle for configuration `cfg`.
+constexpr uint32_t MIN_SLABS_PER_PART = 8;   // 512 K-elements: keeps the partial traffic small
+
+// Deterministic split of each tile's K range when a GEMM has too few tiles
+// to give every CU weight-streaming work (small M): aim for about two parts
+// per CU, with at least MIN_SLABS_PER_PART slabs per part.  (The CuSync
+// README names CUTLASS StreamK as the other way to fill the last wave; this
+// is a fixed split with a fixed-order reduction, so results stay
+// bit-identical across policies.)
+uint32_t plan_split(uint32_t tiles, uint32_t nks, int cus) {
+    const uint32_t target = 2u * (uint32_t)cus;
+    if (tiles >= target / 2) return 1;
+    uint32_t s = (target + tiles - 1) / tiles;
+    const uint32_t cap = nks / MIN_SLABS_PER_PART;
+    if (s > cap) s = cap;
+    if (s < 1) s = 1;
+    const uint32_t ksp = (nks + s - 1) / s;      // no empty parts
+    return (nks + ksp - 1) / ksp;
+}
+
+// (Re)compute the tiling of a handle for configuration `cfg` and the splits.
 int apply_plan(mlp_chain* h, int cfg) {
     const CfgInfo ci = mlpc_config_info(cfg);
     if (ci.id < 0) return fail(MLP_EINVAL, "unknown tile configuration %d", cfg);
@@ -112,6 +139,11 @@ int apply_plan(mlp_chain* h, int cfg) {
     h->N2t = cdiv(h->H, ci.BN);
     h->T1 = h->Mt * h->N1t;
     h->T2 = h->Mt * h->N2t;
+    const uint32_t nks1 = cdiv(h->H, ci.BK), nks2 = cdiv(h->I, ci.BK);
+    h->S1 = h->forced_s1 > 0 ? (uint32_t)h->forced_s1 : plan_split(h->T1, nks1, h->cus);
+    h->S2 = h->forced_s2 > 0 ? (uint32_t)h->forced_s2 : plan_split(h->T2, nks2, h->cus);
+    h->ksp1 = (nks1 + h->S1 - 1) / h->S1;
+    h->ksp2 = (nks2 + h->S2 - 1) / h->S2;
     h->occ = 0;
     h->grid = 0;
     if (h->policy != MLP_POLICY_STREAM_ORDERED) {
@@ -121,21 +153,68 @@ int apply_plan(mlp_chain* h, int cfg) {
         if (occ < 1) return fail(MLP_EHIP, "persistent kernel of config %d does not fit on a CU", cfg);
         h->occ = occ;
         uint64_t g = (uint64_t)occ * (uint64_t)h->cus;
-        const uint64_t tiles = (uint64_t)h->T1 + h->T2;
-        if (g > tiles) g = tiles;
+        const uint64_t parts = (uint64_t)h->T1 * h->S1 + (uint64_t)h->T2 * h->S2;
+        if (g > parts) g = parts;
         h->grid = (uint32_t)g;
     }
     return MLP_OK;
 }
 
 int zero_workspace(mlp_chain* h) {
-    hipError_t e = hipMemset(h->flags, 0, h->ws_bytes - ((char*)h->flags - (char*)h->ws));
+    hipError_t e = hipMemset(h->flags, 0, h->sync_bytes);
     if (e != hipSuccess) return fail(MLP_EHIP, "hipMemset failed: %s", hipGetErrorString(e));
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return fail(MLP_EHIP, "hipDeviceSynchronize failed: %s", hipGetErrorString(e));
     h->epoch = 0;
+    h->gen1 = 0;
+    h->gen2 = 0;
     h->ticket_base = 0;
     return MLP_OK;
+}
+
+// Allocate (or re-allocate) and zero the workspace for the current plan:
+//   T [M, I] | flags | rowcnt | cnt1 | cnt2 | ticket | status | zero page | part1 | part2
+// (flags .. zero page is the region zeroed on create and after a timeout).
+int build_workspace(mlp_chain* h) {
+    if (h->ws) {
+        (void)hipDeviceSynchronize();
+        (void)hipFree(h->ws);
+        h->ws = nullptr;
+    }
+    const size_t acc_bytes = (size_t)h->ci.BM * h->ci.BN * 4;     // one tile's fp32 accumulators
+    const size_t t_b = align_up((size_t)h->M * (size_t)h->I * 2, 256);
+    const size_t f_b = align_up((size_t)h->T1 * 4, 256);
+    const size_t r_b = align_up((size_t)h->Mt * 4, 256);
+    const size_t c1_b = align_up((size_t)h->T1 * 4, 256);
+    const size_t c2_b = align_up((size_t)h->T2 * 4, 256);
+    const size_t p1_b = h->S1 > 1 ? align_up((size_t)h->T1 * h->S1 * acc_bytes, 256) : 0;
+    const size_t p2_b = h->S2 > 1 ? align_up((size_t)h->T2 * h->S2 * acc_bytes, 256) : 0;
+    h->sync_bytes = f_b + r_b + c1_b + c2_b + 3 * 256;
+    h->ws_bytes = t_b + h->sync_bytes + p1_b + p2_b;
+    hipError_t e = hipMalloc(&h->ws, h->ws_bytes);
+    if (e != hipSuccess) {
+        h->ws = nullptr;
+        return fail(MLP_ENOMEM, "hipMalloc of %zu workspace bytes failed: %s", h->ws_bytes, hipGetErrorString(e));
+    }
+    char* p = static_cast<char*>(h->ws);
+    h->t = reinterpret_cast<uint16_t*>(p);
+    p += t_b;
+    h->flags = reinterpret_cast<uint32_t*>(p);
+    p += f_b;
+    h->rowcnt = reinterpret_cast<uint32_t*>(p);
+    p += r_b;
+    h->cnt1 = reinterpret_cast<uint32_t*>(p);
+    p += c1_b;
+    h->cnt2 = reinterpret_cast<uint32_t*>(p);
+    p += c2_b;
+    h->ticket = reinterpret_cast<uint32_t*>(p);
+    h->status = reinterpret_cast<uint32_t*>(p + 256);
+    h->zero = reinterpret_cast<uint16_t*>(p + 512);
+    p += 3 * 256;
+    h->part1 = p1_b ? reinterpret_cast<float*>(p) : nullptr;
+    p += p1_b;
+    h->part2 = p2_b ? reinterpret_cast<float*>(p) : nullptr;
+    return zero_workspace(h);
 }
 
 bool bad_ptr(const void* p) { return p == nullptr || ((uintptr_t)p & 15u) != 0; }
@@ -162,6 +241,16 @@ mlpc::ChainArgs make_args(const mlp_chain* h, const void* x, const void* w1, con
     a.rowcnt = h->rowcnt;
     a.status = h->status;
     a.zero = h->zero;
+    a.S1 = h->S1;
+    a.S2 = h->S2;
+    a.ksp1 = h->ksp1;
+    a.ksp2 = h->ksp2;
+    a.part1 = h->part1;
+    a.part2 = h->part2;
+    a.cnt1 = h->cnt1;
+    a.cnt2 = h->cnt2;
+    a.gen1 = h->gen1;
+    a.gen2 = h->gen2;
     a.ticket_base = h->ticket_base;
     a.epoch = h->epoch;
     a.grid = h->grid;
@@ -230,44 +319,17 @@ mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype
     h->act = act;
     h->dtype = dtype;
     h->policy = policy;
-    h->gb = act == MLP_ACT_SWIGLU ? 2 : 1;
     h->device = dev;
     h->cus = prop.multiProcessorCount;
     h->forced_cfg = -1;
+    h->forced_s1 = 0;
+    h->forced_s2 = 0;
     h->spin_limit = DEFAULT_SPIN_LIMIT;
     h->skip_producer = mlpc::NO_SKIP;
     h->last_stream = nullptr;
-    if (apply_plan(h, plan_config(M)) != MLP_OK) {
-        delete h;
-        return nullptr;
-    }
-    // flags and row counters sized for the finest tiling any config uses
-    uint32_t max_t1 = 0, max_mt = 0;
-    for (int c = 0; c < mlpc_num_configs(); ++c) {
-        const CfgInfo ci = mlpc_config_info(c);
-        const uint32_t mt = cdiv(M, ci.BM), n1 = cdiv(I, act == MLP_ACT_SWIGLU ? ci.BN / 2 : ci.BN);
-        if (mt * n1 > max_t1) max_t1 = mt * n1;
-        if (mt > max_mt) max_mt = mt;
-    }
-    const size_t t_bytes = align_up((size_t)M * (size_t)I * 2, 256);
-    const size_t f_bytes = align_up((size_t)max_t1 * 4, 256);
-    const size_t r_bytes = align_up((size_t)max_mt * 4, 256);
-    h->ws_bytes = t_bytes + f_bytes + r_bytes + 256 + 256 + 256;
-    e = hipMalloc(&h->ws, h->ws_bytes);
-    if (e != hipSuccess) {
-        fail(MLP_ENOMEM, "hipMalloc of %zu workspace bytes failed: %s", h->ws_bytes, hipGetErrorString(e));
-        delete h;
-        return nullptr;
-    }
-    char* p = static_cast<char*>(h->ws);
-    h->t = reinterpret_cast<uint16_t*>(p);
-    h->flags = reinterpret_cast<uint32_t*>(p + t_bytes);
-    h->rowcnt = reinterpret_cast<uint32_t*>(p + t_bytes + f_bytes);
-    h->ticket = reinterpret_cast<uint32_t*>(p + t_bytes + f_bytes + r_bytes);
-    h->status = reinterpret_cast<uint32_t*>(p + t_bytes + f_bytes + r_bytes + 256);
-    h->zero = reinterpret_cast<uint16_t*>(p + t_bytes + f_bytes + r_bytes + 512);
-    if (zero_workspace(h) != MLP_OK) {
-        (void)hipFree(h->ws);
+    h->ws = nullptr;
+    if (apply_plan(h, plan_config(M)) != MLP_OK || build_workspace(h) != MLP_OK) {
+        if (h->ws) (void)hipFree(h->ws);
         delete h;
         return nullptr;
     }
@@ -299,20 +361,24 @@ int mlp_chain_run(mlp_chain_t h, const void* x, const void* w1, const void* w2, 
     if (!g.ok) return fail(MLP_EHIP, "cannot select the handle's device %d", h->device);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     h->last_stream = s;
+    h->gen1 += 1u;
+    h->gen2 += 1u;
     if (h->policy == MLP_POLICY_STREAM_ORDERED) {
         const mlpc::ChainArgs a = make_args(h, x, w1, w2, out);
         int rc = launch_phase(h, LAUNCH_GEMM1, a, s);
-        if (rc != MLP_OK) return rc;
-        return launch_phase(h, LAUNCH_GEMM2, a, s);
+        if (rc == MLP_OK) rc = launch_phase(h, LAUNCH_GEMM2, a, s);
+        return rc;   // (a failed launch leaves the device unusable; counters need not roll back)
     }
     h->epoch += 1u;
     const mlpc::ChainArgs a = make_args(h, x, w1, w2, out);
     int rc = launch_phase(h, h->policy == MLP_POLICY_ROW_SYNC ? LAUNCH_ROW : LAUNCH_TILE, a, s);
     if (rc != MLP_OK) {
         h->epoch -= 1u;
+        h->gen1 -= 1u;
+        h->gen2 -= 1u;
         return rc;
     }
-    h->ticket_base += h->T1 + h->T2 + h->grid;
+    h->ticket_base += h->T1 * h->S1 + h->T2 * h->S2 + h->grid;
     return MLP_OK;
 }
 
@@ -328,6 +394,7 @@ int mlp_chain_run_phase(mlp_chain_t h, int phase, const void* x, const void* w1,
     if (!g.ok) return fail(MLP_EHIP, "cannot select the handle's device %d", h->device);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     h->last_stream = s;
+    if (phase == 1) h->gen1 += 1u; else h->gen2 += 1u;
     const mlpc::ChainArgs a = make_args(h, x, w1, w2, out);
     return launch_phase(h, phase == 1 ? LAUNCH_GEMM1 : LAUNCH_GEMM2, a, s);
 }
@@ -351,9 +418,10 @@ int mlp_chain_status(mlp_chain_t h) {
 int mlp_chain_info(mlp_chain_t h, int64_t* info, int n) {
     if (!h || !info || n < 16) return fail(MLP_EINVAL, "mlp_chain_info needs a handle and 16 slots");
     const int64_t bn1 = h->act == MLP_ACT_SWIGLU ? h->ci.BN / 2 : h->ci.BN;
-    const int64_t v[16] = {h->ci.BM, bn1, h->ci.BN, h->ci.BK, h->Mt, h->N1t, h->N2t, h->T1, h->T2,
-                           h->grid, h->occ, h->ci.NT, h->cus, h->epoch, h->cfg, (int64_t)h->ws_bytes};
-    for (int i = 0; i < 16; ++i) info[i] = v[i];
+    const int64_t v[20] = {h->ci.BM, bn1, h->ci.BN, h->ci.BK, h->Mt, h->N1t, h->N2t, h->T1, h->T2,
+                           h->grid, h->occ, h->ci.NT, h->cus, h->epoch, h->cfg, (int64_t)h->ws_bytes,
+                           h->S1, h->S2, h->ksp1, h->ksp2};
+    for (int i = 0; i < n && i < 20; ++i) info[i] = v[i];
     return MLP_OK;
 }
 
@@ -365,20 +433,33 @@ int mlp_chain_debug_set_spin_limit(mlp_chain_t h, uint32_t limit) {
 
 int mlp_chain_debug_skip_producer(mlp_chain_t h, int64_t tile) {
     if (!h) return fail(MLP_EINVAL, "NULL handle");
-    h->skip_producer = (tile < 0 || tile >= (int64_t)h->T1) ? mlpc::NO_SKIP : (uint32_t)tile;
+    const int64_t parts = (int64_t)h->T1 * h->S1;
+    h->skip_producer = (tile < 0 || tile >= parts) ? mlpc::NO_SKIP : (uint32_t)tile;
     return MLP_OK;
+}
+
+static int replan(mlp_chain_t h) {
+    DeviceGuard g(h->device);
+    const int cfg = h->forced_cfg < 0 ? plan_config(h->M) : h->forced_cfg;
+    int rc = apply_plan(h, cfg);
+    if (rc != MLP_OK) return rc;
+    return build_workspace(h);
 }
 
 int mlp_chain_debug_set_config(mlp_chain_t h, int config_id) {
     if (!h) return fail(MLP_EINVAL, "NULL handle");
     if (config_id < -1 || config_id >= mlpc_num_configs())
         return fail(MLP_EINVAL, "unknown tile configuration %d", config_id);
-    DeviceGuard g(h->device);
-    const int cfg = config_id < 0 ? plan_config(h->M) : config_id;
     h->forced_cfg = config_id;
-    int rc = apply_plan(h, cfg);
-    if (rc != MLP_OK) return rc;
-    return zero_workspace(h);
+    return replan(h);
+}
+
+int mlp_chain_debug_set_split(mlp_chain_t h, int s1, int s2) {
+    if (!h) return fail(MLP_EINVAL, "NULL handle");
+    if (s1 < 0 || s2 < 0 || s1 > 64 || s2 > 64) return fail(MLP_EINVAL, "splits must be in 0..64");
+    h->forced_s1 = s1;
+    h->forced_s2 = s2;
+    return replan(h);
 }
 
 int mlp_chain_debug_read_intermediate(mlp_chain_t h, void* dst, void* hip_stream) {

@@ -64,6 +64,16 @@ struct ChainArgs {
     uint32_t* rowcnt;       // [Mt] producer completions (row_sync)
     uint32_t* status;       // sticky watchdog status (nonzero = a consumer gave up)
     const uint16_t* zero;   // >= 16 zero bytes: the source of every out-of-range chunk
+    // deterministic split of each tile's K range (S1 parts per GEMM1 tile, S2
+    // per GEMM2 tile; S = 1: no split).  Parts write fp32 partials; the last
+    // part to arrive (per-tile counter) sums them in part order 0..S-1.
+    uint32_t S1, S2;        // parts per tile
+    uint32_t ksp1, ksp2;    // K slabs per part
+    float* part1;           // [T1][S1][tile accumulators] (S1 > 1)
+    float* part2;           // [T2][S2][tile accumulators] (S2 > 1)
+    uint32_t* cnt1;         // [T1] part arrivals (S1 > 1)
+    uint32_t* cnt2;         // [T2] part arrivals (S2 > 1)
+    uint32_t gen1, gen2;    // this run's GEMM1 / GEMM2 generation (arrival targets gen * S)
     uint32_t ticket_base;   // tickets drawn by earlier runs (mod 2^32)
     uint32_t epoch;         // this run's epoch (mod 2^32)
     uint32_t grid;          // persistent workgroups
@@ -524,31 +534,98 @@ __device__ __forceinline__ int producer_width(const ChainArgs& a) {
     return a.act == ACT_SWIGLU ? C::BN / 2 : C::BN;
 }
 
+// K-slab range of part s of a tile split into S parts of ksp slabs.
+__device__ __forceinline__ void part_range(int nks, uint32_t s, uint32_t ksp, int& ks0, int& ks1) {
+    ks0 = (int)(s * ksp);
+    ks1 = ks0 + (int)ksp;
+    if (ks0 > nks) ks0 = nks;
+    if (ks1 > nks) ks1 = nks;
+}
+
 template <class C>
-__device__ __forceinline__ TileJob producer_job(const ChainArgs& a, uint32_t mb, uint32_t nb) {
+__device__ __forceinline__ TileJob producer_job(const ChainArgs& a, uint32_t mb, uint32_t nb, uint32_t s) {
     const bool inter = a.act == ACT_SWIGLU;
+    int ks0, ks1;
+    part_range((a.H + BK - 1) / BK, s, a.ksp1, ks0, ks1);
     return TileJob{a.x, a.w1, a.zero, a.H, a.M, (int)mb * C::BM,
                    (inter ? 2 : 1) * a.I, a.I, (int)nb * producer_width<C>(a), inter ? a.I : 0,
-                   a.H, 0, (a.H + BK - 1) / BK, inter};
+                   a.H, ks0, ks1, inter};
 }
 
 template <class C>
-__device__ __forceinline__ TileJob consumer_job(const ChainArgs& a, uint32_t mb, uint32_t nb) {
+__device__ __forceinline__ TileJob consumer_job(const ChainArgs& a, uint32_t mb, uint32_t nb, uint32_t s) {
+    int ks0, ks1;
+    part_range((a.I + BK - 1) / BK, s, a.ksp2, ks0, ks1);
     return TileJob{a.t, a.w2, a.zero, a.I, a.M, (int)mb * C::BM, a.H, a.H, (int)nb * C::BN, 0,
-                   a.I, 0, (a.I + BK - 1) / BK, false};
+                   a.I, ks0, ks1, false};
 }
 
-// One tile of either GEMM.  `role` 1 = producer (X W1 -> act -> T),
-// 2 = consumer (T W2 -> Y); `wait` is only exercised by consumers.
+// Split-K: store this part's accumulators (fp32, in register order so every
+// thread writes and later reads its own 16-byte slots), count the part in
+// with an agent-scope acquire-release, and, in the part that arrives last,
+// replace the accumulators by the sum of all S partials in part order.
+// Returns true in the last part (which then runs the epilogue).
+template <class C>
+__device__ __forceinline__ bool split_reduce(f32x4 (&acc)[C::FM][C::FN], float* part, uint32_t* cnt,
+                                             uint32_t tile, uint32_t s, uint32_t S, uint32_t target,
+                                             uint32_t* s_flag) {
+    constexpr int NF = C::FM * C::FN;
+    const int tid = threadIdx.x;
+    f32x4* base = reinterpret_cast<f32x4*>(part) + (size_t)tile * S * NF * C::NT;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+            base[((size_t)s * NF + fm * C::FN + fn) * C::NT + tid] = acc[fm][fn];
+    // every thread's partial happens before thread 0's agent-scope release
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(cnt + tile, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = (old + 1u == target) ? 1u : 0u;
+    }
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(*s_flag) == 0) return false;
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) {
+            f32x4 sum = s == 0 ? acc[fm][fn] : base[(size_t)(fm * C::FN + fn) * C::NT + tid];
+            for (uint32_t p = 1; p < S; ++p) {
+                const f32x4 v = p == s ? acc[fm][fn] : base[((size_t)p * NF + fm * C::FN + fn) * C::NT + tid];
+                sum = sum + v;
+            }
+            acc[fm][fn] = sum;
+        }
+    return true;
+}
+
+// One tile part of either GEMM.  `role` 1 = producer (X W1 -> act -> T),
+// 2 = consumer (T W2 -> Y); `wait` is only exercised by consumers.  Returns
+// true if this part wrote the tile's output (always, unless the tile is
+// split and another part arrives last).
 template <class C, int DT, class Wait>
-__device__ __forceinline__ void run_tile(const ChainArgs& a, int role, uint32_t mb, uint32_t nb, Wait& wait) {
+__device__ __forceinline__ bool run_tile(const ChainArgs& a, int role, uint32_t tile, uint32_t s,
+                                         uint32_t* s_flag, Wait& wait) {
     f32x4 acc[C::FM][C::FN];
-    const TileJob j = role == 1 ? producer_job<C>(a, mb, nb) : consumer_job<C>(a, mb, nb);
+    uint32_t mb, nb;
+    if (role == 1)
+        tile_coords(tile, a.Mt, a.N1t, a.group_m, mb, nb);
+    else
+        tile_coords(tile, a.Mt, a.N2t, a.group_m, mb, nb);
+    const TileJob j = role == 1 ? producer_job<C>(a, mb, nb, s) : consumer_job<C>(a, mb, nb, s);
     tile_mainloop<C, DT>(j, acc, wait);
+    const uint32_t S = role == 1 ? a.S1 : a.S2;
+    if (S > 1) {
+        const bool last = role == 1 ? split_reduce<C>(acc, a.part1, a.cnt1, tile, s, S, a.gen1 * S, s_flag)
+                                    : split_reduce<C>(acc, a.part2, a.cnt2, tile, s, S, a.gen2 * S, s_flag);
+        if (!last) return false;
+    }
     if (role == 1)
         tile_epilogue<C, DT>(acc, a.act, j.inter, a.t, a.I, a.M, a.I, j.m0, j.n0);
     else
         tile_epilogue<C, DT>(acc, ACT_NONE, false, a.y, a.H, a.M, a.H, j.m0, j.n0);
+    return true;
 }
 
 }  // namespace mlpc

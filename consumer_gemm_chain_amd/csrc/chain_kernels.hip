@@ -28,20 +28,19 @@
 
 namespace mlpc {
 
+// One workgroup per tile part: blockIdx = tile * S + part.
 template <class C, int DT>
 __global__ __launch_bounds__(C::NT) void gemm1_act_kernel(ChainArgs a) {
-    uint32_t mb, nb;
-    tile_coords(blockIdx.x, a.Mt, a.N1t, a.group_m, mb, nb);
+    __shared__ uint32_t s_flag;
     NoWait w;
-    run_tile<C, DT>(a, 1, mb, nb, w);
+    run_tile<C, DT>(a, 1, blockIdx.x / a.S1, blockIdx.x % a.S1, &s_flag, w);
 }
 
 template <class C, int DT>
 __global__ __launch_bounds__(C::NT) void gemm2_kernel(ChainArgs a) {
-    uint32_t mb, nb;
-    tile_coords(blockIdx.x, a.Mt, a.N2t, a.group_m, mb, nb);
+    __shared__ uint32_t s_flag;
     NoWait w;
-    run_tile<C, DT>(a, 2, mb, nb, w);
+    run_tile<C, DT>(a, 2, blockIdx.x / a.S2, blockIdx.x % a.S2, &s_flag, w);
 }
 
 // Consumer-side wait of the persistent kernel.  One functor type serves
@@ -50,12 +49,14 @@ __global__ __launch_bounds__(C::NT) void gemm2_kernel(ChainArgs a) {
 // acquire fence; the result reaches the other waves through LDS behind a
 // barrier that leaves the DMA ring in flight, so one L2 invalidation covers
 // the whole workgroup.
-//   row_sync:  before slab 0, wait until all N1t producer tiles of the row
-//              block have counted themselves in for this epoch;
+//   row_sync:  before the first slab of the part, wait until all N1t
+//              producer tiles of the row block have counted themselves in
+//              for this epoch;
 //   tile_sync: before slab ks, make sure every producer column block that
 //              slab reads has been acquired; if not, wave 0 waits for it and
-//              acquires every block that is ready by then in one go.  Slabs
-//              are still taken in ascending K order.
+//              acquires every block that is ready by then in one go.  A part
+//              starts at the first block of its own K range.  Slabs are
+//              still taken in ascending K order.
 template <int POL>
 struct ChainWait {
     bool active;             // consumer tile (uniform)
@@ -67,11 +68,13 @@ struct ChainWait {
     uint32_t* status;
     uint32_t limit;
     uint32_t* s_ready;       // LDS broadcast slot
-    uint32_t ready;          // producer blocks acquired so far (uniform)
+    uint32_t ready;          // tile_sync: blocks below this are acquired or not needed (uniform)
+    bool waited;             // row_sync: the part's single wait is done (uniform)
     __device__ __forceinline__ void operator()(int ks) {
         if (!active) return;
         if constexpr (POL == POL_ROW) {
-            if (ks != 0) return;
+            if (waited) return;
+            waited = true;
             if ((threadIdx.x >> 6) == 0) wave_acquire_count(cnt, target, status, limit);
             lds_barrier();
         } else {
@@ -93,7 +96,10 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
 void chain_persistent_kernel(ChainArgs a) {
     __shared__ uint32_t s_ticket;
     __shared__ uint32_t s_ready;
-    const uint32_t total = a.T1 + a.T2;
+    __shared__ uint32_t s_flag;
+    // tickets [0, P1) are GEMM1 tile parts, [P1, P1 + P2) GEMM2 tile parts
+    const uint32_t P1 = a.T1 * a.S1, P2 = a.T2 * a.S2;
+    const uint32_t total = P1 + P2;
     const int bn1 = a.act == ACT_SWIGLU ? C::BN / 2 : C::BN;
     for (;;) {
         if (threadIdx.x == 0)
@@ -107,19 +113,21 @@ void chain_persistent_kernel(ChainArgs a) {
         const uint32_t t = __builtin_amdgcn_readfirstlane(s_ticket);
         __syncthreads();
         if (t >= total) break;
-        const bool prod = t < a.T1;
-        // test hook: a skipped producer tile does no work and no release
+        const bool prod = t < P1;
+        // test hook: a skipped producer part does no work and no release
         if (!(prod && t == a.skip_producer)) {
+            const uint32_t S = prod ? a.S1 : a.S2;
+            const uint32_t u = prod ? t : t - P1;
+            const uint32_t tile = u / S, part = u % S;
             uint32_t mb, nb;
-            if (prod)
-                tile_coords(t, a.Mt, a.N1t, a.group_m, mb, nb);
-            else
-                tile_coords(t - a.T1, a.Mt, a.N2t, a.group_m, mb, nb);
+            tile_coords(tile, a.Mt, prod ? a.N1t : a.N2t, a.group_m, mb, nb);
+            // first producer block the part's K range reads
+            const uint32_t first = prod ? 0u : (part * a.ksp2 * BK) / (uint32_t)bn1;
             ChainWait<POL> w{!prod, a.flags + mb * a.N1t, a.rowcnt + mb, a.N1t,
                              POL == POL_ROW ? a.epoch * a.N1t : a.epoch, bn1, a.status, a.spin_limit,
-                             &s_ready, 0u};
-            run_tile<C, DT>(a, prod ? 1 : 2, mb, nb, w);
-            if (prod) {
+                             &s_ready, first, false};
+            const bool wrote = run_tile<C, DT>(a, prod ? 1 : 2, tile, part, &s_flag, w);
+            if (prod && wrote) {
                 // every thread's T stores happen before thread 0's agent-scope
                 // release (workgroup release + barrier), which publishes the tile
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -149,10 +157,10 @@ static hipError_t launch_t(const ChainArgs& a, int what, int grid, hipStream_t s
     // all LDS is static (one object per pipeline stage)
     switch (what) {
     case LAUNCH_GEMM1:
-        hipLaunchKernelGGL((gemm1_act_kernel<C, DT>), dim3(a.T1), dim3(C::NT), 0, s, a);
+        hipLaunchKernelGGL((gemm1_act_kernel<C, DT>), dim3(a.T1 * a.S1), dim3(C::NT), 0, s, a);
         return hipGetLastError();
     case LAUNCH_GEMM2:
-        hipLaunchKernelGGL((gemm2_kernel<C, DT>), dim3(a.T2), dim3(C::NT), 0, s, a);
+        hipLaunchKernelGGL((gemm2_kernel<C, DT>), dim3(a.T2 * a.S2), dim3(C::NT), 0, s, a);
         return hipGetLastError();
     case LAUNCH_ROW:
     case LAUNCH_TILE: {

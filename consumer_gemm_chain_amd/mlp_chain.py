@@ -27,10 +27,11 @@ POLICIES = {"stream_ordered": MLP_POLICY_STREAM_ORDERED, "row_sync": MLP_POLICY_
 EXPORTS = ("mlp_chain_create", "mlp_chain_run", "mlp_chain_destroy", "mlp_chain_run_phase",
            "mlp_chain_status", "mlp_chain_last_error", "mlp_chain_info",
            "mlp_chain_debug_set_spin_limit", "mlp_chain_debug_skip_producer",
-           "mlp_chain_debug_set_config", "mlp_chain_debug_read_intermediate")
+           "mlp_chain_debug_set_config", "mlp_chain_debug_set_split",
+           "mlp_chain_debug_read_intermediate")
 
 INFO_FIELDS = ("BM", "BN1", "BN2", "BK", "Mt", "N1t", "N2t", "T1", "T2", "grid", "wg_per_cu",
-               "threads", "cus", "epoch", "config", "workspace_bytes")
+               "threads", "cus", "epoch", "config", "workspace_bytes", "S1", "S2", "ksp1", "ksp2")
 
 _lib = None
 
@@ -72,6 +73,8 @@ def load_library(path: str | None = None):
     lib.mlp_chain_debug_skip_producer.restype = ci
     lib.mlp_chain_debug_set_config.argtypes = [vp, ci]
     lib.mlp_chain_debug_set_config.restype = ci
+    lib.mlp_chain_debug_set_split.argtypes = [vp, ci, ci]
+    lib.mlp_chain_debug_set_split.restype = ci
     lib.mlp_chain_debug_read_intermediate.argtypes = [vp, vp, vp]
     lib.mlp_chain_debug_read_intermediate.restype = ci
     _lib = lib
@@ -121,8 +124,8 @@ def mlp_chain_status(h: int) -> int:
 
 
 def mlp_chain_info(h: int) -> dict:
-    arr = (ctypes.c_int64 * 16)()
-    _check(load_library().mlp_chain_info(h, arr, 16))
+    arr = (ctypes.c_int64 * len(INFO_FIELDS))()
+    _check(load_library().mlp_chain_info(h, arr, len(INFO_FIELDS)))
     return dict(zip(INFO_FIELDS, (int(v) for v in arr)))
 
 
@@ -136,6 +139,10 @@ def mlp_chain_debug_skip_producer(h: int, tile: int) -> int:
 
 def mlp_chain_debug_set_config(h: int, config_id: int) -> int:
     return _check(load_library().mlp_chain_debug_set_config(h, int(config_id)))
+
+
+def mlp_chain_debug_set_split(h: int, s1: int, s2: int) -> int:
+    return _check(load_library().mlp_chain_debug_set_split(h, int(s1), int(s2)))
 
 
 def mlp_chain_debug_read_intermediate(h: int, dst: int, hip_stream: int | None) -> int:
@@ -210,6 +217,9 @@ class MlpChain:
 
     def set_config(self, cfg: int):
         mlp_chain_debug_set_config(self.h, cfg)
+
+    def set_split(self, s1: int, s2: int):
+        mlp_chain_debug_set_split(self.h, s1, s2)
 
     def set_spin_limit(self, limit: int):
         mlp_chain_debug_set_spin_limit(self.h, limit)

@@ -45,8 +45,9 @@
  * Pointers: x, w1, w2 and out are DEVICE pointers owned by the caller.  The
  * stream argument is a hipStream_t passed as void* (NULL = default stream).
  * The handle owns a device workspace (the intermediate T [M, I], per-tile
- * ready flags, per-row-block counters, a ticket counter, a status word),
- * allocated by create and freed by destroy.
+ * ready flags, per-row-block counters, a ticket counter, a status word, and
+ * for split tiles fp32 partials and per-tile arrival counters), allocated
+ * by create and freed by destroy.
  *
  * Concurrency: runs on one handle must be ordered on one stream (they share
  * the workspace); separate handles are independent.  All entry points are
@@ -115,26 +116,43 @@ int mlp_chain_status(mlp_chain_t h);
  * string is owned by the library and valid until the next call on the thread. */
 const char* mlp_chain_last_error(void);
 
-/* Plan and launch facts of a handle, for tests and measurement:
- * info[0..15] = { BM, BN1, BN2, BK, Mt, N1t, N2t, T1, T2, persistent grid,
- *                 workgroups per CU, threads per workgroup, CUs, epoch,
- *                 config id, workspace bytes }.
+/* Plan and launch facts of a handle, for tests and measurement; fills the
+ * first min(n, 20) of
+ *   { BM, BN1, BN2, BK, Mt, N1t, N2t, T1, T2, persistent grid,
+ *     workgroups per CU, threads per workgroup, CUs, epoch,
+ *     config id, workspace bytes, S1, S2, K slabs per GEMM1 part,
+ *     K slabs per GEMM2 part }.
+ * (S1, S2: the deterministic K split of GEMM1 / GEMM2 tiles, 1 = none.)
  * Returns MLP_EINVAL for a NULL handle or array, or n < 16. */
 int mlp_chain_info(mlp_chain_t h, int64_t* info, int n);
 
 /* Test hooks (never needed for normal use):
  * set the consumer spin limit (iterations of the back-off loop before a
- * consumer gives up; 0 restores the default), and make producer tile
- * `tile` (ticket order, -1 = none) skip its work and its release, which
- * forces the watchdog path without any kernel faulting or hanging.
+ * consumer gives up; 0 restores the default), and make producer part
+ * `tile` (ticket order: tile * S1 + part, -1 = none) skip its work and its
+ * release, which forces the watchdog path without any kernel faulting or
+ * hanging.
  * Return MLP_EINVAL for a NULL handle. */
 int mlp_chain_debug_set_spin_limit(mlp_chain_t h, uint32_t limit);
 int mlp_chain_debug_skip_producer(mlp_chain_t h, int64_t tile);
 
 /* Force a tile configuration by id for the next runs (-1 = planner's
- * choice); used by tests that sweep configurations.  The workspace is kept.
- * Returns MLP_EINVAL for a NULL handle or an unknown id. */
+ * choice); used by tests and tuning sweeps.  Synchronizes the device and
+ * rebuilds (and re-zeroes) the workspace; the intermediate is lost.
+ * Returns MLP_EINVAL for a NULL handle or an unknown id, MLP_ENOMEM if the
+ * new workspace cannot be allocated. */
 int mlp_chain_debug_set_config(mlp_chain_t h, int config_id);
+
+/* Force the number of K parts of GEMM1 tiles (s1) and GEMM2 tiles (s2), 0 =
+ * planner's choice, at most 64; parts may be empty when a split exceeds the
+ * K slabs.  Small-M tiles are split so that every CU streams weights; each
+ * part accumulates its K range in fp32 and the last part to finish sums the
+ * partials in part order, so every policy sees the same arithmetic (the
+ * CuSync README names CUTLASS StreamK as the other remedy for the last
+ * wave; this is a fixed, deterministic split).  Synchronizes and rebuilds
+ * the workspace like mlp_chain_debug_set_config.  Returns MLP_EINVAL for a
+ * NULL handle or a split outside 0..64. */
+int mlp_chain_debug_set_split(mlp_chain_t h, int s1, int s2);
 
 /* Copy the handle's intermediate T [M, I] (as left by the last run on the
  * handle) into the caller's device buffer `dst` (M * I elements of the

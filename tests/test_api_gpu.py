@@ -98,3 +98,37 @@ def test_info_reports_plan():
         assert info["cus"] >= 1 and info["grid"] >= 1 and info["wg_per_cu"] >= 1
         assert info["T1"] == info["Mt"] * info["N1t"] and info["T2"] == info["Mt"] * info["N2t"]
         assert info["grid"] <= info["wg_per_cu"] * info["cus"]
+        assert info["S1"] == 1 and info["S2"] == 1          # enough tiles: no split
+    with mc.MlpChain(1, 12288, 6144, "gelu_tanh", "f16", "tile_sync") as ch:
+        info = ch.info()
+        assert info["S1"] > 1 and info["S2"] > 1            # weight streaming: split K
+        assert info["ksp1"] * info["S1"] >= 12288 // 64 and info["ksp2"] * info["S2"] >= 6144 // 64
+
+
+@pytest.mark.parametrize("policy", ["row_sync", "tile_sync"])
+def test_watchdog_with_split_producer(policy):
+    """A skipped part of a split producer tile means the tile is never
+    reduced or published: its consumers time out and the handle recovers."""
+    import torch
+    x, w1, w2, dev = _inputs(M=32, H=2048, I=1024)
+    ref = run_chain(x, w1, w2, "gelu_tanh", "f16", "stream_ordered", dev=dev)
+    with mc.MlpChain(32, 2048, 1024, "gelu_tanh", "f16", policy) as ch:
+        ch.set_split(4, 2)
+        out = empty_dev((32, 2048), "f16")
+        ch.set_spin_limit(2000)
+        ch.skip_producer(1)              # tile 0, part 1
+        ch.run(*dev, out)
+        torch.cuda.synchronize()
+        assert ch.status() == mc.MLP_ETIMEOUT
+        ch.skip_producer(-1)
+        ch.set_spin_limit(0)
+        ch.run(*dev, out)
+        torch.cuda.synchronize()
+        assert ch.status() == mc.MLP_OK
+        # same split in a stream-ordered handle for the bitwise comparison
+        with mc.MlpChain(32, 2048, 1024, "gelu_tanh", "f16", "stream_ordered") as so:
+            so.set_split(4, 2)
+            out2 = empty_dev((32, 2048), "f16")
+            so.run(*dev, out2)
+            torch.cuda.synchronize()
+        assert np.array_equal(from_dev(out), from_dev(out2))

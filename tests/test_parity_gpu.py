@@ -203,3 +203,62 @@ def test_full_size_workloads(oracle_mod, wl, M):
     rows = _sample_rows(M, seed=wl * 10000 + M)
     y_ref = oracle_mod.mlp_chain(x[rows], w1, w2, w.act, w.dtype)
     check_against_oracle(outs["tile_sync"][rows], y_ref, w.dtype, f"{w.name} M={M}")
+
+
+@pytest.mark.parametrize("s1,s2", [(2, 3), (3, 1), (1, 5), (7, 4), (40, 40)])
+@pytest.mark.parametrize("act,dtype,cfg", [("gelu_tanh", "f16", 0), ("swiglu", "bf16", 0),
+                                           ("none", "f16", 2)])
+def test_split_k_matches_oracle_and_policies(oracle_mod, s1, s2, act, dtype, cfg):
+    """Deterministic K split (partials summed in part order by the last part
+    to arrive): within tolerance of the oracle and bit-identical across the
+    three policies for the same split.  Splits larger than the number of K
+    slabs leave some parts empty."""
+    import torch
+    from consumer_gemm_chain_amd.mlp_chain import MlpChain
+    from tests._helpers import empty_dev, from_dev
+    M, H, I = 40, 1000, 1088
+    x, w1, w2 = _case(M, H, I, act, dtype, seed=s1 * 10 + s2)
+    y_ref = oracle_mod.mlp_chain(x, w1, w2, act, dtype)
+    dev = (to_dev(x, dtype), to_dev(w1, dtype), to_dev(w2, dtype))
+    outs = {}
+    for pol in POLICIES:
+        with MlpChain(M, H, I, act, dtype, pol) as ch:
+            ch.set_config(cfg)
+            ch.set_split(s1, s2)
+            info = ch.info()
+            assert (info["S1"], info["S2"]) == (s1, s2)
+            out = empty_dev((M, H), dtype)
+            for _ in range(2):                     # second run: counters of the next generation
+                out.fill_(float("nan"))
+                ch.run(*dev, out)
+            torch.cuda.synchronize()
+            assert ch.status() == 0
+            outs[pol] = from_dev(out)
+        check_against_oracle(outs[pol], y_ref, dtype, f"{pol} split {s1},{s2}")
+    assert np.array_equal(outs["row_sync"], outs["stream_ordered"])
+    assert np.array_equal(outs["tile_sync"], outs["stream_ordered"])
+
+
+def test_planned_split_at_small_m_alternating_inputs():
+    """At M=16 on a GPT-3-like width the planner splits K; 20 fused runs per
+    policy alternating two inputs equal the stream-ordered outputs exactly."""
+    import torch
+    from consumer_gemm_chain_amd.mlp_chain import MlpChain
+    from tests._helpers import empty_dev, from_dev
+    M, H, I, act, dtype = 16, 4096, 2048, "gelu_tanh", "f16"
+    xa, w1, w2 = _case(M, H, I, act, dtype, seed=21)
+    xb = gen.normal_bits((M, H), 77, 1.0, dtype)
+    dw1, dw2 = to_dev(w1, dtype), to_dev(w2, dtype)
+    dxs = [to_dev(xa, dtype), to_dev(xb, dtype)]
+    refs = [run_chain(x, w1, w2, act, dtype, "stream_ordered", dev=(dx, dw1, dw2)) for x, dx in zip((xa, xb), dxs)]
+    for pol in ("row_sync", "tile_sync"):
+        with MlpChain(M, H, I, act, dtype, pol) as ch:
+            info = ch.info()
+            assert info["S1"] > 1 and info["S2"] > 1, info
+            out = empty_dev((M, H), dtype)
+            for i in range(20):
+                out.fill_(float("nan"))
+                ch.run(dxs[i % 2], dw1, dw2, out)
+                torch.cuda.synchronize()
+                assert np.array_equal(from_dev(out), refs[i % 2]), f"{pol} run {i}"
+            assert ch.status() == 0
