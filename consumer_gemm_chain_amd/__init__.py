@@ -12,5 +12,5 @@ from .mlp_chain import (  # noqa: F401
     mlp_chain_create, mlp_chain_run, mlp_chain_destroy, mlp_chain_run_phase,
     mlp_chain_status, mlp_chain_last_error, mlp_chain_info,
     mlp_chain_debug_set_spin_limit, mlp_chain_debug_skip_producer, mlp_chain_debug_set_config,
-    mlp_chain_debug_read_intermediate, mlp_chain_debug_set_split,
+    mlp_chain_debug_read_intermediate, mlp_chain_debug_set_split, mlp_chain_debug_set_trace,
 )

@@ -4,9 +4,9 @@
 // Per-run synchronization state lives in the workspace and is never reset
 // between runs (no memset on the run path, so a run is a single kernel for
 // the fused policies):
-//   * the tile queue counter only grows; the host keeps the number of tickets
-//     all earlier runs drew (each run draws T1 + T2 + grid: every tile once and
-//     one exit ticket per workgroup) and passes it as the run's base;
+//   * the 8 tile-queue counters only grow: per run, queue x advances by its
+//     length plus the grid (every item once, one failed draw per workgroup),
+//     so the kernel derives each queue's base from the epoch;
 //   * tile flags hold the epoch of the run that last published them, and a
 //     consumer waits for (int32)(flag - epoch) >= 0;
 //   * row counters grow by N1t per run; a consumer of run e waits for
@@ -47,12 +47,14 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 uint32_t cdiv(int64_t a, int64_t b) { return (uint32_t)((a + b - 1) / b); }
 
-// Planner: the narrow 16-row tiles while M is small (weight streaming wants
-// many workgroups), 128 x 128 tiles with two LDS stages (two workgroups per
-// CU) once M grows and the matrix cores bound the run.  The crossover was
+// Planner: 16-row tiles while M fits one of them (weight streaming), 64 x
+// 128 tiles while M is a few hundred (each weight panel is read by as few
+// row blocks as possible), 128 x 128 tiles with two LDS stages (two
+// workgroups per CU) once the matrix cores bound the run.  Crossovers
 // measured on the GPT-3 shard (H=12288, I=6144) for M in 1..2048.
 int plan_config(int64_t M) {
-    if (M <= 96) return 0;
+    if (M <= 16) return 0;
+    if (M <= 256) return 1;
     return 2;
 }
 
@@ -88,9 +90,9 @@ struct mlp_chain {
     // run state
     uint32_t epoch;             // fused runs
     uint32_t gen1, gen2;        // GEMM1 / GEMM2 executions (split arrival targets)
-    uint32_t ticket_base;
     uint32_t spin_limit;
     uint32_t skip_producer;
+    uint64_t* trace;            // caller's timeline buffer (debug), or nullptr
     hipStream_t last_stream;
 };
 
@@ -168,7 +170,6 @@ int zero_workspace(mlp_chain* h) {
     h->epoch = 0;
     h->gen1 = 0;
     h->gen2 = 0;
-    h->ticket_base = 0;
     return MLP_OK;
 }
 
@@ -189,7 +190,7 @@ int build_workspace(mlp_chain* h) {
     const size_t c2_b = align_up((size_t)h->T2 * 4, 256);
     const size_t p1_b = h->S1 > 1 ? align_up((size_t)h->T1 * h->S1 * acc_bytes, 256) : 0;
     const size_t p2_b = h->S2 > 1 ? align_up((size_t)h->T2 * h->S2 * acc_bytes, 256) : 0;
-    h->sync_bytes = f_b + r_b + c1_b + c2_b + 3 * 256;
+    h->sync_bytes = f_b + r_b + c1_b + c2_b + 2048 + 2 * 256;
     h->ws_bytes = t_b + h->sync_bytes + p1_b + p2_b;
     hipError_t e = hipMalloc(&h->ws, h->ws_bytes);
     if (e != hipSuccess) {
@@ -207,10 +208,10 @@ int build_workspace(mlp_chain* h) {
     p += c1_b;
     h->cnt2 = reinterpret_cast<uint32_t*>(p);
     p += c2_b;
-    h->ticket = reinterpret_cast<uint32_t*>(p);
-    h->status = reinterpret_cast<uint32_t*>(p + 256);
-    h->zero = reinterpret_cast<uint16_t*>(p + 512);
-    p += 3 * 256;
+    h->ticket = reinterpret_cast<uint32_t*>(p);            // 8 queue counters, 256 bytes apart
+    h->status = reinterpret_cast<uint32_t*>(p + 2048);
+    h->zero = reinterpret_cast<uint16_t*>(p + 2048 + 256);
+    p += 2048 + 2 * 256;
     h->part1 = p1_b ? reinterpret_cast<float*>(p) : nullptr;
     p += p1_b;
     h->part2 = p2_b ? reinterpret_cast<float*>(p) : nullptr;
@@ -236,6 +237,7 @@ mlpc::ChainArgs make_args(const mlp_chain* h, const void* x, const void* w1, con
     a.T1 = h->T1;
     a.T2 = h->T2;
     a.group_m = GROUP_M;
+    a.rx = h->Mt >= 2 ? 2u : 1u;
     a.ticket = h->ticket;
     a.flags = h->flags;
     a.rowcnt = h->rowcnt;
@@ -251,11 +253,11 @@ mlpc::ChainArgs make_args(const mlp_chain* h, const void* x, const void* w1, con
     a.cnt2 = h->cnt2;
     a.gen1 = h->gen1;
     a.gen2 = h->gen2;
-    a.ticket_base = h->ticket_base;
     a.epoch = h->epoch;
     a.grid = h->grid;
     a.spin_limit = h->spin_limit;
     a.skip_producer = h->skip_producer;
+    a.trace = h->trace;
     a.policy = h->policy;
     return a;
 }
@@ -326,6 +328,7 @@ mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype
     h->forced_s2 = 0;
     h->spin_limit = DEFAULT_SPIN_LIMIT;
     h->skip_producer = mlpc::NO_SKIP;
+    h->trace = nullptr;
     h->last_stream = nullptr;
     h->ws = nullptr;
     if (apply_plan(h, plan_config(M)) != MLP_OK || build_workspace(h) != MLP_OK) {
@@ -378,7 +381,6 @@ int mlp_chain_run(mlp_chain_t h, const void* x, const void* w1, const void* w2, 
         h->gen2 -= 1u;
         return rc;
     }
-    h->ticket_base += h->T1 * h->S1 + h->T2 * h->S2 + h->grid;
     return MLP_OK;
 }
 
@@ -460,6 +462,12 @@ int mlp_chain_debug_set_split(mlp_chain_t h, int s1, int s2) {
     h->forced_s1 = s1;
     h->forced_s2 = s2;
     return replan(h);
+}
+
+int mlp_chain_debug_set_trace(mlp_chain_t h, void* buffer) {
+    if (!h) return fail(MLP_EINVAL, "NULL handle");
+    h->trace = static_cast<uint64_t*>(buffer);
+    return MLP_OK;
 }
 
 int mlp_chain_debug_read_intermediate(mlp_chain_t h, void* dst, void* hip_stream) {

@@ -7,8 +7,10 @@
     X(0, 16, 64, 1, 2, 4, 4)     /* small M: narrow tiles, weight streaming */                \
     X(1, 64, 128, 2, 2, 2, 2)    /* medium M, two stages */                                   \
     X(2, 128, 128, 2, 2, 2, 2)   /* large M, two stages: two workgroups per CU */             \
-    X(3, 128, 128, 2, 2, 3, 1)   /* large M, three stages, one workgroup per CU */            \
-    X(4, 256, 128, 4, 2, 3, 2)   /* large M, 8 waves of 64x64 */
+    X(3, 256, 256, 2, 2, 2, 1)   /* large M, 128x128 per wave */                              \
+    X(4, 256, 128, 2, 2, 2, 1)   /* large M, 128x64 per wave */                               \
+    X(5, 128, 256, 2, 2, 2, 1)   /* large M, 64x128 per wave */                               \
+    X(6, 16, 128, 1, 2, 4, 2)    /* small M, 16x64 per wave */
 
 #define MLPC_COUNT_CFG(id, ...) +1
 constexpr int MLPC_NUM_CONFIGS = 0 MLPC_CONFIGS(MLPC_COUNT_CFG);

@@ -59,7 +59,8 @@ struct ChainArgs {
     int act;
     uint32_t Mt, N1t, N2t, T1, T2;
     uint32_t group_m;       // row blocks per swizzle group
-    uint32_t* ticket;       // tile queue counter
+    uint32_t rx;            // XCD grid rows (1, 2, 4 or 8; the grid is rx x 8/rx)
+    uint32_t* ticket;       // 8 tile-queue counters, 64 words apart (one queue per XCD)
     uint32_t* flags;        // [Mt * N1t] ready epochs (tile_sync)
     uint32_t* rowcnt;       // [Mt] producer completions (row_sync)
     uint32_t* status;       // sticky watchdog status (nonzero = a consumer gave up)
@@ -74,7 +75,7 @@ struct ChainArgs {
     uint32_t* cnt1;         // [T1] part arrivals (S1 > 1)
     uint32_t* cnt2;         // [T2] part arrivals (S2 > 1)
     uint32_t gen1, gen2;    // this run's GEMM1 / GEMM2 generation (arrival targets gen * S)
-    uint32_t ticket_base;   // tickets drawn by earlier runs (mod 2^32)
+    uint64_t* trace;        // optional timeline: 4 words per ticket (nullptr = off)
     uint32_t epoch;         // this run's epoch (mod 2^32)
     uint32_t grid;          // persistent workgroups
     uint32_t spin_limit;    // back-off iterations before a consumer gives up
@@ -177,6 +178,58 @@ __device__ __forceinline__ void tile_coords(uint32_t t, uint32_t Mt, uint32_t Nt
     const uint32_t r = t - gi * per_group;
     mb = first + r % gsz;
     nb = r / gsz;
+}
+
+// Workgroups are dispatched to the 8 XCDs round-robin by index, and each XCD
+// has its own L2.  Map index b to item (b % 8) * chunk + b / 8, so that each
+// XCD gets one contiguous chunk of the item order (whose neighbouring tiles
+// share weight panels and activation rows).  A bijection on [0, n).
+__device__ __forceinline__ uint32_t xcd_chunked(uint32_t b, uint32_t n) {
+    const uint32_t x = b & 7, i = b >> 3;
+    const uint32_t q = n >> 3, r = n & 7;
+    return x < r ? x * (q + 1) + i : r * (q + 1) + (x - r) * q + i;
+}
+
+// XCD partition of a GEMM's Mt x Nt tile grid (S parts per tile): the 8
+// XCDs form an Rx x (8/Rx) grid, XCD x owns a contiguous block of row
+// blocks and column blocks, and walks it row-major with the parts of a tile
+// adjacent.  Both GEMMs use the same row split, so the consumers of a row
+// block sit on the XCDs whose producers complete it, and each row block is
+// finished early (row-major) for its consumers; a block's weight panels and
+// activation rows are shared in that XCD's L2.
+struct XcdBlock {
+    uint32_t r0, c0, nc, len;    // first row block, first column block, columns, items
+};
+
+__device__ __forceinline__ XcdBlock xcd_block(uint32_t Mt, uint32_t Nt, uint32_t S, uint32_t Rx, uint32_t x) {
+    const uint32_t Cx = 8 / Rx;
+    const uint32_t rx = x / Cx, cx = x % Cx;
+    const uint32_t r0 = rx * Mt / Rx, r1 = (rx + 1) * Mt / Rx;
+    const uint32_t c0 = cx * Nt / Cx, c1 = (cx + 1) * Nt / Cx;
+    return XcdBlock{r0, c0, c1 - c0, (r1 - r0) * (c1 - c0) * S};
+}
+
+// Item c of XCD block b -> tile (row block, column block) and part.
+__device__ __forceinline__ void xcd_item(const XcdBlock& b, uint32_t S, uint32_t c, uint32_t& mb, uint32_t& nb,
+                                         uint32_t& part) {
+    part = c % S;
+    const uint32_t tc = c / S;
+    mb = b.r0 + tc / b.nc;
+    nb = b.c0 + tc % b.nc;
+}
+
+// Position p of the concatenation of the 8 XCD blocks -> tile and part.
+__device__ __forceinline__ void xcd_position(uint32_t Mt, uint32_t Nt, uint32_t S, uint32_t Rx, uint32_t p,
+                                             uint32_t& mb, uint32_t& nb, uint32_t& part) {
+    for (uint32_t x = 0; x < 8; ++x) {
+        const XcdBlock b = xcd_block(Mt, Nt, S, Rx, x);
+        if (p < b.len) {
+            xcd_item(b, S, p, mb, nb, part);
+            return;
+        }
+        p -= b.len;
+    }
+    mb = nb = part = 0;   // not reached for p < Mt * Nt * S
 }
 
 // ------------------------------------------------------------ flags / ticket
@@ -352,9 +405,21 @@ __device__ __forceinline__ void issue_a(const TileJob& j, int ks) {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// ds_read_b64_tr_b16 as inline asm.  Through the builtin, the compiler's
+// wait-counter pass could not always tell these reads apart from the DMA
+// writes into the other stages and put s_waitcnt vmcnt(0) in front of them,
+// which drained the whole ring before every slab.  The asm result must not
+// be used before lds_wait() (which carries the fragments as operands, so the
+// MFMAs depend on it).
 __device__ __forceinline__ u32x2 lds_read_tr(const char* p) {
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) s16x4*)(const_cast<char*>(p))));
+    u32x2 r;
+    const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+    return r;
+}
+
+__device__ __forceinline__ void lds_wait(u32x4& v) {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v) :: "memory");
 }
 
 // MFMA over the slab in stage S.
@@ -386,6 +451,8 @@ __device__ __forceinline__ void compute_stage(f32x4 (&acc)[C::FM][C::FN]) {
             const u32x2 hi = lds_read_tr(sb + (k_hi * C::CPR + b_chunk<C>(k_hi, c)) * 16 + half);
             bf[fn] = u32x4{lo[0], lo[1], hi[0], hi[1]};
         }
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) lds_wait(bf[fn]);
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
@@ -605,14 +672,10 @@ __device__ __forceinline__ bool split_reduce(f32x4 (&acc)[C::FM][C::FN], float* 
 // true if this part wrote the tile's output (always, unless the tile is
 // split and another part arrives last).
 template <class C, int DT, class Wait>
-__device__ __forceinline__ bool run_tile(const ChainArgs& a, int role, uint32_t tile, uint32_t s,
+__device__ __forceinline__ bool run_tile(const ChainArgs& a, int role, uint32_t mb, uint32_t nb, uint32_t s,
                                          uint32_t* s_flag, Wait& wait) {
     f32x4 acc[C::FM][C::FN];
-    uint32_t mb, nb;
-    if (role == 1)
-        tile_coords(tile, a.Mt, a.N1t, a.group_m, mb, nb);
-    else
-        tile_coords(tile, a.Mt, a.N2t, a.group_m, mb, nb);
+    const uint32_t tile = mb * (role == 1 ? a.N1t : a.N2t) + nb;
     const TileJob j = role == 1 ? producer_job<C>(a, mb, nb, s) : consumer_job<C>(a, mb, nb, s);
     tile_mainloop<C, DT>(j, acc, wait);
     const uint32_t S = role == 1 ? a.S1 : a.S2;

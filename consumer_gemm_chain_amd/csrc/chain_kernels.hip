@@ -29,18 +29,25 @@
 namespace mlpc {
 
 // One workgroup per tile part: blockIdx = tile * S + part.
+// One workgroup per tile part.  Workgroups are dispatched to the XCDs
+// round-robin, so block b runs on XCD b % 8: give each XCD a contiguous
+// chunk of the concatenated XCD blocks.
 template <class C, int DT>
 __global__ __launch_bounds__(C::NT) void gemm1_act_kernel(ChainArgs a) {
     __shared__ uint32_t s_flag;
     NoWait w;
-    run_tile<C, DT>(a, 1, blockIdx.x / a.S1, blockIdx.x % a.S1, &s_flag, w);
+    uint32_t mb, nb, part;
+    xcd_position(a.Mt, a.N1t, a.S1, a.rx, xcd_chunked(blockIdx.x, a.T1 * a.S1), mb, nb, part);
+    run_tile<C, DT>(a, 1, mb, nb, part, &s_flag, w);
 }
 
 template <class C, int DT>
 __global__ __launch_bounds__(C::NT) void gemm2_kernel(ChainArgs a) {
     __shared__ uint32_t s_flag;
     NoWait w;
-    run_tile<C, DT>(a, 2, blockIdx.x / a.S2, blockIdx.x % a.S2, &s_flag, w);
+    uint32_t mb, nb, part;
+    xcd_position(a.Mt, a.N2t, a.S2, a.rx, xcd_chunked(blockIdx.x, a.T2 * a.S2), mb, nb, part);
+    run_tile<C, DT>(a, 2, mb, nb, part, &s_flag, w);
 }
 
 // Consumer-side wait of the persistent kernel.  One functor type serves
@@ -70,6 +77,7 @@ struct ChainWait {
     uint32_t* s_ready;       // LDS broadcast slot
     uint32_t ready;          // tile_sync: blocks below this are acquired or not needed (uniform)
     bool waited;             // row_sync: the part's single wait is done (uniform)
+    uint64_t t_waited;       // realtime clock after the last wait (timeline trace)
     __device__ __forceinline__ void operator()(int ks) {
         if (!active) return;
         if constexpr (POL == POL_ROW) {
@@ -77,6 +85,7 @@ struct ChainWait {
             waited = true;
             if ((threadIdx.x >> 6) == 0) wave_acquire_count(cnt, target, status, limit);
             lds_barrier();
+            t_waited = __builtin_amdgcn_s_memrealtime();
         } else {
             uint32_t need = (uint32_t)((ks * BK + BK - 1) / bn1);    // last block slab ks reads
             if (need > n1t - 1) need = n1t - 1;
@@ -87,46 +96,96 @@ struct ChainWait {
             }
             lds_barrier();
             ready = __builtin_amdgcn_readfirstlane(*s_ready);
+            t_waited = __builtin_amdgcn_s_memrealtime();
         }
     }
 };
 
+// The tile queue.  Queue x (one counter per XCD) holds the GEMM1 tile
+// parts of XCD x's block of the GEMM1 grid, then the GEMM2 tile parts of its
+// block of the GEMM2 grid (same row split), each walked row-major.  A
+// workgroup owns queue blockIdx % 8 -- the XCD it is dispatched to -- and
+// when its queue runs dry it takes from the next queues in order.  Every
+// workgroup fails exactly once on each queue per run, so each queue's counter
+// advances by its length plus the grid per run and needs no reset.  Items
+// are numbered for flags, trace and test hooks as GEMM1 parts
+// (mb * N1t + nb) * S1 + part, then GEMM2 parts P1 + (mb * N2t + nb) * S2 + part.
+// Deadlock freedom: a queue hands out consumers only after all its producers
+// are drawn; a consumer waits only for producers; a queue with an undrawn
+// producer has handed out no consumer, so its owner workgroups (at least one
+// per queue: grid >= 8) are running producers or about to draw one, and
+// producers never wait.
 template <class C, int DT, int POL>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
 void chain_persistent_kernel(ChainArgs a) {
     __shared__ uint32_t s_ticket;
     __shared__ uint32_t s_ready;
     __shared__ uint32_t s_flag;
-    // tickets [0, P1) are GEMM1 tile parts, [P1, P1 + P2) GEMM2 tile parts
-    const uint32_t P1 = a.T1 * a.S1, P2 = a.T2 * a.S2;
-    const uint32_t total = P1 + P2;
+    const uint32_t P1 = a.T1 * a.S1;
     const int bn1 = a.act == ACT_SWIGLU ? C::BN / 2 : C::BN;
+    const uint32_t own = blockIdx.x & 7;
+    uint32_t visit = 0;              // queues visited so far (own queue first)
     for (;;) {
-        if (threadIdx.x == 0)
-            s_ticket = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
-                       a.ticket_base;
+        // draw the next item (thread 0), from the current queue or the next ones
+        if (threadIdx.x == 0) {
+            uint32_t item = 0xffffffffu;
+            while (visit < 8) {
+                const uint32_t x = (own + visit) & 7;
+                const XcdBlock bp = xcd_block(a.Mt, a.N1t, a.S1, a.rx, x);
+                const XcdBlock bc = xcd_block(a.Mt, a.N2t, a.S2, a.rx, x);
+                const uint32_t len = bp.len + bc.len;
+                const uint32_t base = (a.epoch - 1u) * (len + a.grid);
+                const uint32_t c = __hip_atomic_fetch_add(a.ticket + 64 * x, 1u, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT) - base;
+                if (c < len) {
+                    uint32_t mb, nb, part;
+                    if (c < bp.len) {
+                        xcd_item(bp, a.S1, c, mb, nb, part);
+                        item = (mb * a.N1t + nb) * a.S1 + part;
+                    } else {
+                        xcd_item(bc, a.S2, c - bp.len, mb, nb, part);
+                        item = P1 + (mb * a.N2t + nb) * a.S2 + part;
+                    }
+                    break;
+                }
+                ++visit;                 // this queue is dry: never come back
+            }
+            s_ticket = item;
+        }
         __syncthreads();
-        // The ticket is the same for every thread of the workgroup; reading it
+        // The item is the same for every thread of the workgroup; reading it
         // through readfirstlane makes that visible to the compiler, so every
         // branch on it (and the loop exit) is a scalar branch and all lanes of
         // a wave stay on one path through the barriers below.
         const uint32_t t = __builtin_amdgcn_readfirstlane(s_ticket);
         __syncthreads();
-        if (t >= total) break;
+        if (t == 0xffffffffu) break;
         const bool prod = t < P1;
         // test hook: a skipped producer part does no work and no release
         if (!(prod && t == a.skip_producer)) {
             const uint32_t S = prod ? a.S1 : a.S2;
             const uint32_t u = prod ? t : t - P1;
             const uint32_t tile = u / S, part = u % S;
-            uint32_t mb, nb;
-            tile_coords(tile, a.Mt, prod ? a.N1t : a.N2t, a.group_m, mb, nb);
+            const uint32_t nt = prod ? a.N1t : a.N2t;
+            const uint32_t mb = tile / nt, nb = tile % nt;
             // first producer block the part's K range reads
             const uint32_t first = prod ? 0u : (part * a.ksp2 * BK) / (uint32_t)bn1;
+            const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
             ChainWait<POL> w{!prod, a.flags + mb * a.N1t, a.rowcnt + mb, a.N1t,
                              POL == POL_ROW ? a.epoch * a.N1t : a.epoch, bn1, a.status, a.spin_limit,
-                             &s_ready, first, false};
-            const bool wrote = run_tile<C, DT>(a, prod ? 1 : 2, tile, part, &s_flag, w);
+                             &s_ready, first, false, t_start};
+            const bool wrote = run_tile<C, DT>(a, prod ? 1 : 2, mb, nb, part, &s_flag, w);
+            if (a.trace && threadIdx.x == 0) {
+                // timeline: start, last wait done, end (100 MHz realtime clock), and where it ran
+                uint32_t hw = 0, xcc = 0;
+                asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+                asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+                uint64_t* r = a.trace + 4 * (size_t)t;
+                r[0] = t_start;
+                r[1] = w.t_waited;
+                r[2] = __builtin_amdgcn_s_memrealtime();
+                r[3] = (uint64_t)t | ((uint64_t)(xcc & 0xf) << 32) | ((uint64_t)hw << 36) | ((uint64_t)wrote << 63);
+            }
             if (prod && wrote) {
                 // every thread's T stores happen before thread 0's agent-scope
                 // release (workgroup release + barrier), which publishes the tile

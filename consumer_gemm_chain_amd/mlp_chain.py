@@ -28,7 +28,7 @@ EXPORTS = ("mlp_chain_create", "mlp_chain_run", "mlp_chain_destroy", "mlp_chain_
            "mlp_chain_status", "mlp_chain_last_error", "mlp_chain_info",
            "mlp_chain_debug_set_spin_limit", "mlp_chain_debug_skip_producer",
            "mlp_chain_debug_set_config", "mlp_chain_debug_set_split",
-           "mlp_chain_debug_read_intermediate")
+           "mlp_chain_debug_set_trace", "mlp_chain_debug_read_intermediate")
 
 INFO_FIELDS = ("BM", "BN1", "BN2", "BK", "Mt", "N1t", "N2t", "T1", "T2", "grid", "wg_per_cu",
                "threads", "cus", "epoch", "config", "workspace_bytes", "S1", "S2", "ksp1", "ksp2")
@@ -75,6 +75,8 @@ def load_library(path: str | None = None):
     lib.mlp_chain_debug_set_config.restype = ci
     lib.mlp_chain_debug_set_split.argtypes = [vp, ci, ci]
     lib.mlp_chain_debug_set_split.restype = ci
+    lib.mlp_chain_debug_set_trace.argtypes = [vp, vp]
+    lib.mlp_chain_debug_set_trace.restype = ci
     lib.mlp_chain_debug_read_intermediate.argtypes = [vp, vp, vp]
     lib.mlp_chain_debug_read_intermediate.restype = ci
     _lib = lib
@@ -143,6 +145,10 @@ def mlp_chain_debug_set_config(h: int, config_id: int) -> int:
 
 def mlp_chain_debug_set_split(h: int, s1: int, s2: int) -> int:
     return _check(load_library().mlp_chain_debug_set_split(h, int(s1), int(s2)))
+
+
+def mlp_chain_debug_set_trace(h: int, buffer: int | None) -> int:
+    return _check(load_library().mlp_chain_debug_set_trace(h, buffer))
 
 
 def mlp_chain_debug_read_intermediate(h: int, dst: int, hip_stream: int | None) -> int:
@@ -226,6 +232,20 @@ class MlpChain:
 
     def skip_producer(self, tile: int):
         mlp_chain_debug_skip_producer(self.h, tile)
+
+    def trace(self, enable: bool = True):
+        """Attach a timeline buffer (a device int64 tensor of 4 words per
+        ticket) to the fused runs, or detach it; returns the buffer."""
+        import torch
+        if not enable:
+            mlp_chain_debug_set_trace(self.h, None)
+            self._trace = None
+            return None
+        info = self.info()
+        n = info["T1"] * info["S1"] + info["T2"] * info["S2"]
+        self._trace = torch.zeros((n, 4), dtype=torch.int64, device="cuda")
+        mlp_chain_debug_set_trace(self.h, self._trace.data_ptr())
+        return self._trace
 
     def read_intermediate(self, stream=None):
         """Copy of the intermediate T [M, I] left by the last run (a device tensor)."""

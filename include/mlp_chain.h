@@ -154,6 +154,17 @@ int mlp_chain_debug_set_config(mlp_chain_t h, int config_id);
  * NULL handle or a split outside 0..64. */
 int mlp_chain_debug_set_split(mlp_chain_t h, int s1, int s2);
 
+/* Timeline trace of the fused policies (measurement of the non-overlapped
+ * share, as the FLUX summary card advises in Interesting ideas, I3):
+ * `buffer` is a DEVICE buffer of 4 * (T1*S1 + T2*S2) uint64 (see
+ * mlp_chain_info), NULL turns tracing off.  Each run then writes, per ticket
+ * t (producer parts first), words 4t..4t+3 = { start, end of the part's
+ * last wait, end } on the 100 MHz realtime clock, and { t | XCD << 32 |
+ * HW_ID << 36 | (part wrote the tile's output) << 63 }.  The buffer stays
+ * owned by the caller and must outlive the runs that use it.  Returns
+ * MLP_EINVAL for a NULL handle. */
+int mlp_chain_debug_set_trace(mlp_chain_t h, void* buffer);
+
 /* Copy the handle's intermediate T [M, I] (as left by the last run on the
  * handle) into the caller's device buffer `dst` (M * I elements of the
  * storage dtype), enqueued on `hip_stream` after the handle's work.  For

@@ -1,13 +1,14 @@
 """Regression check on the compiled gfx950 code of the persistent kernel
 (no GPU needed: hipcc cross-compiles).
 
-The persistent kernel's loop draws a ticket on thread 0, publishes it through
-LDS, and every thread reads it back between two barriers.  An earlier build
-let the compiler merge the thread-0-only flag release at the end of an
-iteration with the thread-0-only ticket draw at the top, producing an inner
-loop in which the other threads re-read the old ticket forever.  This test
-asserts that, in every instantiation, the ticket atomic and the LDS read of
-the ticket sit at the same (outermost) loop depth."""
+The persistent kernel's loop draws a ticket on thread 0 (a small loop over
+the per-XCD queues), publishes it through LDS, and every thread reads it
+back between two barriers.  An earlier build let the compiler merge the
+thread-0-only flag release at the end of an iteration with the thread-0-only
+ticket draw at the top, producing an inner loop in which the other threads
+re-read the old ticket forever.  This test asserts that, in every
+instantiation, the LDS read of the ticket sits in the outermost loop and the
+ticket atomic either there or in the draw loop nested directly in it."""
 import os
 import re
 import shutil
@@ -45,7 +46,7 @@ def _functions(text, prefix):
         yield m.group(1), text[start:end]
 
 
-def test_ticket_draw_and_read_at_same_loop_depth(asm):
+def test_ticket_read_in_outermost_loop(asm):
     kernels = list(_functions(asm, "_ZN4mlpc23chain_persistent_kernel"))
     assert len(kernels) == 4 * b.num_configs()   # configs x 2 dtypes x 2 policies
     for name, body in kernels:
@@ -59,7 +60,7 @@ def test_ticket_draw_and_read_at_same_loop_depth(asm):
                 d_atomic = depth
             if d_atomic is not None and d_read is None and "ds_read_b32" in line:
                 d_read = depth
-        assert d_atomic == 1 and d_read == 1, (name, d_atomic, d_read)
+        assert d_read == 1 and d_atomic in (1, 2), (name, d_atomic, d_read)
 
 
 def test_no_mixed_precision_fma_in_epilogues(asm):
