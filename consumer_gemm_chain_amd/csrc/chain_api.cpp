@@ -280,8 +280,10 @@ mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype
              (long long)H, (long long)I);
         return nullptr;
     }
+    // Every operand stays below 2^31 bytes and every row below 2^23 elements
+    // (32-bit element and byte offsets within an operand cannot wrap).
     const int64_t lim = (int64_t)1 << 30;
-    if (M * H >= lim || M * I >= lim || H * I * 2 >= lim || M >= (1 << 24)) {
+    if (M * H >= lim || M * I >= lim || H * I * 2 >= lim || M >= (1 << 24) || H > (1 << 22) || I > (1 << 22)) {
         fail(MLP_EINVAL, "sizes too large for 32-bit tile indexing (M=%lld H=%lld I=%lld)",
              (long long)M, (long long)H, (long long)I);
         return nullptr;

@@ -4,13 +4,14 @@
 #pragma once
 
 #define MLPC_CONFIGS(X)                                                                        \
-    X(0, 16, 64, 1, 2, 4, 4)     /* small M: narrow tiles, weight streaming */                \
+    X(0, 16, 64, 1, 2, 4, 2)     /* small M: narrow tiles, weight streaming */                \
     X(1, 64, 128, 2, 2, 2, 2)    /* medium M, two stages */                                   \
     X(2, 128, 128, 2, 2, 2, 2)   /* large M, two stages: two workgroups per CU */             \
-    X(3, 256, 256, 2, 2, 2, 1)   /* large M, 128x128 per wave */                              \
-    X(4, 256, 128, 2, 2, 2, 1)   /* large M, 128x64 per wave */                               \
-    X(5, 128, 256, 2, 2, 2, 1)   /* large M, 64x128 per wave */                               \
-    X(6, 16, 128, 1, 2, 4, 2)    /* small M, 16x64 per wave */
+    X(3, 256, 128, 2, 2, 2, 1)   /* 128x64 per wave, one wave per SIMD */                     \
+    X(4, 128, 256, 2, 2, 2, 1)   /* 64x128 per wave, one wave per SIMD */                     \
+    X(5, 16, 128, 1, 2, 4, 1)    /* small M, 16x64 per wave */                                \
+    X(6, 128, 256, 2, 4, 2, 2)   /* eight waves of 64x64 */                                   \
+    X(7, 256, 128, 4, 2, 2, 2)   /* eight waves of 64x64 */
 
 #define MLPC_COUNT_CFG(id, ...) +1
 constexpr int MLPC_NUM_CONFIGS = 0 MLPC_CONFIGS(MLPC_COUNT_CFG);

@@ -6,19 +6,26 @@
 //   * MFMA main loop: v_mfma_f32_16x16x32_{f16,bf16}, fp32 accumulators,
 //     BK = 64 K-slab per step, K steps in ascending order.
 //   * Operand staging: both operands go from global memory straight into
-//     LDS (global_load_lds_dwordx4, no registers) through an NS-deep ring
-//     of LDS stages, so NS-1 slabs are in flight while one is computed (the
+//     LDS (global_load_lds_dwordx4, no registers) through a ring of NS LDS
+//     stages, so up to NS-1 slabs are in flight while one is computed (the
 //     pipeline depth of the jonahsamost bearblog post on adding depth to a
-//     GEMM).  Every stage is a separate LDS object so the compiler can tell
-//     the stages apart and does not drain the ring before each LDS read; the
-//     ring is synchronized by explicit vmcnt waits and bare barriers.
+//     GEMM).  The ring is synchronized by explicit vmcnt waits and bare
+//     barriers.  All main-loop LDS reads are inline asm with explicit
+//     lgkmcnt waits: the compiler's wait-counter pass cannot tell an LDS
+//     read of one stage from the DMA writes into another and would otherwise
+//     wait for every DMA in flight (vmcnt(0)) before the first read of each
+//     slab, draining the ring.
+//   * Fragment double buffering: the MFMA fragments of the next half slab
+//     are read from LDS while the MFMAs of the current half run.
 //   * LDS layouts: the activation tile A is stored K-contiguous (8 chunks of
 //     16 bytes per row) and read as MFMA fragments with ds_read_b128; the
 //     weight tile B keeps the weights' [K, N] row-major layout and is read
 //     with the gfx950 transpose read ds_read_b64_tr_b16 (each 16-lane group
 //     reads a 4 x 16 block and receives it transposed).  Both use XOR chunk
 //     swizzles, applied by choosing which global chunk each lane fetches,
-//     against LDS bank conflicts (the bearblog post on swizzling).
+//     against LDS bank conflicts (the bearblog post on swizzling).  The
+//     swizzles depend only on the lane, so every fragment address is a
+//     per-lane base plus a compile-time offset.
 //   * Edges: chunks outside the matrices are fetched from a zero page, so
 //     the ring always holds zeros beyond M, N and K.
 //   * Epilogue: activation on the fp32 accumulators, one round-to-nearest-even
@@ -33,6 +40,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace mlpc {
 
@@ -106,17 +115,26 @@ struct TileCfg {
     static constexpr int EPI_PASSES = BM * (BN + 8) * 2 <= STAGE ? 1 : BM * (BN + 8) * 2 <= 2 * STAGE ? 2 : 4;
     static constexpr int EPI_ROWS = BM / EPI_PASSES;
     static_assert(EPI_ROWS * (BN + 8) * 2 <= STAGE, "epilogue pass must fit one stage");
-    static constexpr int STAGE0 = STAGE;
     static constexpr int CPR = BN / 8;                   // 16-byte chunks per B row
     static constexpr int A_PER_WAVE = BM / 8 / NW;       // 1 KB DMA instructions per wave per slab
     static constexpr int B_PER_WAVE = CPR / NW;
     static_assert(A_PER_WAVE * NW * 8 == BM && B_PER_WAVE * NW == CPR, "DMA split across waves");
     static constexpr int LPS = A_PER_WAVE + B_PER_WAVE;  // DMA instructions per wave per slab
     static_assert(LPS * (NS - 2) <= 63, "vmcnt range");
-    static constexpr int lds_bytes() { return STAGE0 + (NS - 1) * STAGE; }
+    static constexpr int NREAD = FM + 2 * FN;            // LDS reads per fragment set
+    static constexpr int lds_bytes() { return NS * STAGE; }
 };
 
 // ------------------------------------------------------------------ helpers
+
+// f(std::integral_constant<int, i>) for i = I .. N-1 (compile-time indices).
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
 
 template <int DT>
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
@@ -336,16 +354,24 @@ __device__ __forceinline__ int b_column(const TileJob& j, int nb, bool& ok) {
     return oc;
 }
 
-// The LDS stages of configuration C: one LDS object per stage (stage 0 also
-// holds the epilogue staging area).
-template <class C, int S>
-__device__ __forceinline__ char* lds_stage() {
-    __shared__ __attribute__((aligned(16))) char buf[S == 0 ? C::STAGE0 : C::STAGE];
+// The LDS ring of configuration C: NS stages of STAGE bytes (A slab, then B
+// slab); stage 0 also holds the epilogue staging area.
+template <class C>
+__device__ __forceinline__ char* lds_ring() {
+    __shared__ __attribute__((aligned(16))) char buf[C::lds_bytes()];
     return buf;
 }
 
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+
 // Physical 16-byte chunk of logical chunk c in A row r (8 chunks per row).
-__device__ __forceinline__ int a_chunk(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+// A ds_read_b128 fragment read covers 16 consecutive rows (one chunk each);
+// the XOR term takes 16 distinct (row parity, chunk) pairs over any 16
+// aligned rows, so those 16 lanes hit 64 distinct banks.  It depends on
+// r mod 16 only, so fragments 16 rows apart are a fixed offset apart.
+__device__ __forceinline__ int a_chunk(int r, int c) { return c ^ ((r ^ ((r & 15) >> 3)) & 7); }
 
 // Physical chunk of logical chunk c in B row k.  A transpose read covers,
 // per 32 lanes, rows 8g + (0..3) for g in {0,1} (or {2,3}) and two adjacent
@@ -366,12 +392,15 @@ __device__ __forceinline__ void dma16(const uint16_t* src, char* lds) {
 // Issue the DMA of slab ks (B part and/or A part) into stage S.  Every wave
 // issues B_PER_WAVE B instructions and A_PER_WAVE A instructions; lane i of
 // an instruction fills LDS chunk L0 + i, and picks the global chunk that
-// belongs there under the swizzle (or the zero page).
+// belongs there under the swizzle (or the zero page).  Slabs at or past the
+// tile's ks1 are issued too (all zero page), so that every wave always has
+// the same number of DMA instructions in flight.
 template <class C, int S>
 __device__ __forceinline__ void issue_b(const TileJob& j, int ks) {
-    char* st = lds_stage<C, S>() + C::A_BYTES;
+    char* st = lds_ring<C>() + S * C::STAGE + C::A_BYTES;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int k0 = ks * BK;
+    const int kend = min(j.K, j.ks1 * BK);      // slabs at or past ks1 read the zero page
 #pragma unroll
     for (int q = 0; q < C::B_PER_WAVE; ++q) {
         const int L0 = (wave * C::B_PER_WAVE + q) * 64;
@@ -381,92 +410,142 @@ __device__ __forceinline__ void issue_b(const TileJob& j, int ks) {
         bool ok;
         const int gcol = b_column(j, c, ok);
         const int gk = k0 + k;
-        const uint16_t* src = (ok && gk < j.K) ? j.B + (size_t)gk * j.ldb + gcol : j.zero;
+        const uint16_t* src = (ok && gk < kend) ? j.B + (size_t)gk * j.ldb + gcol : j.zero;
         dma16(src, st + L0 * 16);
     }
 }
 
 template <class C, int S>
 __device__ __forceinline__ void issue_a(const TileJob& j, int ks) {
-    char* st = lds_stage<C, S>();
+    char* st = lds_ring<C>() + S * C::STAGE;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int k0 = ks * BK;
+    const int kend = min(j.K, j.ks1 * BK);
 #pragma unroll
     for (int q = 0; q < C::A_PER_WAVE; ++q) {
         const int L0 = (wave * C::A_PER_WAVE + q) * 64;
         const int L = L0 + lane;
         const int r = L >> 3, c = a_chunk(r, L & 7);
         const int gm = j.m0 + r, gk = k0 + c * 8;
-        const uint16_t* src = (gm < j.a_rows && gk < j.K) ? j.A + (size_t)gm * j.lda + gk : j.zero;
+        const uint16_t* src = (gm < j.a_rows && gk < kend) ? j.A + (size_t)gm * j.lda + gk : j.zero;
         dma16(src, st + L0 * 16);
     }
 }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// ds_read_b64_tr_b16 as inline asm.  Through the builtin, the compiler's
-// wait-counter pass could not always tell these reads apart from the DMA
-// writes into the other stages and put s_waitcnt vmcnt(0) in front of them,
-// which drained the whole ring before every slab.  The asm result must not
-// be used before lds_wait() (which carries the fragments as operands, so the
-// MFMAs depend on it).
-__device__ __forceinline__ u32x2 lds_read_tr(const char* p) {
-    u32x2 r;
-    const uint32_t addr = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
-    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+// LDS fragment reads as inline asm: the result must not be used before
+// lgkm_wait() and pin() (the MFMAs depend on the pinned values).
+template <uint32_t OFF>
+__device__ __forceinline__ u32x4 ds_read_b128(uint32_t addr) {
+    static_assert(OFF < 65536, "ds offset field");
+    u32x4 r;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
     return r;
 }
 
-__device__ __forceinline__ void lds_wait(u32x4& v) {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(v) :: "memory");
+template <uint32_t OFF>
+__device__ __forceinline__ u32x2 ds_read_tr16_b64(uint32_t addr) {
+    static_assert(OFF < 65536, "ds offset field");
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+    return r;
 }
 
-// MFMA over the slab in stage S.
-template <class C, int DT, int S>
-__device__ __forceinline__ void compute_stage(f32x4 (&acc)[C::FM][C::FN]) {
-    const char* sa = lds_stage<C, S>();
-    const char* sb = sa + C::A_BYTES;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+// Wait until at most N LDS instructions of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void lgkm_wait() {
+    asm volatile("s_waitcnt lgkmcnt(%0)" :: "i"(N < 15 ? N : 15) : "memory");
+}
+
+template <class T>
+__device__ __forceinline__ void pin(T& v) { asm volatile("" : "+v"(v)); }
+
+// One wave's MFMA operands for a 32-deep half slab.
+template <class C>
+struct Frags {
+    u32x4 a[C::FM];
+    u32x4 b[C::FN];
+};
+
+// Per-lane LDS byte addresses of the first fragments in stage 0: A
+// fragment fm = 0 for each half slab kk, B fragment fn (half slab 0, rows
+// k..k+3).  Every other fragment address is one of these plus a
+// compile-time offset (stage, fm, kk, upper four rows).
+template <class C>
+struct FragBase {
+    uint32_t a[2];
+    uint32_t b[C::FN];
+};
+
+template <class C>
+__device__ __forceinline__ FragBase<C> frag_base() {
+    FragBase<C> f;
+    const uint32_t ring = lds_addr(lds_ring<C>());
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int g = lane >> 4, jj = lane & 15;
+    const int r = wm * C::WTM + jj;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        u32x4 af[C::FM];
-        u32x4 bf[C::FN];
+    for (int kk = 0; kk < 2; ++kk) f.a[kk] = ring + (r * 8 + a_chunk(r, kk * 4 + g)) * 16;
+    // lane (g, jj) of a transpose read: row k = 8g + jj/4 (+4 for the upper
+    // rows, +32 for half slab 1), columns (jj%4)*4..+3 of the fragment.
+    // b_chunk depends on k & 3 and (k >> 3) & 1 only, which neither +4 nor
+    // +32 changes.
+    const int k = g * 8 + (jj >> 2);
 #pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm) {
-            const int r = wm * C::WTM + fm * 16 + jj;
-            af[fm] = lds_ld16(sa, (r * 8 + a_chunk(r, kk * 4 + g)) * 16);
-        }
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) {
-            // lane (g, jj): rows k = 32kk + 8g + 4h + jj/4, columns (jj%4)*4..+3 of the fragment
-            const int col = wn * C::WTN + fn * 16 + (jj & 3) * 4;
-            const int c = col >> 3, half = (col & 7) * 2;
-            const int k_lo = kk * 32 + g * 8 + (jj >> 2);
-            const int k_hi = k_lo + 4;
-            const u32x2 lo = lds_read_tr(sb + (k_lo * C::CPR + b_chunk<C>(k_lo, c)) * 16 + half);
-            const u32x2 hi = lds_read_tr(sb + (k_hi * C::CPR + b_chunk<C>(k_hi, c)) * 16 + half);
-            bf[fn] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-        }
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) lds_wait(bf[fn]);
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn)
-                acc[fm][fn] = mfma16x16x32<DT>(af[fm], bf[fn], acc[fm][fn]);
+    for (int fn = 0; fn < C::FN; ++fn) {
+        const int col = wn * C::WTN + fn * 16 + (jj & 3) * 4;
+        const int c = col >> 3, half = (col & 7) * 2;
+        f.b[fn] = ring + C::A_BYTES + (k * C::CPR + b_chunk<C>(k, c)) * 16 + half;
     }
+    return f;
+}
+
+// Issue the LDS reads of half slab KK of stage S into f.
+template <class C, int S, int KK>
+__device__ __forceinline__ void frag_load(const FragBase<C>& fb, Frags<C>& f) {
+    constexpr uint32_t SO = S * C::STAGE;
+    constexpr uint32_t A_MAX = (C::FM - 1) * 16 * 128;
+    constexpr uint32_t B_MAX = (KK * 32 + 4) * C::CPR * 16;
+    // fold the stage offset into the immediate when it fits the 16-bit field
+    constexpr bool FOLD = SO + C::A_BYTES + B_MAX < 65536;
+    constexpr uint32_t SI = FOLD ? SO : 0;
+    const uint32_t sr = FOLD ? 0 : SO;
+    static_assert(A_MAX < 65536 && C::A_BYTES + B_MAX < 65536, "stage too large for ds offsets");
+    static_for<0, C::FM>([&](auto fm) {
+        f.a[fm] = ds_read_b128<SI + decltype(fm)::value * 16 * 128>(fb.a[KK] + sr);
+    });
+    static_for<0, C::FN>([&](auto fn) {
+        const u32x2 lo = ds_read_tr16_b64<SI + KK * 32 * C::CPR * 16>(fb.b[fn] + sr);
+        const u32x2 hi = ds_read_tr16_b64<SI + (KK * 32 + 4) * C::CPR * 16>(fb.b[fn] + sr);
+        f.b[fn] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    });
+}
+
+// Make the fragment registers available to the MFMAs (after lgkm_wait).
+template <class C>
+__device__ __forceinline__ void frag_pin(Frags<C>& f) {
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm) pin(f.a[fm]);
+#pragma unroll
+    for (int fn = 0; fn < C::FN; ++fn) pin(f.b[fn]);
+}
+
+template <class C, int DT>
+__device__ __forceinline__ void mfma_block(f32x4 (&acc)[C::FM][C::FN], const Frags<C>& f) {
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = mfma16x16x32<DT>(f.a[fm], f.b[fn], acc[fm][fn]);
 }
 
 // Wait until at most `n` DMA instructions of this wave are outstanding and
 // every LDS access of this wave has completed, then meet the other waves.
 // (A bare s_barrier: __syncthreads() would also wait for all DMA.)
 // The empty asm statements with a memory clobber and the scheduling
-// barriers keep the compiler from moving any memory access (in particular
-// LDS reads of the next stage) across the barrier.
+// barriers keep the compiler from moving any memory access across the
+// barrier.
 template <int N>
 __device__ __forceinline__ void ring_barrier() {
     static_assert(N >= 0 && N <= 63, "vmcnt");
@@ -484,20 +563,33 @@ __device__ __forceinline__ void lds_barrier() { ring_barrier<63>(); }
 template <class C, class Wait, int S>
 __device__ __forceinline__ void issue_slab(const TileJob& j, int ks, Wait& wait) {
     issue_b<C, S>(j, ks);
-    wait(ks);
+    if (ks < j.ks1) wait(ks);
     issue_a<C, S>(j, ks);
 }
 
-// One pipeline step: slab ks (in stage S) is computed while slabs ks+1 ..
-// ks+NS-1 are in flight.
+// One pipeline step over slab ks, which lives in stage S: once slab ks has
+// landed and every wave is done with the previous stage, refill that stage
+// with slab ks+NS-1, read both half slabs of stage S, and run the first
+// half's MFMAs while the second half's reads are still in flight.  The step
+// has no data-dependent branch between its MFMAs (the accumulators stay in
+// place): past the tile's last slab the DMA reads the zero page.
 template <class C, int DT, int S, class Wait>
-__device__ __forceinline__ void pipe_step(const TileJob& j, int ks, f32x4 (&acc)[C::FM][C::FN], Wait& wait) {
-    // slab ks has landed once only the slabs issued after it remain in flight
-    if (ks + C::NS - 2 < j.ks1) ring_barrier<C::LPS * (C::NS - 2)>();
-    else ring_barrier<0>();
-    constexpr int SN = (S + C::NS - 1) % C::NS;
-    if (ks + C::NS - 1 < j.ks1) issue_slab<C, Wait, SN>(j, ks + C::NS - 1, wait);
-    compute_stage<C, DT, S>(acc);
+__device__ __forceinline__ void pipe_step(const TileJob& j, int ks, const FragBase<C>& fb,
+                                          f32x4 (&acc)[C::FM][C::FN], Wait& wait) {
+    // slab ks has landed once only slabs ks+1 .. ks+NS-2 remain in flight
+    ring_barrier<C::LPS * (C::NS - 2)>();
+    issue_slab<C, Wait, (S + C::NS - 1) % C::NS>(j, ks + C::NS - 1, wait);
+    Frags<C> f0, f1;
+    frag_load<C, S, 0>(fb, f0);
+    frag_load<C, S, 1>(fb, f1);
+    lgkm_wait<C::NREAD>();
+    frag_pin(f0);
+    mfma_block<C, DT>(acc, f0);
+    __builtin_amdgcn_sched_barrier(0);
+    lgkm_wait<0>();
+    frag_pin(f1);
+    mfma_block<C, DT>(acc, f1);
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // The K loop of one tile.  `wait(ks)` is called (uniformly) before the
@@ -510,25 +602,28 @@ __device__ __forceinline__ void tile_mainloop(const TileJob& j, f32x4 (&acc)[C::
     for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int n = j.ks1 - j.ks0;
-    // prologue: slabs ks0 .. ks0+NS-2 into stages 0 .. NS-2
-    if (n > 0) issue_slab<C, Wait, 0>(j, j.ks0, wait);
-    if constexpr (C::NS > 2) if (n > 1) issue_slab<C, Wait, 1>(j, j.ks0 + 1, wait);
-    if constexpr (C::NS > 3) if (n > 2) issue_slab<C, Wait, 2>(j, j.ks0 + 2, wait);
-    // whole rounds of NS steps, then the remaining steps (no exits mid-round,
-    // so the accumulators stay in place across the loop)
-    int ks = j.ks0;
-    for (; ks + C::NS <= j.ks1; ks += C::NS) {
-        pipe_step<C, DT, 0>(j, ks, acc, wait);
-        pipe_step<C, DT, 1>(j, ks + 1, acc, wait);
-        if constexpr (C::NS > 2) pipe_step<C, DT, 2>(j, ks + 2, acc, wait);
-        if constexpr (C::NS > 3) pipe_step<C, DT, 3>(j, ks + 3, acc, wait);
+    if (j.ks1 > j.ks0) {
+        const FragBase<C> fb = frag_base<C>();
+        // prologue: slabs ks0 .. ks0+NS-2 into stages 0 .. NS-2
+        issue_slab<C, Wait, 0>(j, j.ks0, wait);
+        if constexpr (C::NS > 2) issue_slab<C, Wait, 1>(j, j.ks0 + 1, wait);
+        if constexpr (C::NS > 3) issue_slab<C, Wait, 2>(j, j.ks0 + 2, wait);
+        // whole rounds of NS steps, then the remaining steps (no exits
+        // mid-round, so the accumulators stay in place across the loop)
+        int ks = j.ks0;
+        for (; ks + C::NS <= j.ks1; ks += C::NS) {
+            pipe_step<C, DT, 0>(j, ks, fb, acc, wait);
+            pipe_step<C, DT, 1>(j, ks + 1, fb, acc, wait);
+            if constexpr (C::NS > 2) pipe_step<C, DT, 2>(j, ks + 2, fb, acc, wait);
+            if constexpr (C::NS > 3) pipe_step<C, DT, 3>(j, ks + 3, fb, acc, wait);
+        }
+        const int rem = j.ks1 - ks;
+        if (rem > 0) pipe_step<C, DT, 0>(j, ks, fb, acc, wait);
+        if constexpr (C::NS > 2) if (rem > 1) pipe_step<C, DT, 1>(j, ks + 1, fb, acc, wait);
+        if constexpr (C::NS > 3) if (rem > 2) pipe_step<C, DT, 2>(j, ks + 2, fb, acc, wait);
     }
-    const int rem = j.ks1 - ks;
-    if (rem > 0) pipe_step<C, DT, 0>(j, ks, acc, wait);
-    if constexpr (C::NS > 2) if (rem > 1) pipe_step<C, DT, 1>(j, ks + 1, acc, wait);
-    if constexpr (C::NS > 3) if (rem > 2) pipe_step<C, DT, 2>(j, ks + 2, acc, wait);
-    // every wave is done reading the ring before the epilogue reuses stage 0
+    // every wave is done reading the ring (and all DMA has landed) before
+    // the epilogue reuses stage 0
     ring_barrier<0>();
 }
 
@@ -540,7 +635,7 @@ __device__ __forceinline__ void tile_mainloop(const TileJob& j, f32x4 (&acc)[C::
 template <class C, int DT>
 __device__ __forceinline__ void tile_epilogue(const f32x4 (&acc)[C::FM][C::FN], int act, bool inter,
                                               uint16_t* D, int ldd, int rows, int cols, int m0, int n0) {
-    char* smem = lds_stage<C, 0>();
+    char* smem = lds_ring<C>();
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wm = wave / C::WN, wn = wave % C::WN;
