@@ -389,6 +389,48 @@ __device__ __forceinline__ void dma16(const uint16_t* src, char* lds) {
                                      (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
 }
 
+// Per-tile DMA state of one lane.  Interior slabs (every row, column and
+// K index of the slab inside the matrices) are fetched as a wave-uniform
+// base pointer (scalar registers, advanced per slab) plus the lane's 32-bit
+// byte offset of each chunk, computed once per tile -- the saddr form of
+// global_load_lds, with no per-slab address arithmetic.  Edge slabs (and
+// the slabs past a tile's ks1 that keep the pipeline count fixed) take the
+// per-lane path with the zero page.
+template <class C>
+struct TileDma {
+    const char* a_base;           // row m0 of A
+    const char* b_base;           // B
+    uint32_t va[C::A_PER_WAVE];   // A chunk offsets in slab 0 (bytes from a_base)
+    uint32_t vb[C::B_PER_WAVE];   // B chunk offsets in slab 0 (bytes from b_base)
+    bool a_full;                  // every row of the tile is below a_rows
+    bool b_full;                  // every output column of the tile is below b_cols
+};
+
+template <class C>
+__device__ __forceinline__ TileDma<C> tile_dma(const TileJob& j) {
+    TileDma<C> d;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    d.a_base = reinterpret_cast<const char*>(j.A + (size_t)j.m0 * j.lda);
+    d.b_base = reinterpret_cast<const char*>(j.B);
+#pragma unroll
+    for (int q = 0; q < C::A_PER_WAVE; ++q) {
+        const int L = (wave * C::A_PER_WAVE + q) * 64 + lane;
+        const int r = L >> 3, c = a_chunk(r, L & 7);
+        d.va[q] = (uint32_t)r * (uint32_t)j.lda * 2u + (uint32_t)c * 16u;
+    }
+#pragma unroll
+    for (int q = 0; q < C::B_PER_WAVE; ++q) {
+        const int L = (wave * C::B_PER_WAVE + q) * 64 + lane;
+        const int k = L / C::CPR, p = L % C::CPR;
+        bool ok;
+        const int gcol = b_column(j, b_chunk<C>(k, p), ok);
+        d.vb[q] = ((uint32_t)k * (uint32_t)j.ldb + (uint32_t)gcol) * 2u;
+    }
+    d.a_full = j.m0 + C::BM <= j.a_rows;
+    d.b_full = j.n0 + (j.inter ? C::BN / 2 : C::BN) <= j.b_cols;
+    return d;
+}
+
 // Issue the DMA of slab ks (B part and/or A part) into stage S.  Every wave
 // issues B_PER_WAVE B instructions and A_PER_WAVE A instructions; lane i of
 // an instruction fills LDS chunk L0 + i, and picks the global chunk that
@@ -396,11 +438,18 @@ __device__ __forceinline__ void dma16(const uint16_t* src, char* lds) {
 // tile's ks1 are issued too (all zero page), so that every wave always has
 // the same number of DMA instructions in flight.
 template <class C, int S>
-__device__ __forceinline__ void issue_b(const TileJob& j, int ks) {
+__device__ __forceinline__ void issue_b(const TileJob& j, const TileDma<C>& d, int ks) {
     char* st = lds_ring<C>() + S * C::STAGE + C::A_BYTES;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int k0 = ks * BK;
     const int kend = min(j.K, j.ks1 * BK);      // slabs at or past ks1 read the zero page
+    if (d.b_full && k0 + BK <= kend) {
+        const char* base = d.b_base + (size_t)k0 * j.ldb * 2;
+#pragma unroll
+        for (int q = 0; q < C::B_PER_WAVE; ++q)
+            dma16(reinterpret_cast<const uint16_t*>(base + d.vb[q]), st + (wave * C::B_PER_WAVE + q) * 1024);
+        return;
+    }
 #pragma unroll
     for (int q = 0; q < C::B_PER_WAVE; ++q) {
         const int L0 = (wave * C::B_PER_WAVE + q) * 64;
@@ -416,11 +465,18 @@ __device__ __forceinline__ void issue_b(const TileJob& j, int ks) {
 }
 
 template <class C, int S>
-__device__ __forceinline__ void issue_a(const TileJob& j, int ks) {
+__device__ __forceinline__ void issue_a(const TileJob& j, const TileDma<C>& d, int ks) {
     char* st = lds_ring<C>() + S * C::STAGE;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int k0 = ks * BK;
     const int kend = min(j.K, j.ks1 * BK);
+    if (d.a_full && k0 + BK <= kend) {
+        const char* base = d.a_base + (size_t)k0 * 2;
+#pragma unroll
+        for (int q = 0; q < C::A_PER_WAVE; ++q)
+            dma16(reinterpret_cast<const uint16_t*>(base + d.va[q]), st + (wave * C::A_PER_WAVE + q) * 1024);
+        return;
+    }
 #pragma unroll
     for (int q = 0; q < C::A_PER_WAVE; ++q) {
         const int L0 = (wave * C::A_PER_WAVE + q) * 64;
@@ -561,10 +617,10 @@ __device__ __forceinline__ void ring_barrier() {
 __device__ __forceinline__ void lds_barrier() { ring_barrier<63>(); }
 
 template <class C, class Wait, int S>
-__device__ __forceinline__ void issue_slab(const TileJob& j, int ks, Wait& wait) {
-    issue_b<C, S>(j, ks);
+__device__ __forceinline__ void issue_slab(const TileJob& j, const TileDma<C>& d, int ks, Wait& wait) {
+    issue_b<C, S>(j, d, ks);
     if (ks < j.ks1) wait(ks);
-    issue_a<C, S>(j, ks);
+    issue_a<C, S>(j, d, ks);
 }
 
 // One pipeline step over slab ks, which lives in stage S: once slab ks has
@@ -574,11 +630,11 @@ __device__ __forceinline__ void issue_slab(const TileJob& j, int ks, Wait& wait)
 // has no data-dependent branch between its MFMAs (the accumulators stay in
 // place): past the tile's last slab the DMA reads the zero page.
 template <class C, int DT, int S, class Wait>
-__device__ __forceinline__ void pipe_step(const TileJob& j, int ks, const FragBase<C>& fb,
+__device__ __forceinline__ void pipe_step(const TileJob& j, const TileDma<C>& d, int ks, const FragBase<C>& fb,
                                           f32x4 (&acc)[C::FM][C::FN], Wait& wait) {
     // slab ks has landed once only slabs ks+1 .. ks+NS-2 remain in flight
     ring_barrier<C::LPS * (C::NS - 2)>();
-    issue_slab<C, Wait, (S + C::NS - 1) % C::NS>(j, ks + C::NS - 1, wait);
+    issue_slab<C, Wait, (S + C::NS - 1) % C::NS>(j, d, ks + C::NS - 1, wait);
     Frags<C> f0, f1;
     frag_load<C, S, 0>(fb, f0);
     frag_load<C, S, 1>(fb, f1);
@@ -604,23 +660,24 @@ __device__ __forceinline__ void tile_mainloop(const TileJob& j, f32x4 (&acc)[C::
         for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (j.ks1 > j.ks0) {
         const FragBase<C> fb = frag_base<C>();
+        const TileDma<C> d = tile_dma<C>(j);
         // prologue: slabs ks0 .. ks0+NS-2 into stages 0 .. NS-2
-        issue_slab<C, Wait, 0>(j, j.ks0, wait);
-        if constexpr (C::NS > 2) issue_slab<C, Wait, 1>(j, j.ks0 + 1, wait);
-        if constexpr (C::NS > 3) issue_slab<C, Wait, 2>(j, j.ks0 + 2, wait);
+        issue_slab<C, Wait, 0>(j, d, j.ks0, wait);
+        if constexpr (C::NS > 2) issue_slab<C, Wait, 1>(j, d, j.ks0 + 1, wait);
+        if constexpr (C::NS > 3) issue_slab<C, Wait, 2>(j, d, j.ks0 + 2, wait);
         // whole rounds of NS steps, then the remaining steps (no exits
         // mid-round, so the accumulators stay in place across the loop)
         int ks = j.ks0;
         for (; ks + C::NS <= j.ks1; ks += C::NS) {
-            pipe_step<C, DT, 0>(j, ks, fb, acc, wait);
-            pipe_step<C, DT, 1>(j, ks + 1, fb, acc, wait);
-            if constexpr (C::NS > 2) pipe_step<C, DT, 2>(j, ks + 2, fb, acc, wait);
-            if constexpr (C::NS > 3) pipe_step<C, DT, 3>(j, ks + 3, fb, acc, wait);
+            pipe_step<C, DT, 0>(j, d, ks, fb, acc, wait);
+            pipe_step<C, DT, 1>(j, d, ks + 1, fb, acc, wait);
+            if constexpr (C::NS > 2) pipe_step<C, DT, 2>(j, d, ks + 2, fb, acc, wait);
+            if constexpr (C::NS > 3) pipe_step<C, DT, 3>(j, d, ks + 3, fb, acc, wait);
         }
         const int rem = j.ks1 - ks;
-        if (rem > 0) pipe_step<C, DT, 0>(j, ks, fb, acc, wait);
-        if constexpr (C::NS > 2) if (rem > 1) pipe_step<C, DT, 1>(j, ks + 1, fb, acc, wait);
-        if constexpr (C::NS > 3) if (rem > 2) pipe_step<C, DT, 2>(j, ks + 2, fb, acc, wait);
+        if (rem > 0) pipe_step<C, DT, 0>(j, d, ks, fb, acc, wait);
+        if constexpr (C::NS > 2) if (rem > 1) pipe_step<C, DT, 1>(j, d, ks + 1, fb, acc, wait);
+        if constexpr (C::NS > 3) if (rem > 2) pipe_step<C, DT, 2>(j, d, ks + 2, fb, acc, wait);
     }
     // every wave is done reading the ring (and all DMA has landed) before
     // the epilogue reuses stage 0

@@ -75,8 +75,9 @@ def test_no_packed_fp32_arithmetic(asm):
 
 
 @pytest.mark.skip(reason="buffer-descriptor DMA (buffer_load ... lds) is switched off: two GPU runs of it "
-                         "ended in memory faults whose cause is not yet shown; the operand DMA uses "
-                         "global_load_lds with a zero page")
+                         "ended in memory faults (cause, read from the compiled code: the descriptor base was "
+                         "built from readfirstlane's signed int result, which sign-extended into the address's "
+                         "upper word); the operand DMA uses global_load_lds with a zero page")
 def test_dma_only_through_range_checked_offsets(asm):
     """Operand tiles reach LDS only through buffer loads whose whole offset is
     in the per-lane VGPR (the part the hardware range check covers): scalar
