@@ -367,11 +367,13 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // Physical 16-byte chunk of logical chunk c in A row r (8 chunks per row).
-// A ds_read_b128 fragment read covers 16 consecutive rows (one chunk each);
-// the XOR term takes 16 distinct (row parity, chunk) pairs over any 16
-// aligned rows, so those 16 lanes hit 64 distinct banks.  It depends on
-// r mod 16 only, so fragments 16 rows apart are a fixed offset apart.
-__device__ __forceinline__ int a_chunk(int r, int c) { return c ^ ((r ^ ((r & 15) >> 3)) & 7); }
+// A ds_read_b128 fragment read covers 16 consecutive rows (one chunk
+// each).  XOR with r mod 8 reads free of LDS bank conflicts on gfx950
+// (measured with the SQ_LDS_BANK_CONFLICT counter on this exact access
+// pattern; variants that also mixed bit 3 of the row into the XOR
+// conflicted two-way).  It depends on r mod 8 only, so fragments 16 rows
+// apart are a fixed offset apart.
+__device__ __forceinline__ int a_chunk(int r, int c) { return c ^ (r & 7); }
 
 // Physical chunk of logical chunk c in B row k.  A transpose read covers,
 // per 32 lanes, rows 8g + (0..3) for g in {0,1} (or {2,3}) and two adjacent
