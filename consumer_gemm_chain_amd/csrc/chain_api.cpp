@@ -49,13 +49,23 @@ uint32_t cdiv(int64_t a, int64_t b) { return (uint32_t)((a + b - 1) / b); }
 
 // Planner: 16-row tiles while M fits one of them (weight streaming), 64 x
 // 128 tiles while M is a few hundred (each weight panel is read by as few
-// row blocks as possible), 128 x 128 tiles with two LDS stages (two
-// workgroups per CU) once the matrix cores bound the run.  Crossovers
-// measured on the GPT-3 shard (H=12288, I=6144) for M in 1..2048.
-int plan_config(int64_t M) {
+// row blocks as possible), then 128 x 128 tiles with two workgroups per CU,
+// or 256 x 128 tiles with one workgroup of eight waves per CU (about 5% more
+// matrix-core throughput per CU, but half as many tiles) once there are
+// enough of those tiles: for the stream-ordered pair when GEMM1 alone fills
+// a wave of them, for the fused policies when it fills three quarters of a
+// wave (the consumer tiles fill the rest -- the CuSync README's point about
+// the producer kernel's last wave).  Crossovers measured on the GPT-3,
+// LLaMA-65 and 8192^3 shards for M in 1..2048.
+constexpr int CFG_WIDE = 9;     // 256 x 128, eight waves, three stages
+
+int plan_config(int64_t M, int64_t I, int act, int policy, int cus) {
     if (M <= 16) return 0;
     if (M <= 256) return 1;
-    return 2;
+    const int64_t bn1 = act == MLP_ACT_SWIGLU ? 64 : 128;     // producer output columns of the wide config
+    const int64_t t1 = ((M + 255) / 256) * ((I + bn1 - 1) / bn1);
+    const int64_t need = policy == MLP_POLICY_STREAM_ORDERED ? cus : 3 * (int64_t)cus / 4;
+    return t1 >= need ? CFG_WIDE : 2;
 }
 
 }  // namespace
@@ -68,6 +78,7 @@ struct mlp_chain {
     int cfg;
     int forced_cfg;
     int forced_s1, forced_s2;   // 0 = planner's split
+    int forced_grid;            // 0 = planner's persistent grid
     CfgInfo ci;
     uint32_t Mt, N1t, N2t, T1, T2;
     uint32_t S1, S2, ksp1, ksp2;  // K split of GEMM1 / GEMM2 tiles
@@ -111,18 +122,30 @@ struct DeviceGuard {
     }
 };
 
-constexpr uint32_t MIN_SLABS_PER_PART = 8;   // 512 K-elements: keeps the partial traffic small
+constexpr uint32_t MIN_SLABS_PER_PART = 24;  // 1536 K-elements: keeps the partial traffic small
 
 // Deterministic split of each tile's K range when a GEMM has too few tiles
-// to give every CU weight-streaming work (small M): aim for about two parts
-// per CU, with at least MIN_SLABS_PER_PART slabs per part.  (The CuSync
-// README names CUTLASS StreamK as the other way to fill the last wave; this
-// is a fixed split with a fixed-order reduction, so results stay
-// bit-identical across policies.)
-uint32_t plan_split(uint32_t tiles, uint32_t nks, int cus) {
-    const uint32_t target = 2u * (uint32_t)cus;
-    if (tiles >= target / 2) return 1;
-    uint32_t s = (target + tiles - 1) / tiles;
+// to keep every CU busy.  (The CuSync README names CUTLASS StreamK as the
+// other way to fill the last wave; this is a fixed split with a fixed-order
+// reduction, so results stay bit-identical across policies.)  Targets,
+// measured on the GPT-3 shard (H=12288, I=6144) over M = 1..2048 and every
+// split up to 16:
+//   * weight streaming (M < 256): about 3/4 of a part per CU when a single
+//     row block reads each weight panel once, 3/2 parts per CU otherwise --
+//     more parts add partial-sum traffic without adding bandwidth;
+//   * otherwise: as many parts as fit one wave of two workgroups per CU
+//     (a second, partial wave costs more than the split saves).
+// Every part keeps at least MIN_SLABS_PER_PART slabs: on the LLaMA-65 shard
+// (K = 2752 for GEMM2) shorter parts lost more to the fp32 partial sums
+// than the split gained.
+uint32_t plan_split(uint32_t tiles, uint32_t nks, int cus, int64_t M, uint32_t Mt) {
+    uint32_t s;
+    if (M < 256) {
+        const uint32_t target = Mt == 1 ? 3u * (uint32_t)cus / 4u : 3u * (uint32_t)cus / 2u;
+        s = (target + tiles / 2) / tiles;
+    } else {
+        s = 2u * (uint32_t)cus / tiles;
+    }
     const uint32_t cap = nks / MIN_SLABS_PER_PART;
     if (s > cap) s = cap;
     if (s < 1) s = 1;
@@ -142,8 +165,8 @@ int apply_plan(mlp_chain* h, int cfg) {
     h->T1 = h->Mt * h->N1t;
     h->T2 = h->Mt * h->N2t;
     const uint32_t nks1 = cdiv(h->H, ci.BK), nks2 = cdiv(h->I, ci.BK);
-    h->S1 = h->forced_s1 > 0 ? (uint32_t)h->forced_s1 : plan_split(h->T1, nks1, h->cus);
-    h->S2 = h->forced_s2 > 0 ? (uint32_t)h->forced_s2 : plan_split(h->T2, nks2, h->cus);
+    h->S1 = h->forced_s1 > 0 ? (uint32_t)h->forced_s1 : plan_split(h->T1, nks1, h->cus, h->M, h->Mt);
+    h->S2 = h->forced_s2 > 0 ? (uint32_t)h->forced_s2 : plan_split(h->T2, nks2, h->cus, h->M, h->Mt);
     h->ksp1 = (nks1 + h->S1 - 1) / h->S1;
     h->ksp2 = (nks2 + h->S2 - 1) / h->S2;
     h->occ = 0;
@@ -154,9 +177,26 @@ int apply_plan(mlp_chain* h, int cfg) {
         if (e != hipSuccess) return fail(MLP_EHIP, "occupancy query failed: %s", hipGetErrorString(e));
         if (occ < 1) return fail(MLP_EHIP, "persistent kernel of config %d does not fit on a CU", cfg);
         h->occ = occ;
-        uint64_t g = (uint64_t)occ * (uint64_t)h->cus;
+        // Persistent workgroups: as many per CU as fit, but no more than the
+        // whole items per CU the run has.  When the run is under two items
+        // per CU (small M), one workgroup per CU runs a producer part and then
+        // a consumer part, so the consumers spread over the CUs the producers
+        // used instead of sharing the CUs their workgroups were placed on at
+        // launch.
         const uint64_t parts = (uint64_t)h->T1 * h->S1 + (uint64_t)h->T2 * h->S2;
+        uint64_t per_cu = parts / (uint64_t)h->cus;
+        if (per_cu < 1) per_cu = 1;
+        if (per_cu > (uint64_t)occ) per_cu = (uint64_t)occ;
+        uint64_t g = per_cu * (uint64_t)h->cus;
         if (g > parts) g = parts;
+        // at least one workgroup per tile queue (the kernel's deadlock-freedom
+        // argument needs an owner for every queue); extras exit at once
+        if (g < 8) g = 8;
+        if (h->forced_grid > 0) {
+            g = (uint64_t)h->forced_grid;
+            if (g > (uint64_t)occ * (uint64_t)h->cus) g = (uint64_t)occ * (uint64_t)h->cus;
+            if (g < 8) g = 8;
+        }
         h->grid = (uint32_t)g;
     }
     return MLP_OK;
@@ -190,7 +230,7 @@ int build_workspace(mlp_chain* h) {
     const size_t c2_b = align_up((size_t)h->T2 * 4, 256);
     const size_t p1_b = h->S1 > 1 ? align_up((size_t)h->T1 * h->S1 * acc_bytes, 256) : 0;
     const size_t p2_b = h->S2 > 1 ? align_up((size_t)h->T2 * h->S2 * acc_bytes, 256) : 0;
-    h->sync_bytes = f_b + r_b + c1_b + c2_b + 2048 + 2 * 256;
+    h->sync_bytes = f_b + r_b + c1_b + c2_b + 2304 + 2 * 256;
     h->ws_bytes = t_b + h->sync_bytes + p1_b + p2_b;
     hipError_t e = hipMalloc(&h->ws, h->ws_bytes);
     if (e != hipSuccess) {
@@ -208,10 +248,10 @@ int build_workspace(mlp_chain* h) {
     p += c1_b;
     h->cnt2 = reinterpret_cast<uint32_t*>(p);
     p += c2_b;
-    h->ticket = reinterpret_cast<uint32_t*>(p);            // 8 queue counters, 256 bytes apart
-    h->status = reinterpret_cast<uint32_t*>(p + 2048);
-    h->zero = reinterpret_cast<uint16_t*>(p + 2048 + 256);
-    p += 2048 + 2 * 256;
+    h->ticket = reinterpret_cast<uint32_t*>(p);            // 8 queue counters + exit counter, 256 B apart
+    h->status = reinterpret_cast<uint32_t*>(p + 2304);
+    h->zero = reinterpret_cast<uint16_t*>(p + 2304 + 256);
+    p += 2304 + 2 * 256;
     h->part1 = p1_b ? reinterpret_cast<float*>(p) : nullptr;
     p += p1_b;
     h->part2 = p2_b ? reinterpret_cast<float*>(p) : nullptr;
@@ -327,13 +367,14 @@ mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype
     h->cus = prop.multiProcessorCount;
     h->forced_cfg = -1;
     h->forced_s1 = 0;
+    h->forced_grid = 0;
     h->forced_s2 = 0;
     h->spin_limit = DEFAULT_SPIN_LIMIT;
     h->skip_producer = mlpc::NO_SKIP;
     h->trace = nullptr;
     h->last_stream = nullptr;
     h->ws = nullptr;
-    if (apply_plan(h, plan_config(M)) != MLP_OK || build_workspace(h) != MLP_OK) {
+    if (apply_plan(h, plan_config(M, I, act, policy, h->cus)) != MLP_OK || build_workspace(h) != MLP_OK) {
         if (h->ws) (void)hipFree(h->ws);
         delete h;
         return nullptr;
@@ -444,7 +485,7 @@ int mlp_chain_debug_skip_producer(mlp_chain_t h, int64_t tile) {
 
 static int replan(mlp_chain_t h) {
     DeviceGuard g(h->device);
-    const int cfg = h->forced_cfg < 0 ? plan_config(h->M) : h->forced_cfg;
+    const int cfg = h->forced_cfg < 0 ? plan_config(h->M, h->I, h->act, h->policy, h->cus) : h->forced_cfg;
     int rc = apply_plan(h, cfg);
     if (rc != MLP_OK) return rc;
     return build_workspace(h);
@@ -456,6 +497,13 @@ int mlp_chain_debug_set_config(mlp_chain_t h, int config_id) {
         return fail(MLP_EINVAL, "unknown tile configuration %d", config_id);
     h->forced_cfg = config_id;
     return replan(h);
+}
+
+int mlp_chain_debug_set_grid(mlp_chain_t h, int grid) {
+    if (!h) return fail(MLP_EINVAL, "NULL handle");
+    if (grid < 0) return fail(MLP_EINVAL, "grid must be >= 0, got %d", grid);
+    h->forced_grid = grid;
+    return apply_plan(h, h->cfg);
 }
 
 int mlp_chain_debug_set_split(mlp_chain_t h, int s1, int s2) {

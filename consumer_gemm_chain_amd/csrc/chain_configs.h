@@ -11,7 +11,9 @@
     X(4, 128, 256, 2, 2, 2, 1)   /* 64x128 per wave, one wave per SIMD */                     \
     X(5, 16, 128, 1, 2, 4, 1)    /* small M, 16x64 per wave */                                \
     X(6, 128, 256, 2, 4, 2, 2)   /* eight waves of 64x64 */                                   \
-    X(7, 256, 128, 4, 2, 2, 2)   /* eight waves of 64x64 */
+    X(7, 256, 128, 4, 2, 2, 2)   /* eight waves of 64x64 */                                   \
+    X(8, 128, 256, 2, 4, 3, 2)   /* eight waves of 64x64, three stages */                     \
+    X(9, 256, 128, 4, 2, 3, 2)   /* large M: eight waves of 64x64, three stages, one WG per CU */
 
 #define MLPC_COUNT_CFG(id, ...) +1
 constexpr int MLPC_NUM_CONFIGS = 0 MLPC_CONFIGS(MLPC_COUNT_CFG);

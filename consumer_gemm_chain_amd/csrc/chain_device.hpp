@@ -69,7 +69,8 @@ struct ChainArgs {
     uint32_t Mt, N1t, N2t, T1, T2;
     uint32_t group_m;       // row blocks per swizzle group
     uint32_t rx;            // XCD grid rows (1, 2, 4 or 8; the grid is rx x 8/rx)
-    uint32_t* ticket;       // 8 tile-queue counters, 64 words apart (one queue per XCD)
+    uint32_t* ticket;       // 8 tile-queue counters (one per XCD) and an exit counter, 64 words apart;
+                            // zero when a run starts (the last workgroup of a run resets them)
     uint32_t* flags;        // [Mt * N1t] ready epochs (tile_sync)
     uint32_t* rowcnt;       // [Mt] producer completions (row_sync)
     uint32_t* status;       // sticky watchdog status (nonzero = a consumer gave up)
@@ -276,18 +277,44 @@ __device__ __forceinline__ uint32_t wave_count_ready(const uint32_t* flags, uint
     return r < n ? r : n;
 }
 
+// Acquire side of a producer -> consumer hand-off inside one launch.  The
+// producer's release (agent scope) writes its data back to memory before it
+// publishes the flag or count.  The consumer then only needs its own loads
+// ordered after the flag load it observed, not an L2 invalidation: every
+// buffer handed off this way (the intermediate T, the split-K partials) is
+// written exactly once per launch, each 128-byte line of it by exactly one
+// workgroup, and read only after that workgroup's release; the kernel
+// dispatch invalidates the caches, so no line of such a buffer from an
+// earlier launch can be cached, and no line of it is read before it is
+// written.  An agent-scope acquire fence (buffer_inv sc1) would also drop
+// every other line of the XCD's L2 -- the weight panels and activation rows
+// the co-running tiles share -- once per hand-off.
+__device__ __forceinline__ void handoff_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup"); }
+
+// Poll back-off: sleep `units` x 64 clocks, then double the interval up to
+// POLL_MAX_UNITS (about 1 us).  Every consumer of a row block polls the
+// same few flag lines with loads that bypass the L2; at a fixed short
+// interval hundreds of waiting consumers concentrate enough traffic on
+// those lines' memory channel to slow the producers they are waiting for.
+constexpr uint32_t POLL_MAX_UNITS = 32;
+
+__device__ __forceinline__ void poll_backoff(uint32_t& units) {
+    for (uint32_t i = 0; i < units; ++i) __builtin_amdgcn_s_sleep(1);
+    if (units < POLL_MAX_UNITS) units <<= 1;
+}
+
 // Called by ONE whole wave: flags [0, from) are already acquired; wait
-// until flags from..need are all ready (polling from `from`, s_sleep
-// back-off), then take an agent-scope acquire fence so that the workgroup's
-// later loads see the producers' data.  Returns the first flag index not
-// known ready (> need), or n if the wait gave up (status records it).
+// until flags from..need are all ready (polling from `from`, with
+// back-off), then acquire (handoff_acquire) so that the workgroup's later
+// loads see the producers' data.  Returns the first flag index not known
+// ready (> need), or n if the wait gave up (status records it).
 __device__ __forceinline__ uint32_t wave_acquire_flags(const uint32_t* flags, uint32_t from, uint32_t need,
                                                        uint32_t n, uint32_t epoch, uint32_t* status,
                                                        uint32_t limit) {
     uint32_t r = wave_count_ready(flags, from, n, epoch);
-    uint32_t polls = 0;
+    uint32_t polls = 0, units = 1;
     while (r <= need) {
-        __builtin_amdgcn_s_sleep(2);
+        poll_backoff(units);
         r = wave_count_ready(flags, r, n, epoch);
         if (r <= need && (++polls >= limit || atomic_load_relaxed(status) != 0)) {
             if ((threadIdx.x & 63) == 0)
@@ -296,7 +323,7 @@ __device__ __forceinline__ uint32_t wave_acquire_flags(const uint32_t* flags, ui
             break;
         }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    handoff_acquire();
     return r;
 }
 
@@ -305,9 +332,9 @@ __device__ __forceinline__ uint32_t wave_acquire_flags(const uint32_t* flags, ui
 __device__ __forceinline__ bool wave_acquire_count(const uint32_t* cnt, uint32_t target, uint32_t* status,
                                                    uint32_t limit) {
     bool ok = true;
-    uint32_t polls = 0;
+    uint32_t polls = 0, units = 1;
     while ((int32_t)(atomic_load_relaxed(cnt) - target) < 0) {
-        __builtin_amdgcn_s_sleep(2);
+        poll_backoff(units);
         if (++polls >= limit || atomic_load_relaxed(status) != 0) {
             if ((threadIdx.x & 63) == 0)
                 __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -315,7 +342,7 @@ __device__ __forceinline__ bool wave_acquire_count(const uint32_t* cnt, uint32_t
             break;
         }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    handoff_acquire();
     return ok;
 }
 
@@ -802,8 +829,10 @@ __device__ __forceinline__ bool split_reduce(f32x4 (&acc)[C::FM][C::FN], float* 
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
     if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(cnt + tile, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const uint32_t old = __hip_atomic_fetch_add(cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         *s_flag = (old + 1u == target) ? 1u : 0u;
+        handoff_acquire();
     }
     __syncthreads();
     if (__builtin_amdgcn_readfirstlane(*s_flag) == 0) return false;
@@ -821,24 +850,27 @@ __device__ __forceinline__ bool split_reduce(f32x4 (&acc)[C::FM][C::FN], float* 
     return true;
 }
 
-// One tile part of either GEMM.  `role` 1 = producer (X W1 -> act -> T),
-// 2 = consumer (T W2 -> Y); `wait` is only exercised by consumers.  Returns
-// true if this part wrote the tile's output (always, unless the tile is
-// split and another part arrives last).
-template <class C, int DT, class Wait>
-__device__ __forceinline__ bool run_tile(const ChainArgs& a, int role, uint32_t mb, uint32_t nb, uint32_t s,
-                                         uint32_t* s_flag, Wait& wait) {
+// One tile part of either GEMM.  ROLE 1 = producer (X W1 -> act -> T),
+// 2 = consumer (T W2 -> Y); `wait` is only exercised by consumers.  The role
+// is a template parameter so that each role gets its own main loop compiled
+// for it (the persistent kernel holds both): with one loop shared at run
+// time, the tiles ran 2-20% slower than the same tiles in the stand-alone
+// kernels.  Returns true if this part wrote the tile's output (always,
+// unless the tile is split and another part arrives last).
+template <class C, int DT, int ROLE, class Wait>
+__device__ __forceinline__ bool run_tile(const ChainArgs& a, uint32_t mb, uint32_t nb, uint32_t s, uint32_t* s_flag,
+                                         Wait& wait) {
     f32x4 acc[C::FM][C::FN];
-    const uint32_t tile = mb * (role == 1 ? a.N1t : a.N2t) + nb;
-    const TileJob j = role == 1 ? producer_job<C>(a, mb, nb, s) : consumer_job<C>(a, mb, nb, s);
+    const uint32_t tile = mb * (ROLE == 1 ? a.N1t : a.N2t) + nb;
+    const TileJob j = ROLE == 1 ? producer_job<C>(a, mb, nb, s) : consumer_job<C>(a, mb, nb, s);
     tile_mainloop<C, DT>(j, acc, wait);
-    const uint32_t S = role == 1 ? a.S1 : a.S2;
+    const uint32_t S = ROLE == 1 ? a.S1 : a.S2;
     if (S > 1) {
-        const bool last = role == 1 ? split_reduce<C>(acc, a.part1, a.cnt1, tile, s, S, a.gen1 * S, s_flag)
+        const bool last = ROLE == 1 ? split_reduce<C>(acc, a.part1, a.cnt1, tile, s, S, a.gen1 * S, s_flag)
                                     : split_reduce<C>(acc, a.part2, a.cnt2, tile, s, S, a.gen2 * S, s_flag);
         if (!last) return false;
     }
-    if (role == 1)
+    if constexpr (ROLE == 1)
         tile_epilogue<C, DT>(acc, a.act, j.inter, a.t, a.I, a.M, a.I, j.m0, j.n0);
     else
         tile_epilogue<C, DT>(acc, ACT_NONE, false, a.y, a.H, a.M, a.H, j.m0, j.n0);

@@ -28,7 +28,20 @@
 
 namespace mlpc {
 
-// One workgroup per tile part: blockIdx = tile * S + part.
+// Timeline record of item t (thread 0): start, end of its last wait, end
+// (100 MHz realtime clock), and where it ran.
+__device__ __forceinline__ void trace_item(const ChainArgs& a, uint32_t t, uint64_t t_start, uint64_t t_waited,
+                                           bool wrote) {
+    uint32_t hw = 0, xcc = 0;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    uint64_t* r = a.trace + 4 * (size_t)t;
+    r[0] = t_start;
+    r[1] = t_waited;
+    r[2] = __builtin_amdgcn_s_memrealtime();
+    r[3] = (uint64_t)t | ((uint64_t)(xcc & 0xf) << 32) | ((uint64_t)hw << 36) | ((uint64_t)wrote << 63);
+}
+
 // One workgroup per tile part.  Workgroups are dispatched to the XCDs
 // round-robin, so block b runs on XCD b % 8: give each XCD a contiguous
 // chunk of the concatenated XCD blocks.
@@ -38,7 +51,9 @@ __global__ __launch_bounds__(C::NT) void gemm1_act_kernel(ChainArgs a) {
     NoWait w;
     uint32_t mb, nb, part;
     xcd_position(a.Mt, a.N1t, a.S1, a.rx, xcd_chunked(blockIdx.x, a.T1 * a.S1), mb, nb, part);
-    run_tile<C, DT>(a, 1, mb, nb, part, &s_flag, w);
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    const bool wrote = run_tile<C, DT, 1>(a, mb, nb, part, &s_flag, w);
+    if (a.trace && threadIdx.x == 0) trace_item(a, (mb * a.N1t + nb) * a.S1 + part, t0, t0, wrote);
 }
 
 template <class C, int DT>
@@ -47,7 +62,10 @@ __global__ __launch_bounds__(C::NT) void gemm2_kernel(ChainArgs a) {
     NoWait w;
     uint32_t mb, nb, part;
     xcd_position(a.Mt, a.N2t, a.S2, a.rx, xcd_chunked(blockIdx.x, a.T2 * a.S2), mb, nb, part);
-    run_tile<C, DT>(a, 2, mb, nb, part, &s_flag, w);
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    const bool wrote = run_tile<C, DT, 2>(a, mb, nb, part, &s_flag, w);
+    if (a.trace && threadIdx.x == 0)
+        trace_item(a, a.T1 * a.S1 + (mb * a.N2t + nb) * a.S2 + part, t0, t0, wrote);
 }
 
 // Consumer-side wait of the persistent kernel.  One functor type serves
@@ -101,20 +119,79 @@ struct ChainWait {
     }
 };
 
-// The tile queue.  Queue x (one counter per XCD) holds the GEMM1 tile
-// parts of XCD x's block of the GEMM1 grid, then the GEMM2 tile parts of its
-// block of the GEMM2 grid (same row split), each walked row-major.  A
-// workgroup owns queue blockIdx % 8 -- the XCD it is dispatched to -- and
-// when its queue runs dry it takes from the next queues in order.  Every
-// workgroup fails exactly once on each queue per run, so each queue's counter
-// advances by its length plus the grid per run and needs no reset.  Items
-// are numbered for flags, trace and test hooks as GEMM1 parts
-// (mb * N1t + nb) * S1 + part, then GEMM2 parts P1 + (mb * N2t + nb) * S2 + part.
-// Deadlock freedom: a queue hands out consumers only after all its producers
-// are drawn; a consumer waits only for producers; a queue with an undrawn
-// producer has handed out no consumer, so its owner workgroups (at least one
-// per queue: grid >= 8) are running producers or about to draw one, and
-// producers never wait.
+// The tile queues.  Queue x (one per XCD) holds the GEMM1 tile parts of XCD
+// x's block of the GEMM1 grid, then the GEMM2 tile parts of its block of the
+// GEMM2 grid (same row split), each walked row-major.  Workgroup b belongs to
+// queue b % 8 -- the XCD it is dispatched to -- and starts with item b / 8
+// of it, with no atomic (queue x's first items, one per owner, are handed
+// out at launch).  Further items are drawn by wave 0: one round of relaxed
+// loads reads the counters of all queues not yet seen dry, and an atomic
+// draws from the first of them, in the order own queue, then the next ones
+// -- so a workgroup takes its own queue's remaining items before stealing.
+// The last workgroup to find every queue dry resets the counters, so every
+// run starts from zero with no clearing launch.  Items are numbered for
+// flags, trace and test hooks as GEMM1 parts (mb * N1t + nb) * S1 + part,
+// then GEMM2 parts P1 + (mb * N2t + nb) * S2 + part.
+// Deadlock freedom: a queue hands out its items in order, producers first,
+// so a consumer is handed out only after every producer of its queue has
+// been; a consumer waits only for producers; every queue has an owner (grid
+// >= 8), and an owner takes its own queue's items before any other's, so a
+// producer not yet handed out will be, by an owner that is running a
+// producer or about to draw one -- producers never wait.
+struct Queues {
+    uint32_t own;
+    uint32_t dry;          // bit v: queue (own + v) & 7 is known to be empty (wave-uniform)
+    uint32_t P1;
+};
+
+__device__ __forceinline__ uint32_t queue_item(const ChainArgs& a, const XcdBlock& bp, const XcdBlock& bc,
+                                               uint32_t P1, uint32_t c) {
+    uint32_t mb, nb, part;
+    if (c < bp.len) {
+        xcd_item(bp, a.S1, c, mb, nb, part);
+        return (mb * a.N1t + nb) * a.S1 + part;
+    }
+    xcd_item(bc, a.S2, c - bp.len, mb, nb, part);
+    return P1 + (mb * a.N2t + nb) * a.S2 + part;
+}
+
+// Owners of queue x: workgroups b < grid with b % 8 == x.
+__device__ __forceinline__ uint32_t queue_owners(uint32_t grid, uint32_t x) {
+    return grid > x ? (grid - x + 7) / 8 : 0;
+}
+
+// Wave 0 only: the next item for this workgroup, or NO_ITEM.
+constexpr uint32_t NO_ITEM = 0xffffffffu;
+__device__ __forceinline__ uint32_t draw_item(const ChainArgs& a, Queues& q) {
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t x = (q.own + lane) & 7;
+    XcdBlock bp{0, 0, 1, 0}, bc{0, 0, 1, 0};
+    uint32_t len = 0, first = 0;
+    if (lane < 8) {
+        bp = xcd_block(a.Mt, a.N1t, a.S1, a.rx, x);
+        bc = xcd_block(a.Mt, a.N2t, a.S2, a.rx, x);
+        len = bp.len + bc.len;
+        first = min(len, queue_owners(a.grid, x));   // items handed out at launch
+    }
+    for (;;) {
+        bool avail = false;
+        if (lane < 8 && !((q.dry >> lane) & 1u))
+            avail = atomic_load_relaxed(a.ticket + 64 * x) + first < len;
+        const uint64_t m = __ballot(avail);
+        if (m == 0) return NO_ITEM;
+        const uint32_t k = (uint32_t)__builtin_ctzll(m);
+        uint32_t item = NO_ITEM;
+        if (lane == k) {
+            const uint32_t c = __hip_atomic_fetch_add(a.ticket + 64 * x, 1u, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT) + first;
+            if (c < len) item = queue_item(a, bp, bc, q.P1, c);
+        }
+        item = __builtin_amdgcn_readlane(item, k);
+        if (item != NO_ITEM) return item;
+        q.dry |= 1u << k;
+    }
+}
+
 template <class C, int DT, int POL>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
 void chain_persistent_kernel(ChainArgs a) {
@@ -123,43 +200,33 @@ void chain_persistent_kernel(ChainArgs a) {
     __shared__ uint32_t s_flag;
     const uint32_t P1 = a.T1 * a.S1;
     const int bn1 = a.act == ACT_SWIGLU ? C::BN / 2 : C::BN;
-    const uint32_t own = blockIdx.x & 7;
-    uint32_t visit = 0;              // queues visited so far (own queue first)
+    Queues q{blockIdx.x & 7u, 0u, P1};
+    uint32_t item = NO_ITEM;
+    {
+        // the launch-time item: position blockIdx / 8 of the own queue
+        const XcdBlock bp = xcd_block(a.Mt, a.N1t, a.S1, a.rx, q.own);
+        const XcdBlock bc = xcd_block(a.Mt, a.N2t, a.S2, a.rx, q.own);
+        const uint32_t pos = blockIdx.x >> 3;
+        if (pos < bp.len + bc.len) item = queue_item(a, bp, bc, P1, pos);
+    }
     for (;;) {
-        // draw the next item (thread 0), from the current queue or the next ones
-        if (threadIdx.x == 0) {
-            uint32_t item = 0xffffffffu;
-            while (visit < 8) {
-                const uint32_t x = (own + visit) & 7;
-                const XcdBlock bp = xcd_block(a.Mt, a.N1t, a.S1, a.rx, x);
-                const XcdBlock bc = xcd_block(a.Mt, a.N2t, a.S2, a.rx, x);
-                const uint32_t len = bp.len + bc.len;
-                const uint32_t base = (a.epoch - 1u) * (len + a.grid);
-                const uint32_t c = __hip_atomic_fetch_add(a.ticket + 64 * x, 1u, __ATOMIC_RELAXED,
-                                                          __HIP_MEMORY_SCOPE_AGENT) - base;
-                if (c < len) {
-                    uint32_t mb, nb, part;
-                    if (c < bp.len) {
-                        xcd_item(bp, a.S1, c, mb, nb, part);
-                        item = (mb * a.N1t + nb) * a.S1 + part;
-                    } else {
-                        xcd_item(bc, a.S2, c - bp.len, mb, nb, part);
-                        item = P1 + (mb * a.N2t + nb) * a.S2 + part;
-                    }
-                    break;
-                }
-                ++visit;                 // this queue is dry: never come back
+        if (item == NO_ITEM) {
+            // draw the next item (wave 0), from the own queue or the next ones
+            if ((threadIdx.x >> 6) == 0) {
+                const uint32_t it = draw_item(a, q);
+                if (threadIdx.x == 0) s_ticket = it;
             }
-            s_ticket = item;
+            __syncthreads();
+            // The item is the same for every thread of the workgroup; reading
+            // it through readfirstlane makes that visible to the compiler, so
+            // every branch on it (and the loop exit) is a scalar branch and
+            // all lanes of a wave stay on one path through the barriers below.
+            item = __builtin_amdgcn_readfirstlane(s_ticket);
+            __syncthreads();
+            if (item == NO_ITEM) break;
         }
-        __syncthreads();
-        // The item is the same for every thread of the workgroup; reading it
-        // through readfirstlane makes that visible to the compiler, so every
-        // branch on it (and the loop exit) is a scalar branch and all lanes of
-        // a wave stay on one path through the barriers below.
-        const uint32_t t = __builtin_amdgcn_readfirstlane(s_ticket);
-        __syncthreads();
-        if (t == 0xffffffffu) break;
+        const uint32_t t = item;
+        item = NO_ITEM;
         const bool prod = t < P1;
         // test hook: a skipped producer part does no work and no release
         if (!(prod && t == a.skip_producer)) {
@@ -174,18 +241,14 @@ void chain_persistent_kernel(ChainArgs a) {
             ChainWait<POL> w{!prod, a.flags + mb * a.N1t, a.rowcnt + mb, a.N1t,
                              POL == POL_ROW ? a.epoch * a.N1t : a.epoch, bn1, a.status, a.spin_limit,
                              &s_ready, first, false, t_start};
-            const bool wrote = run_tile<C, DT>(a, prod ? 1 : 2, mb, nb, part, &s_flag, w);
-            if (a.trace && threadIdx.x == 0) {
-                // timeline: start, last wait done, end (100 MHz realtime clock), and where it ran
-                uint32_t hw = 0, xcc = 0;
-                asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
-                asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-                uint64_t* r = a.trace + 4 * (size_t)t;
-                r[0] = t_start;
-                r[1] = w.t_waited;
-                r[2] = __builtin_amdgcn_s_memrealtime();
-                r[3] = (uint64_t)t | ((uint64_t)(xcc & 0xf) << 32) | ((uint64_t)hw << 36) | ((uint64_t)wrote << 63);
+            bool wrote;
+            if (prod) {
+                NoWait nw;
+                wrote = run_tile<C, DT, 1>(a, mb, nb, part, &s_flag, nw);
+            } else {
+                wrote = run_tile<C, DT, 2>(a, mb, nb, part, &s_flag, w);
             }
+            if (a.trace && threadIdx.x == 0) trace_item(a, t, t_start, w.t_waited, wrote);
             if (prod && wrote) {
                 // every thread's T stores happen before thread 0's agent-scope
                 // release (workgroup release + barrier), which publishes the tile
@@ -206,6 +269,16 @@ void chain_persistent_kernel(ChainArgs a) {
         // the other threads re-read the old ticket at the barriers while
         // thread 0 waits to draw the next one, which never ends.
         __syncthreads();
+    }
+    // every queue is dry for this workgroup; the last one to get here resets
+    // the counters for the next run (no workgroup draws after its exit count)
+    if (threadIdx.x == 0) {
+        uint32_t* exits = a.ticket + 64 * 8;
+        if (__hip_atomic_fetch_add(exits, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.grid - 1) {
+            for (int x = 0; x < 8; ++x)
+                __hip_atomic_store(a.ticket + 64 * x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(exits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
     }
 }
 

@@ -27,7 +27,7 @@ POLICIES = {"stream_ordered": MLP_POLICY_STREAM_ORDERED, "row_sync": MLP_POLICY_
 EXPORTS = ("mlp_chain_create", "mlp_chain_run", "mlp_chain_destroy", "mlp_chain_run_phase",
            "mlp_chain_status", "mlp_chain_last_error", "mlp_chain_info",
            "mlp_chain_debug_set_spin_limit", "mlp_chain_debug_skip_producer",
-           "mlp_chain_debug_set_config", "mlp_chain_debug_set_split",
+           "mlp_chain_debug_set_config", "mlp_chain_debug_set_split", "mlp_chain_debug_set_grid",
            "mlp_chain_debug_set_trace", "mlp_chain_debug_read_intermediate")
 
 INFO_FIELDS = ("BM", "BN1", "BN2", "BK", "Mt", "N1t", "N2t", "T1", "T2", "grid", "wg_per_cu",
@@ -75,6 +75,8 @@ def load_library(path: str | None = None):
     lib.mlp_chain_debug_set_config.restype = ci
     lib.mlp_chain_debug_set_split.argtypes = [vp, ci, ci]
     lib.mlp_chain_debug_set_split.restype = ci
+    lib.mlp_chain_debug_set_grid.argtypes = [vp, ci]
+    lib.mlp_chain_debug_set_grid.restype = ci
     lib.mlp_chain_debug_set_trace.argtypes = [vp, vp]
     lib.mlp_chain_debug_set_trace.restype = ci
     lib.mlp_chain_debug_read_intermediate.argtypes = [vp, vp, vp]
@@ -145,6 +147,10 @@ def mlp_chain_debug_set_config(h: int, config_id: int) -> int:
 
 def mlp_chain_debug_set_split(h: int, s1: int, s2: int) -> int:
     return _check(load_library().mlp_chain_debug_set_split(h, int(s1), int(s2)))
+
+
+def mlp_chain_debug_set_grid(h: int, grid: int) -> int:
+    return _check(load_library().mlp_chain_debug_set_grid(h, int(grid)))
 
 
 def mlp_chain_debug_set_trace(h: int, buffer: int | None) -> int:
@@ -226,6 +232,9 @@ class MlpChain:
 
     def set_split(self, s1: int, s2: int):
         mlp_chain_debug_set_split(self.h, s1, s2)
+
+    def set_grid(self, grid: int):
+        mlp_chain_debug_set_grid(self.h, grid)
 
     def set_spin_limit(self, limit: int):
         mlp_chain_debug_set_spin_limit(self.h, limit)

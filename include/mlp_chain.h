@@ -154,12 +154,23 @@ int mlp_chain_debug_set_config(mlp_chain_t h, int config_id);
  * NULL handle or a split outside 0..64. */
 int mlp_chain_debug_set_split(mlp_chain_t h, int s1, int s2);
 
-/* Timeline trace of the fused policies (measurement of the non-overlapped
- * share, as the FLUX summary card advises in Interesting ideas, I3):
+/* Force the number of persistent workgroups of the fused policies, 0 = the
+ * planner's (as many per CU as fit, but no more than the run's whole items
+ * per CU).  Values are clamped to [8, workgroups per CU x CUs]: at least one
+ * workgroup per tile queue, and never more than can be resident at once
+ * (the persistent kernel needs all its workgroups resident).  For
+ * measurements of the schedule (the CuSync README's point about the last
+ * wave of the producer kernel); takes effect on the next run.  Returns
+ * MLP_EINVAL for a NULL handle or a negative value. */
+int mlp_chain_debug_set_grid(mlp_chain_t h, int grid);
+
+/* Timeline trace of every policy (measurement of the non-overlapped share,
+ * as the FLUX summary card advises in Interesting ideas, I3):
  * `buffer` is a DEVICE buffer of 4 * (T1*S1 + T2*S2) uint64 (see
  * mlp_chain_info), NULL turns tracing off.  Each run then writes, per ticket
  * t (producer parts first), words 4t..4t+3 = { start, end of the part's
- * last wait, end } on the 100 MHz realtime clock, and { t | XCD << 32 |
+ * last wait (= start where nothing waits), end } on the 100 MHz realtime
+ * clock, and { t | XCD << 32 |
  * HW_ID << 36 | (part wrote the tile's output) << 63 }.  The buffer stays
  * owned by the caller and must outlive the runs that use it.  Returns
  * MLP_EINVAL for a NULL handle. */

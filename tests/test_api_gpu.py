@@ -99,10 +99,12 @@ def test_info_reports_plan():
         assert info["T1"] == info["Mt"] * info["N1t"] and info["T2"] == info["Mt"] * info["N2t"]
         assert info["grid"] <= info["wg_per_cu"] * info["cus"]
         assert info["S1"] == 1 and info["S2"] == 1          # enough tiles: no split
-    with mc.MlpChain(1, 12288, 6144, "gelu_tanh", "f16", "tile_sync") as ch:
+    with mc.MlpChain(1, 8192, 4096, "gelu_tanh", "f16", "tile_sync") as ch:
         info = ch.info()
         assert info["S1"] > 1 and info["S2"] > 1            # weight streaming: split K
-        assert info["ksp1"] * info["S1"] >= 12288 // 64 and info["ksp2"] * info["S2"] >= 6144 // 64
+        assert info["ksp1"] * info["S1"] >= 8192 // 64 and info["ksp2"] * info["S2"] >= 4096 // 64
+        assert (info["S1"] - 1) * info["ksp1"] < 8192 // 64  # no empty part
+        assert info["ksp1"] >= 24 and info["ksp2"] >= 24
 
 
 @pytest.mark.parametrize("policy", ["row_sync", "tile_sync"])

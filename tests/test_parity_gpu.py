@@ -25,7 +25,7 @@ def _case(M, H, I, act, dtype, seed):
 
 @pytest.mark.parametrize("act", ACTS)
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("cfg", [0, 1, 2])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 9])
 def test_small_all_policies_match_oracle(oracle_mod, act, dtype, cfg):
     # several tiles in M, N1, N2 and K for every config, ragged everywhere
     M, H, I = 200, 328, 456
@@ -67,7 +67,7 @@ def test_tiny_workload(oracle_mod):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("cfg", [0, 1, 2])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 9])
 def test_exact_integer_pin_on_gpu(oracle_mod, dtype, cfg):
     """Integer inputs whose partial sums are exact in fp32 in any order (also
     inside the matrix cores): every policy, the oracle and exact int64
@@ -125,7 +125,7 @@ def test_linear_in_w2_on_gpu():
         assert np.array_equal(y4[normal], 4 * y1[normal])
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 9])
 def test_repeated_runs_alternating_inputs(cfg):
     """Race check: 40 back-to-back runs of each fused policy on one handle,
     alternating between two inputs, must each equal the stream-ordered output
@@ -240,12 +240,13 @@ def test_split_k_matches_oracle_and_policies(oracle_mod, s1, s2, act, dtype, cfg
 
 
 def test_planned_split_at_small_m_alternating_inputs():
-    """At M=16 on a GPT-3-like width the planner splits K; 20 fused runs per
-    policy alternating two inputs equal the stream-ordered outputs exactly."""
+    """At M=16 on a wide layer the planner splits K in both GEMMs; 20 fused
+    runs per policy alternating two inputs equal the stream-ordered outputs
+    exactly."""
     import torch
     from consumer_gemm_chain_amd.mlp_chain import MlpChain
     from tests._helpers import empty_dev, from_dev
-    M, H, I, act, dtype = 16, 4096, 2048, "gelu_tanh", "f16"
+    M, H, I, act, dtype = 16, 8192, 4096, "gelu_tanh", "f16"
     xa, w1, w2 = _case(M, H, I, act, dtype, seed=21)
     xb = gen.normal_bits((M, H), 77, 1.0, dtype)
     dw1, dw2 = to_dev(w1, dtype), to_dev(w2, dtype)
