@@ -165,8 +165,19 @@ int apply_plan(mlp_chain* h, int cfg) {
     h->T1 = h->Mt * h->N1t;
     h->T2 = h->Mt * h->N2t;
     const uint32_t nks1 = cdiv(h->H, ci.BK), nks2 = cdiv(h->I, ci.BK);
-    h->S1 = h->forced_s1 > 0 ? (uint32_t)h->forced_s1 : plan_split(h->T1, nks1, h->cus, h->M, h->Mt);
-    h->S2 = h->forced_s2 > 0 ? (uint32_t)h->forced_s2 : plan_split(h->T2, nks2, h->cus, h->M, h->Mt);
+    // The split is planned on the tiling of the stream-ordered plan for M
+    // (not of `cfg`), so every policy splits K alike.  The tile shape does
+    // not change any output element's arithmetic (same MFMA sequence over
+    // the same slabs), the split does: equal splits keep the policies
+    // bit-identical while each uses its own tile configuration.
+    {
+        const CfgInfo cs = mlpc_config_info(plan_config(h->M, h->I, h->act, MLP_POLICY_STREAM_ORDERED, h->cus));
+        const uint32_t mt = cdiv(h->M, cs.BM);
+        const uint32_t t1 = mt * cdiv(h->I, h->act == MLP_ACT_SWIGLU ? cs.BN / 2 : cs.BN);
+        const uint32_t t2 = mt * cdiv(h->H, cs.BN);
+        h->S1 = h->forced_s1 > 0 ? (uint32_t)h->forced_s1 : plan_split(t1, nks1, h->cus, h->M, mt);
+        h->S2 = h->forced_s2 > 0 ? (uint32_t)h->forced_s2 : plan_split(t2, nks2, h->cus, h->M, mt);
+    }
     h->ksp1 = (nks1 + h->S1 - 1) / h->S1;
     h->ksp2 = (nks2 + h->S2 - 1) / h->S2;
     h->occ = 0;

@@ -164,8 +164,8 @@ def _sample_rows(M, k=6, seed=0):
     return sorted(rows)
 
 
-FULL = [(1, 1), (1, 64), (1, 512), (1, 2048),
-        (2, 1), (2, 256), (2, 2048),
+FULL = [(1, 1), (1, 64), (1, 512), (1, 1024), (1, 2048),
+        (2, 1), (2, 256), (2, 1024), (2, 2048),
         (3, 128), (3, 2048), (3, 8192),
         (4, 8192)]
 
@@ -263,3 +263,33 @@ def test_planned_split_at_small_m_alternating_inputs():
                 torch.cuda.synchronize()
                 assert np.array_equal(from_dev(out), refs[i % 2]), f"{pol} run {i}"
             assert ch.status() == 0
+
+
+@pytest.mark.parametrize("act,dtype", [("gelu_tanh", "f16"), ("swiglu", "bf16")])
+def test_tile_configs_agree_bitwise(act, dtype):
+    """The tile shape does not change any output element's arithmetic: with
+    the same K split, every tile configuration and every policy gives the
+    same bits (the planner relies on this to pick a configuration per
+    policy)."""
+    import torch
+    from consumer_gemm_chain_amd.mlp_chain import MlpChain
+    from tests._helpers import empty_dev, from_dev
+    from consumer_gemm_chain_amd import build as b
+    M, H, I = 200, 1032, 776
+    x, w1, w2 = _case(M, H, I, act, dtype, seed=31)
+    dev = (to_dev(x, dtype), to_dev(w1, dtype), to_dev(w2, dtype))
+    for s1, s2 in ((1, 1), (2, 3)):
+        ref = None
+        for cfg in range(b.num_configs()):
+            for pol in ("stream_ordered", "tile_sync"):
+                with MlpChain(M, H, I, act, dtype, pol) as ch:
+                    ch.set_config(cfg)
+                    ch.set_split(s1, s2)
+                    out = empty_dev((M, H), dtype)
+                    ch.run(*dev, out)
+                    torch.cuda.synchronize()
+                    assert ch.status() == 0
+                    y = from_dev(out)
+                if ref is None:
+                    ref = y
+                assert np.array_equal(y, ref), (cfg, pol, s1, s2)
