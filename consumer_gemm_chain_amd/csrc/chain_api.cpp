@@ -41,7 +41,6 @@ int fail(int code, const char* fmt, ...) {
 }
 
 constexpr uint32_t DEFAULT_SPIN_LIMIT = 1u << 20;   // ~1 s of polling with back-off
-constexpr uint32_t GROUP_M = 8;
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -287,7 +286,6 @@ mlpc::ChainArgs make_args(const mlp_chain* h, const void* x, const void* w1, con
     a.N2t = h->N2t;
     a.T1 = h->T1;
     a.T2 = h->T2;
-    a.group_m = GROUP_M;
     a.rx = h->Mt >= 2 ? 2u : 1u;
     a.ticket = h->ticket;
     a.flags = h->flags;

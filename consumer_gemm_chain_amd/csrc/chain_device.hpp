@@ -67,7 +67,6 @@ struct ChainArgs {
     int M, H, I;
     int act;
     uint32_t Mt, N1t, N2t, T1, T2;
-    uint32_t group_m;       // row blocks per swizzle group
     uint32_t rx;            // XCD grid rows (1, 2, 4 or 8; the grid is rx x 8/rx)
     uint32_t* ticket;       // 8 tile-queue counters (one per XCD) and an exit counter, 64 words apart;
                             // zero when a run starts (the last workgroup of a run resets them)
@@ -184,20 +183,6 @@ __device__ __forceinline__ u32x4 lds_ld16(const char* smem, int off) {
     return *reinterpret_cast<const u32x4*>(smem + off);
 }
 
-
-// Grouped tile order: walk GROUP row blocks down one column block before
-// moving to the next column block, so tiles that run together share weight
-// columns (and the activation rows) in L2 / MALL.
-__device__ __forceinline__ void tile_coords(uint32_t t, uint32_t Mt, uint32_t Nt, uint32_t group,
-                                            uint32_t& mb, uint32_t& nb) {
-    const uint32_t per_group = group * Nt;
-    const uint32_t gi = t / per_group;
-    const uint32_t first = gi * group;
-    const uint32_t gsz = (Mt - first) < group ? (Mt - first) : group;
-    const uint32_t r = t - gi * per_group;
-    mb = first + r % gsz;
-    nb = r / gsz;
-}
 
 // Workgroups are dispatched to the 8 XCDs round-robin by index, and each XCD
 // has its own L2.  Map index b to item (b % 8) * chunk + b / 8, so that each
