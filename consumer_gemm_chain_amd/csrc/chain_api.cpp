@@ -46,21 +46,32 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 uint32_t cdiv(int64_t a, int64_t b) { return (uint32_t)((a + b - 1) / b); }
 
-// Planner: 16-row tiles while M fits one of them (weight streaming), 64 x
-// 128 tiles while M is a few hundred (each weight panel is read by as few
-// row blocks as possible), then 128 x 128 tiles with two workgroups per CU,
-// or 256 x 128 tiles with one workgroup of eight waves per CU (about 5% more
-// matrix-core throughput per CU, but half as many tiles) once there are
-// enough of those tiles: for the stream-ordered pair when GEMM1 alone fills
-// a wave of them, for the fused policies when it fills three quarters of a
-// wave (the consumer tiles fill the rest -- the CuSync README's point about
-// the producer kernel's last wave).  Crossovers measured on the GPT-3,
-// LLaMA-65 and 8192^3 shards for M in 1..2048.
+// Planner.  Tile configurations (chain_configs.h), chosen by M and tile
+// counts; crossovers measured on the GPT-3, LLaMA-65, Llama-2 and 8192^3
+// shards for M in 1..2048:
+//   * M <= 16: 16 x 64 tiles, four LDS stages (weight streaming);
+//   * M <= 256: 64 x 128 tiles -- with four stages and one workgroup per CU
+//     (three slabs of weights in flight per CU) when each GEMM has at most
+//     one tile per CU, else with two stages and up to three workgroups per
+//     CU;
+//   * above: 128 x 128 tiles with two workgroups per CU, or 256 x 128 tiles
+//     with one workgroup of eight waves per CU (about 5% more matrix-core
+//     throughput per CU, but half as many tiles) once there are enough of
+//     those tiles: for the stream-ordered pair when GEMM1 alone fills a wave
+//     of them, for the fused policies when it fills three quarters of a wave
+//     (the consumer tiles fill the rest -- the CuSync README's point about
+//     the producer kernel's last wave).
+constexpr int CFG_DEEP = 10;    // 64 x 128, four stages, one workgroup per CU
 constexpr int CFG_WIDE = 9;     // 256 x 128, eight waves, three stages
 
-int plan_config(int64_t M, int64_t I, int act, int policy, int cus) {
+int plan_config(int64_t M, int64_t H, int64_t I, int act, int policy, int cus) {
     if (M <= 16) return 0;
-    if (M <= 256) return 1;
+    if (M <= 256) {
+        const int64_t mt = (M + 63) / 64;
+        const int64_t t1 = mt * ((I + (act == MLP_ACT_SWIGLU ? 63 : 127)) / (act == MLP_ACT_SWIGLU ? 64 : 128));
+        const int64_t t2 = mt * ((H + 127) / 128);
+        return t1 <= cus && t2 <= cus ? CFG_DEEP : 1;
+    }
     const int64_t bn1 = act == MLP_ACT_SWIGLU ? 64 : 128;     // producer output columns of the wide config
     const int64_t t1 = ((M + 255) / 256) * ((I + bn1 - 1) / bn1);
     const int64_t need = policy == MLP_POLICY_STREAM_ORDERED ? cus : 3 * (int64_t)cus / 4;
@@ -121,31 +132,39 @@ struct DeviceGuard {
     }
 };
 
+constexpr int LDS_PER_CU = 160 * 1024;        // gfx950
 constexpr uint32_t MIN_SLABS_PER_PART = 24;  // 1536 K-elements: keeps the partial traffic small
+constexpr uint32_t MIN_SLABS_SHARED = 32;    // 2048 K-elements
 
 // Deterministic split of each tile's K range when a GEMM has too few tiles
 // to keep every CU busy.  (The CuSync README names CUTLASS StreamK as the
 // other way to fill the last wave; this is a fixed split with a fixed-order
 // reduction, so results stay bit-identical across policies.)  Targets,
-// measured on the GPT-3 shard (H=12288, I=6144) over M = 1..2048 and every
-// split up to 16:
+// measured on the GPT-3, LLaMA-65 and Llama-2 shards over M = 1..2048 and
+// every split up to 16:
 //   * weight streaming (M < 256): about 3/4 of a part per CU when a single
-//     row block reads each weight panel once, 3/2 parts per CU otherwise --
-//     more parts add partial-sum traffic without adding bandwidth;
-//   * otherwise: as many parts as fit one wave of two workgroups per CU
-//     (a second, partial wave costs more than the split saves).
-// Every part keeps at least MIN_SLABS_PER_PART slabs: on the LLaMA-65 shard
-// (K = 2752 for GEMM2) shorter parts lost more to the fp32 partial sums
-// than the split gained.
-uint32_t plan_split(uint32_t tiles, uint32_t nks, int cus, int64_t M, uint32_t Mt) {
+//     row block reads each weight panel once, at most one part per CU
+//     otherwise -- more parts add partial-sum traffic without adding
+//     bandwidth;
+//   * otherwise no split once the GEMM has a tile per CU (a workgroup alone
+//     on a CU runs much faster than one of two), else as many parts as fit
+//     one wave of the configuration's workgroups per CU (at most two).
+// Every part keeps at least MIN_SLABS_PER_PART slabs (MIN_SLABS_SHARED when
+// several row blocks read each weight panel): on the LLaMA-65 and Llama-2
+// shards (K = 2752 and 3584 for GEMM2) shorter parts lost more to the fp32
+// partial sums than the split gained.
+uint32_t plan_split(uint32_t tiles, uint32_t nks, int cus, int64_t M, uint32_t Mt, uint32_t wg_per_cu) {
     uint32_t s;
-    if (M < 256) {
-        const uint32_t target = Mt == 1 ? 3u * (uint32_t)cus / 4u : 3u * (uint32_t)cus / 2u;
-        s = (target + tiles / 2) / tiles;
+    if (M < 256 && Mt == 1) {
+        s = (3u * (uint32_t)cus / 4u + tiles / 2) / tiles;
+    } else if (M < 256) {
+        s = (uint32_t)cus / tiles;
+    } else if (tiles >= (uint32_t)cus) {
+        s = 1;
     } else {
-        s = 2u * (uint32_t)cus / tiles;
+        s = (wg_per_cu < 2 ? wg_per_cu : 2u) * (uint32_t)cus / tiles;
     }
-    const uint32_t cap = nks / MIN_SLABS_PER_PART;
+    const uint32_t cap = nks / (Mt == 1 ? MIN_SLABS_PER_PART : MIN_SLABS_SHARED);
     if (s > cap) s = cap;
     if (s < 1) s = 1;
     const uint32_t ksp = (nks + s - 1) / s;      // no empty parts
@@ -170,12 +189,13 @@ int apply_plan(mlp_chain* h, int cfg) {
     // the same slabs), the split does: equal splits keep the policies
     // bit-identical while each uses its own tile configuration.
     {
-        const CfgInfo cs = mlpc_config_info(plan_config(h->M, h->I, h->act, MLP_POLICY_STREAM_ORDERED, h->cus));
+        const CfgInfo cs = mlpc_config_info(plan_config(h->M, h->H, h->I, h->act, MLP_POLICY_STREAM_ORDERED, h->cus));
         const uint32_t mt = cdiv(h->M, cs.BM);
         const uint32_t t1 = mt * cdiv(h->I, h->act == MLP_ACT_SWIGLU ? cs.BN / 2 : cs.BN);
         const uint32_t t2 = mt * cdiv(h->H, cs.BN);
-        h->S1 = h->forced_s1 > 0 ? (uint32_t)h->forced_s1 : plan_split(t1, nks1, h->cus, h->M, mt);
-        h->S2 = h->forced_s2 > 0 ? (uint32_t)h->forced_s2 : plan_split(t2, nks2, h->cus, h->M, mt);
+        const uint32_t wg = (uint32_t)(LDS_PER_CU / cs.lds);          // workgroups per CU the ring allows
+        h->S1 = h->forced_s1 > 0 ? (uint32_t)h->forced_s1 : plan_split(t1, nks1, h->cus, h->M, mt, wg);
+        h->S2 = h->forced_s2 > 0 ? (uint32_t)h->forced_s2 : plan_split(t2, nks2, h->cus, h->M, mt, wg);
     }
     h->ksp1 = (nks1 + h->S1 - 1) / h->S1;
     h->ksp2 = (nks2 + h->S2 - 1) / h->S2;
@@ -383,7 +403,7 @@ mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype
     h->trace = nullptr;
     h->last_stream = nullptr;
     h->ws = nullptr;
-    if (apply_plan(h, plan_config(M, I, act, policy, h->cus)) != MLP_OK || build_workspace(h) != MLP_OK) {
+    if (apply_plan(h, plan_config(M, H, I, act, policy, h->cus)) != MLP_OK || build_workspace(h) != MLP_OK) {
         if (h->ws) (void)hipFree(h->ws);
         delete h;
         return nullptr;
@@ -494,7 +514,7 @@ int mlp_chain_debug_skip_producer(mlp_chain_t h, int64_t tile) {
 
 static int replan(mlp_chain_t h) {
     DeviceGuard g(h->device);
-    const int cfg = h->forced_cfg < 0 ? plan_config(h->M, h->I, h->act, h->policy, h->cus) : h->forced_cfg;
+    const int cfg = h->forced_cfg < 0 ? plan_config(h->M, h->H, h->I, h->act, h->policy, h->cus) : h->forced_cfg;
     int rc = apply_plan(h, cfg);
     if (rc != MLP_OK) return rc;
     return build_workspace(h);

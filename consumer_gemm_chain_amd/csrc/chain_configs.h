@@ -13,7 +13,10 @@
     X(6, 128, 256, 2, 4, 2, 2)   /* eight waves of 64x64 */                                   \
     X(7, 256, 128, 4, 2, 2, 2)   /* eight waves of 64x64 */                                   \
     X(8, 128, 256, 2, 4, 3, 2)   /* eight waves of 64x64, three stages */                     \
-    X(9, 256, 128, 4, 2, 3, 2)   /* large M: eight waves of 64x64, three stages, one WG per CU */
+    X(9, 256, 128, 4, 2, 3, 2)   /* large M: eight waves of 64x64, three stages, one WG per CU */ \
+    X(10, 64, 128, 2, 2, 4, 1)   /* exp: weight streaming, three slabs in flight */           \
+    X(11, 32, 128, 1, 2, 4, 1)   /* exp */                                                    \
+    X(12, 16, 256, 1, 2, 4, 1)   /* exp: decode, 512-byte weight strips */
 
 #define MLPC_COUNT_CFG(id, ...) +1
 constexpr int MLPC_NUM_CONFIGS = 0 MLPC_CONFIGS(MLPC_COUNT_CFG);

@@ -11,7 +11,7 @@ enum { LAUNCH_GEMM1 = 1, LAUNCH_GEMM2 = 2, LAUNCH_ROW = 3, LAUNCH_TILE = 4 };
 struct CfgInfo {
     int id;
     int BM, BN, BK, NT;   // BN: weight columns per tile (SwiGLU producers: BN/2 output columns)
-    int lds;              // dynamic LDS bytes per workgroup
+    int lds;              // LDS bytes of the ring per workgroup
 };
 
 int mlpc_num_configs();
