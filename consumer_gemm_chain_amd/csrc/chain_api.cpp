@@ -61,8 +61,8 @@ uint32_t cdiv(int64_t a, int64_t b) { return (uint32_t)((a + b - 1) / b); }
 //     of them, for the fused policies when it fills three quarters of a wave
 //     (the consumer tiles fill the rest -- the CuSync README's point about
 //     the producer kernel's last wave).
-constexpr int CFG_DEEP = 10;    // 64 x 128, four stages, one workgroup per CU
-constexpr int CFG_WIDE = 9;     // 256 x 128, eight waves, three stages
+constexpr int CFG_DEEP = 4;     // 64 x 128, four stages, one workgroup per CU
+constexpr int CFG_WIDE = 3;     // 256 x 128, eight waves, three stages
 
 int plan_config(int64_t M, int64_t H, int64_t I, int act, int policy, int cus) {
     if (M <= 16) return 0;

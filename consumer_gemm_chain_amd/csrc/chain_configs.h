@@ -4,19 +4,13 @@
 #pragma once
 
 #define MLPC_CONFIGS(X)                                                                        \
-    X(0, 16, 64, 1, 2, 4, 2)     /* small M: narrow tiles, weight streaming */                \
-    X(1, 64, 128, 2, 2, 2, 2)    /* medium M, two stages */                                   \
-    X(2, 128, 128, 2, 2, 2, 2)   /* large M, two stages: two workgroups per CU */             \
-    X(3, 256, 128, 2, 2, 2, 1)   /* 128x64 per wave, one wave per SIMD */                     \
-    X(4, 128, 256, 2, 2, 2, 1)   /* 64x128 per wave, one wave per SIMD */                     \
-    X(5, 16, 128, 1, 2, 4, 1)    /* small M, 16x64 per wave */                                \
-    X(6, 128, 256, 2, 4, 2, 2)   /* eight waves of 64x64 */                                   \
-    X(7, 256, 128, 4, 2, 2, 2)   /* eight waves of 64x64 */                                   \
-    X(8, 128, 256, 2, 4, 3, 2)   /* eight waves of 64x64, three stages */                     \
-    X(9, 256, 128, 4, 2, 3, 2)   /* large M: eight waves of 64x64, three stages, one WG per CU */ \
-    X(10, 64, 128, 2, 2, 4, 1)   /* exp: weight streaming, three slabs in flight */           \
-    X(11, 32, 128, 1, 2, 4, 1)   /* exp */                                                    \
-    X(12, 16, 256, 1, 2, 4, 1)   /* exp: decode, 512-byte weight strips */
+    X(0, 16, 64, 1, 2, 4, 2)     /* M <= 16: weight streaming, four stages */                 \
+    X(1, 64, 128, 2, 2, 2, 2)    /* M <= 256: two stages, up to three workgroups per CU */     \
+    X(2, 128, 128, 2, 2, 2, 2)   /* large M: two stages, two workgroups per CU */              \
+    X(3, 256, 128, 4, 2, 3, 2)   /* large M: eight waves of 64x64, three stages, one WG/CU */   \
+    X(4, 64, 128, 2, 2, 4, 1)    /* M <= 256: four stages, one workgroup per CU */            \
+    X(5, 256, 128, 2, 2, 3, 1)   /* measurements: four waves of 128x64 */                     \
+    X(6, 128, 256, 2, 4, 3, 2)   /* measurements: eight waves of 64x64, 128 x 256 */
 
 #define MLPC_COUNT_CFG(id, ...) +1
 constexpr int MLPC_NUM_CONFIGS = 0 MLPC_CONFIGS(MLPC_COUNT_CFG);
