@@ -26,8 +26,10 @@
 //     against LDS bank conflicts (the bearblog post on swizzling).  The
 //     swizzles depend only on the lane, so every fragment address is a
 //     per-lane base plus a compile-time offset.
-//   * Edges: chunks outside the matrices are fetched from a zero page, so
-//     the ring always holds zeros beyond M, N and K.
+//   * Edges: rows past M and columns past N are clamped to the last valid
+//     row / chunk (their results are never stored); a tile part whose K
+//     range ends past K (only when K % 64 != 0) fetches out-of-range chunks
+//     from a zero page, so the ring holds zeros beyond K.
 //   * Epilogue: activation on the fp32 accumulators, one round-to-nearest-even
 //     conversion, staged through LDS and written with 16-byte stores (the
 //     registers -> shared memory -> global (M, N) epilogue of the bearblog
@@ -366,6 +368,17 @@ __device__ __forceinline__ int b_column(const TileJob& j, int nb, bool& ok) {
     return oc;
 }
 
+// Global column of B-tile column block nb, with output columns past b_cols
+// clamped to the last 8-column chunk (b_cols is a multiple of 8).
+__device__ __forceinline__ int b_column_clamped(const TileJob& j, int nb) {
+    if (j.inter) {
+        const int f = nb >> 1;
+        const int oc = min(j.n0 + (f >> 1) * 16 + (nb & 1) * 8, j.b_cols - 8);
+        return oc + (f & 1) * j.up;
+    }
+    return min(j.n0 + nb * 8, j.b_cols - 8);
+}
+
 // The LDS ring of configuration C: NS stages of STAGE bytes (A slab, then B
 // slab); stage 0 also holds the epilogue staging area.
 template <class C>
@@ -397,27 +410,39 @@ __device__ __forceinline__ int b_chunk(int k, int c) {
     return c ^ ((2 * ((k & 3) | (((k >> 3) & 1) << 2))) & (C::CPR - 1));
 }
 
-__device__ __forceinline__ void dma16(const uint16_t* src, char* lds) {
+__device__ __forceinline__ void dma16(const void* src, char* lds) {
     // (a C-style cast is the way to change the address space to LDS)
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
-                                     (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
 }
 
-// Per-tile DMA state of one lane.  Interior slabs (every row, column and
-// K index of the slab inside the matrices) are fetched as a wave-uniform
-// base pointer (scalar registers, advanced per slab) plus the lane's 32-bit
-// byte offset of each chunk, computed once per tile -- the saddr form of
-// global_load_lds, with no per-slab address arithmetic.  Edge slabs (and
-// the slabs past a tile's ks1 that keep the pipeline count fixed) take the
-// per-lane path with the zero page.
+// The wave index as a scalar (wave-uniform) value, so that LDS destinations
+// built from it stay in scalar registers (M0 comes straight from them).
+__device__ __forceinline__ int uniform_wave() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// A per-lane 32-bit offset re-materialised at its use: this keeps the
+// compiler from hoisting its 64-bit extension out of the K loop, so that
+// `uniform pointer + offset` selects the saddr form of the DMA (scalar base,
+// 32-bit vector offset) instead of a 64-bit vector add per instruction.
+__device__ __forceinline__ uint32_t fresh(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// Per-tile DMA state of one lane.  A tile whose K range ends inside the
+// matrices (every part except a last one with K % 64 != 0) is fetched in
+// the saddr form of global_load_lds: a wave-uniform base pointer (scalar
+// registers, advanced per slab) plus the lane's 32-bit byte offset of each
+// chunk, computed once per tile, with no per-slab address arithmetic.  Rows
+// past a_rows and columns past b_cols are clamped to the last row / column
+// chunk: they read valid memory, and the results they produce are never
+// stored.  A tile with a K tail takes the per-lane path with the zero page
+// for every slab.
 template <class C>
 struct TileDma {
     const char* a_base;           // row m0 of A
     const char* b_base;           // B
     uint32_t va[C::A_PER_WAVE];   // A chunk offsets in slab 0 (bytes from a_base)
     uint32_t vb[C::B_PER_WAVE];   // B chunk offsets in slab 0 (bytes from b_base)
-    bool a_full;                  // every row of the tile is below a_rows
-    bool b_full;                  // every output column of the tile is below b_cols
 };
 
 template <class C>
@@ -430,75 +455,72 @@ __device__ __forceinline__ TileDma<C> tile_dma(const TileJob& j) {
     for (int q = 0; q < C::A_PER_WAVE; ++q) {
         const int L = (wave * C::A_PER_WAVE + q) * 64 + lane;
         const int r = L >> 3, c = a_chunk(r, L & 7);
-        d.va[q] = (uint32_t)r * (uint32_t)j.lda * 2u + (uint32_t)c * 16u;
+        const int rr = min(j.m0 + r, j.a_rows - 1) - j.m0;
+        d.va[q] = (uint32_t)rr * (uint32_t)j.lda * 2u + (uint32_t)c * 16u;
     }
 #pragma unroll
     for (int q = 0; q < C::B_PER_WAVE; ++q) {
         const int L = (wave * C::B_PER_WAVE + q) * 64 + lane;
         const int k = L / C::CPR, p = L % C::CPR;
-        bool ok;
-        const int gcol = b_column(j, b_chunk<C>(k, p), ok);
+        const int gcol = b_column_clamped(j, b_chunk<C>(k, p));
         d.vb[q] = ((uint32_t)k * (uint32_t)j.ldb + (uint32_t)gcol) * 2u;
     }
-    d.a_full = j.m0 + C::BM <= j.a_rows;
-    d.b_full = j.n0 + (j.inter ? C::BN / 2 : C::BN) <= j.b_cols;
     return d;
 }
 
-// Issue the DMA of slab ks (B part and/or A part) into stage S.  Every wave
-// issues B_PER_WAVE B instructions and A_PER_WAVE A instructions; lane i of
-// an instruction fills LDS chunk L0 + i, and picks the global chunk that
-// belongs there under the swizzle (or the zero page).  Slabs at or past the
-// tile's ks1 are issued too (all zero page), so that every wave always has
-// the same number of DMA instructions in flight.
-template <class C, int S>
-__device__ __forceinline__ void issue_b(const TileJob& j, const TileDma<C>& d, int ks) {
-    char* st = lds_ring<C>() + S * C::STAGE + C::A_BYTES;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// Issue the DMA of slab ks (B part and/or A part) into stage `stage`.  Every
+// wave issues B_PER_WAVE B instructions and A_PER_WAVE A instructions; lane
+// i of an instruction fills LDS chunk L0 + i with the global chunk that
+// belongs there under the swizzle.  TAIL: per-lane addresses, with the zero
+// page for rows, columns and K indices outside the matrices.
+template <class C, bool TAIL>
+__device__ __forceinline__ void issue_b(const TileJob& j, const TileDma<C>& d, int ks, int stage) {
+    char* st = lds_ring<C>() + stage * C::STAGE + C::A_BYTES;
+    const int wave = uniform_wave();
     const int k0 = ks * BK;
-    const int kend = min(j.K, j.ks1 * BK);      // slabs at or past ks1 read the zero page
-    if (d.b_full && k0 + BK <= kend) {
+    if constexpr (!TAIL) {
         const char* base = d.b_base + (size_t)k0 * j.ldb * 2;
 #pragma unroll
         for (int q = 0; q < C::B_PER_WAVE; ++q)
-            dma16(reinterpret_cast<const uint16_t*>(base + d.vb[q]), st + (wave * C::B_PER_WAVE + q) * 1024);
-        return;
-    }
+            dma16(base + fresh(d.vb[q]), st + (wave * C::B_PER_WAVE + q) * 1024);
+    } else {
+        const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int q = 0; q < C::B_PER_WAVE; ++q) {
-        const int L0 = (wave * C::B_PER_WAVE + q) * 64;
-        const int L = L0 + lane;
-        const int k = L / C::CPR, p = L % C::CPR;
-        const int c = b_chunk<C>(k, p);
-        bool ok;
-        const int gcol = b_column(j, c, ok);
-        const int gk = k0 + k;
-        const uint16_t* src = (ok && gk < kend) ? j.B + (size_t)gk * j.ldb + gcol : j.zero;
-        dma16(src, st + L0 * 16);
+        for (int q = 0; q < C::B_PER_WAVE; ++q) {
+            const int L0 = (wave * C::B_PER_WAVE + q) * 64;
+            const int L = L0 + lane;
+            const int k = L / C::CPR, p = L % C::CPR;
+            const int c = b_chunk<C>(k, p);
+            bool ok;
+            const int gcol = b_column(j, c, ok);
+            const int gk = k0 + k;
+            const uint16_t* src = (ok && gk < j.K) ? j.B + (size_t)gk * j.ldb + gcol : j.zero;
+            dma16(src, st + L0 * 16);
+        }
     }
 }
 
-template <class C, int S>
-__device__ __forceinline__ void issue_a(const TileJob& j, const TileDma<C>& d, int ks) {
-    char* st = lds_ring<C>() + S * C::STAGE;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+template <class C, bool TAIL>
+__device__ __forceinline__ void issue_a(const TileJob& j, const TileDma<C>& d, int ks, int stage) {
+    char* st = lds_ring<C>() + stage * C::STAGE;
+    const int wave = uniform_wave();
     const int k0 = ks * BK;
-    const int kend = min(j.K, j.ks1 * BK);
-    if (d.a_full && k0 + BK <= kend) {
+    if constexpr (!TAIL) {
         const char* base = d.a_base + (size_t)k0 * 2;
 #pragma unroll
         for (int q = 0; q < C::A_PER_WAVE; ++q)
-            dma16(reinterpret_cast<const uint16_t*>(base + d.va[q]), st + (wave * C::A_PER_WAVE + q) * 1024);
-        return;
-    }
+            dma16(base + fresh(d.va[q]), st + (wave * C::A_PER_WAVE + q) * 1024);
+    } else {
+        const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int q = 0; q < C::A_PER_WAVE; ++q) {
-        const int L0 = (wave * C::A_PER_WAVE + q) * 64;
-        const int L = L0 + lane;
-        const int r = L >> 3, c = a_chunk(r, L & 7);
-        const int gm = j.m0 + r, gk = k0 + c * 8;
-        const uint16_t* src = (gm < j.a_rows && gk < kend) ? j.A + (size_t)gm * j.lda + gk : j.zero;
-        dma16(src, st + L0 * 16);
+        for (int q = 0; q < C::A_PER_WAVE; ++q) {
+            const int L0 = (wave * C::A_PER_WAVE + q) * 64;
+            const int L = L0 + lane;
+            const int r = L >> 3, c = a_chunk(r, L & 7);
+            const int gm = j.m0 + r, gk = k0 + c * 8;
+            const uint16_t* src = (gm < j.a_rows && gk < j.K) ? j.A + (size_t)gm * j.lda + gk : j.zero;
+            dma16(src, st + L0 * 16);
+        }
     }
 }
 
@@ -572,23 +594,18 @@ __device__ __forceinline__ FragBase<C> frag_base() {
     return f;
 }
 
-// Issue the LDS reads of half slab KK of stage S into f.
-template <class C, int S, int KK>
-__device__ __forceinline__ void frag_load(const FragBase<C>& fb, Frags<C>& f) {
-    constexpr uint32_t SO = S * C::STAGE;
+// Issue the LDS reads of half slab KK of the stage at byte offset `so` into f.
+template <class C, int KK>
+__device__ __forceinline__ void frag_load(const FragBase<C>& fb, uint32_t so, Frags<C>& f) {
     constexpr uint32_t A_MAX = (C::FM - 1) * 16 * 128;
     constexpr uint32_t B_MAX = (KK * 32 + 4) * C::CPR * 16;
-    // fold the stage offset into the immediate when it fits the 16-bit field
-    constexpr bool FOLD = SO + C::A_BYTES + B_MAX < 65536;
-    constexpr uint32_t SI = FOLD ? SO : 0;
-    const uint32_t sr = FOLD ? 0 : SO;
     static_assert(A_MAX < 65536 && C::A_BYTES + B_MAX < 65536, "stage too large for ds offsets");
-    static_for<0, C::FM>([&](auto fm) {
-        f.a[fm] = ds_read_b128<SI + decltype(fm)::value * 16 * 128>(fb.a[KK] + sr);
-    });
+    const uint32_t a = fb.a[KK] + so;
+    static_for<0, C::FM>([&](auto fm) { f.a[fm] = ds_read_b128<decltype(fm)::value * 16 * 128>(a); });
     static_for<0, C::FN>([&](auto fn) {
-        const u32x2 lo = ds_read_tr16_b64<SI + KK * 32 * C::CPR * 16>(fb.b[fn] + sr);
-        const u32x2 hi = ds_read_tr16_b64<SI + (KK * 32 + 4) * C::CPR * 16>(fb.b[fn] + sr);
+        const uint32_t b = fb.b[fn] + so;
+        const u32x2 lo = ds_read_tr16_b64<KK * 32 * C::CPR * 16>(b);
+        const u32x2 hi = ds_read_tr16_b64<(KK * 32 + 4) * C::CPR * 16>(b);
         f.b[fn] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     });
 }
@@ -630,42 +647,56 @@ __device__ __forceinline__ void ring_barrier() {
 // LDS-visible barrier that leaves the DMA ring in flight.
 __device__ __forceinline__ void lds_barrier() { ring_barrier<63>(); }
 
-template <class C, class Wait, int S>
-__device__ __forceinline__ void issue_slab(const TileJob& j, const TileDma<C>& d, int ks, Wait& wait) {
-    issue_b<C, S>(j, d, ks);
-    if (ks < j.ks1) wait(ks);
-    issue_a<C, S>(j, d, ks);
+template <class C, bool TAIL, class Wait>
+__device__ __forceinline__ void issue_slab(const TileJob& j, const TileDma<C>& d, int ks, int stage, Wait& wait) {
+    issue_b<C, TAIL>(j, d, ks, stage);
+    wait(ks);
+    issue_a<C, TAIL>(j, d, ks, stage);
 }
 
-// One pipeline step over slab ks, which lives in stage S: once slab ks has
-// landed and every wave is done with the previous stage, refill that stage
-// with slab ks+NS-1, read both half slabs of stage S, and run the first
-// half's MFMAs while the second half's reads are still in flight.  The step
-// has no data-dependent branch between its MFMAs (the accumulators stay in
-// place): past the tile's last slab the DMA reads the zero page.
-template <class C, int DT, int S, class Wait>
-__device__ __forceinline__ void pipe_step(const TileJob& j, const TileDma<C>& d, int ks, const FragBase<C>& fb,
-                                          f32x4 (&acc)[C::FM][C::FN], Wait& wait) {
-    // slab ks has landed once only slabs ks+1 .. ks+NS-2 remain in flight
-    ring_barrier<C::LPS * (C::NS - 2)>();
-    issue_slab<C, Wait, (S + C::NS - 1) % C::NS>(j, d, ks + C::NS - 1, wait);
-    Frags<C> f0, f1;
-    frag_load<C, S, 0>(fb, f0);
-    frag_load<C, S, 1>(fb, f1);
-    lgkm_wait<C::NREAD>();
-    frag_pin(f0);
-    mfma_block<C, DT>(acc, f0);
-    __builtin_amdgcn_sched_barrier(0);
-    lgkm_wait<0>();
-    frag_pin(f1);
-    mfma_block<C, DT>(acc, f1);
-    __builtin_amdgcn_sched_barrier(0);
+// The K loop of one tile over slabs ks0 .. ks1-1.  `wait(ks)` is called
+// (uniformly) before the A-operand DMA of slab ks -- the consumer's
+// dependency on its producers; the B-operand (weight) DMA of that slab is
+// issued before the wait.  Slab ks0 + i lives in stage i % NS; slabs ks0 ..
+// ks0+NS-2 are requested before the first step.  One step per slab ks
+// (stage st): once slab ks has landed and every wave is done with the
+// previous stage, refill that stage with slab ks+NS-1, read both half slabs
+// of stage st, and run the first half's MFMAs while the second half's reads
+// are still in flight.  A slab's DMA has NS-1 steps to land.  In the last
+// NS-2 steps no slab is requested and the barrier waits for every
+// outstanding one.  The branches in a step are wave-uniform and hold only
+// waits and DMA issues, so the accumulators stay in place.  (Requesting the
+// next slab's first half slab during the second half's MFMAs, with the
+// barrier between the two MFMA groups, measured 4-10% more cycles per tile.)
+template <class C, int DT, bool TAIL, class Wait>
+__device__ __forceinline__ void tile_kloop(const TileJob& j, f32x4 (&acc)[C::FM][C::FN], Wait& wait) {
+    const FragBase<C> fb = frag_base<C>();
+    const TileDma<C> d = tile_dma<C>(j);
+    const int ks0 = j.ks0, ks1 = j.ks1;
+#pragma unroll
+    for (int i = 0; i < C::NS - 1; ++i)
+        if (ks0 + i < ks1) issue_slab<C, TAIL, Wait>(j, d, ks0 + i, i, wait);
+    int st = 0;
+    for (int ks = ks0; ks < ks1; ++ks) {
+        const int pv = st == 0 ? C::NS - 1 : st - 1;
+        if (ks + C::NS - 1 <= ks1) ring_barrier<C::LPS * (C::NS - 2)>();
+        else ring_barrier<0>();
+        if (ks + C::NS - 1 < ks1) issue_slab<C, TAIL, Wait>(j, d, ks + C::NS - 1, pv, wait);
+        Frags<C> f0, f1;
+        frag_load<C, 0>(fb, (uint32_t)st * C::STAGE, f0);
+        frag_load<C, 1>(fb, (uint32_t)st * C::STAGE, f1);
+        lgkm_wait<C::NREAD>();
+        frag_pin(f0);
+        mfma_block<C, DT>(acc, f0);
+        __builtin_amdgcn_sched_barrier(0);
+        lgkm_wait<0>();
+        frag_pin(f1);
+        mfma_block<C, DT>(acc, f1);
+        __builtin_amdgcn_sched_barrier(0);
+        st = st + 1 == C::NS ? 0 : st + 1;
+    }
 }
 
-// The K loop of one tile.  `wait(ks)` is called (uniformly) before the
-// A-operand DMA of slab ks -- the consumer's dependency on its producers;
-// the B-operand (weight) DMA of that slab is issued before the wait.
-// Slab ks0 + i lives in stage i % NS.
 template <class C, int DT, class Wait>
 __device__ __forceinline__ void tile_mainloop(const TileJob& j, f32x4 (&acc)[C::FM][C::FN], Wait& wait) {
 #pragma unroll
@@ -673,25 +704,8 @@ __device__ __forceinline__ void tile_mainloop(const TileJob& j, f32x4 (&acc)[C::
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (j.ks1 > j.ks0) {
-        const FragBase<C> fb = frag_base<C>();
-        const TileDma<C> d = tile_dma<C>(j);
-        // prologue: slabs ks0 .. ks0+NS-2 into stages 0 .. NS-2
-        issue_slab<C, Wait, 0>(j, d, j.ks0, wait);
-        if constexpr (C::NS > 2) issue_slab<C, Wait, 1>(j, d, j.ks0 + 1, wait);
-        if constexpr (C::NS > 3) issue_slab<C, Wait, 2>(j, d, j.ks0 + 2, wait);
-        // whole rounds of NS steps, then the remaining steps (no exits
-        // mid-round, so the accumulators stay in place across the loop)
-        int ks = j.ks0;
-        for (; ks + C::NS <= j.ks1; ks += C::NS) {
-            pipe_step<C, DT, 0>(j, d, ks, fb, acc, wait);
-            pipe_step<C, DT, 1>(j, d, ks + 1, fb, acc, wait);
-            if constexpr (C::NS > 2) pipe_step<C, DT, 2>(j, d, ks + 2, fb, acc, wait);
-            if constexpr (C::NS > 3) pipe_step<C, DT, 3>(j, d, ks + 3, fb, acc, wait);
-        }
-        const int rem = j.ks1 - ks;
-        if (rem > 0) pipe_step<C, DT, 0>(j, d, ks, fb, acc, wait);
-        if constexpr (C::NS > 2) if (rem > 1) pipe_step<C, DT, 1>(j, d, ks + 1, fb, acc, wait);
-        if constexpr (C::NS > 3) if (rem > 2) pipe_step<C, DT, 2>(j, d, ks + 2, fb, acc, wait);
+        if (j.ks1 * BK <= j.K) tile_kloop<C, DT, false>(j, acc, wait);
+        else tile_kloop<C, DT, true>(j, acc, wait);
     }
     // every wave is done reading the ring (and all DMA has landed) before
     // the epilogue reuses stage 0

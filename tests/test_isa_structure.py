@@ -39,10 +39,12 @@ def asm(tmp_path_factory):
         return "\n".join(ex.map(one, range(b.num_configs())))
 
 
-def _functions(text, prefix):
+def _functions(text, prefix, whole=False):
+    """(name, body) of each kernel; the body ends at the first s_endpgm, or
+    at the end of the function when `whole`."""
     for m in re.finditer(rf"^({prefix}\w*):", text, flags=re.M):
         start = m.end()
-        end = text.index("s_endpgm", start)
+        end = text.index(".Lfunc_end", start) if whole else text.index("s_endpgm", start)
         yield m.group(1), text[start:end]
 
 
@@ -89,3 +91,38 @@ def test_dma_only_through_range_checked_offsets(asm):
         m = re.match(r"buffer_load_dword\w*\s+v\d+,\s*s\[\d+:\d+\],\s*(\S+)\s+offen\s+lds\s*$", ins)
         assert m and m.group(1) == "0", ins
     assert "global_load_lds" not in asm
+
+
+def _inner_mfma_loops(body):
+    """Innermost loops (back-edges to an earlier label) that contain MFMAs."""
+    lines = body.split("\n")
+    labels = {}
+    for i, l in enumerate(lines):
+        m = re.match(r"^(\.LBB\d+_\d+):", l)
+        if m:
+            labels[m.group(1)] = i
+    loops = []
+    for i, l in enumerate(lines):
+        m = re.search(r"s_(?:c)?branch\w*\s+(\.LBB\d+_\d+)", l)
+        if m and m.group(1) in labels and labels[m.group(1)] < i:
+            seg = lines[labels[m.group(1)]:i + 1]
+            if any("v_mfma" in s for s in seg):
+                loops.append((labels[m.group(1)], i, seg))
+    return [seg for lo, hi, seg in loops
+            if not any((o[0], o[1]) != (lo, hi) and o[0] >= lo and o[1] <= hi for o in loops)]
+
+
+def test_k_loops_keep_accumulators_in_place_and_use_scalar_base_dma(asm):
+    """The K loops of the stand-alone GEMM kernels: no accumulator moves
+    between register files (a sign that control flow inside the loop made the
+    compiler shuffle them), no scratch traffic, and operand DMA in the saddr
+    form (scalar base + 32-bit lane offset) present in the kernel."""
+    for prefix in ("_ZN4mlpc12gemm2_kernel", "_ZN4mlpc16gemm1_act_kernel"):
+        for name, body in _functions(asm, prefix, whole=True):
+            loops = _inner_mfma_loops(body)
+            assert loops, name
+            for seg in loops:
+                text = "\n".join(seg)
+                assert "v_accvgpr_mov" not in text and "v_accvgpr_read" not in text, name
+                assert "scratch_" not in text, name
+            assert re.search(r"global_load_lds_dwordx4 v\d+, s\[\d+:\d+\]", body), name
