@@ -124,6 +124,12 @@ struct TileCfg {
     static constexpr int LPS = A_PER_WAVE + B_PER_WAVE;  // DMA instructions per wave per slab
     static_assert(LPS * (NS - 2) <= 63, "vmcnt range");
     static constexpr int NREAD = FM + 2 * FN;            // LDS reads per fragment set
+    // DMA of the next slab spread over the second half slab's MFMAs (eight
+    // waves, at least three stages); otherwise issued in one group after the
+    // first half slab's reads.  The spread form needs a branch-free step,
+    // which made the compiler copy AGPR-resident accumulators around the
+    // loop in the smaller configurations.
+    static constexpr bool SPREAD = NW == 8 && NS >= 3;
     static constexpr int lds_bytes() { return NS * STAGE; }
 };
 
@@ -627,6 +633,41 @@ __device__ __forceinline__ void mfma_block(f32x4 (&acc)[C::FM][C::FN], const Fra
         for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = mfma16x16x32<DT>(f.a[fm], f.b[fn], acc[fm][fn]);
 }
 
+// Read number R (A fragments first, then the two halves of each B
+// fragment) of half slab KK of the stage at byte offset `so` into f.
+template <class C, int KK, int R>
+__device__ __forceinline__ void frag_read_one(const FragBase<C>& fb, uint32_t so, Frags<C>& f) {
+    if constexpr (R < C::FM) {
+        f.a[R] = ds_read_b128<R * 16 * 128>(fb.a[KK] + so);
+    } else {
+        constexpr int fn = (R - C::FM) / 2, hi = (R - C::FM) % 2;
+        const u32x2 v = ds_read_tr16_b64<(KK * 32 + 4 * hi) * C::CPR * 16>(fb.b[fn] + so);
+        if constexpr (hi == 0) {
+            f.b[fn][0] = v[0];
+            f.b[fn][1] = v[1];
+        } else {
+            f.b[fn][2] = v[0];
+            f.b[fn][3] = v[1];
+        }
+    }
+}
+
+// The MFMAs of fragments f, with the reads of half slab KK into g issued one
+// after each of the first NREAD MFMAs.
+template <class C, int DT, int KK>
+__device__ __forceinline__ void mfma_block_reading(f32x4 (&acc)[C::FM][C::FN], const Frags<C>& f,
+                                                   const FragBase<C>& fb, uint32_t so, Frags<C>& g) {
+    static_for<0, C::FM * C::FN>([&](auto i) {
+        constexpr int I = decltype(i)::value;
+        acc[I / C::FN][I % C::FN] = mfma16x16x32<DT>(f.a[I / C::FN], f.b[I % C::FN], acc[I / C::FN][I % C::FN]);
+        if constexpr (I < C::NREAD) frag_read_one<C, KK, I>(fb, so, g);
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (C::FM * C::FN < C::NREAD) {
+        static_for<C::FM * C::FN, C::NREAD>([&](auto i) { frag_read_one<C, KK, decltype(i)::value>(fb, so, g); });
+    }
+}
+
 // Wait until at most `n` DMA instructions of this wave are outstanding and
 // every LDS access of this wave has completed, then meet the other waves.
 // (A bare s_barrier: __syncthreads() would also wait for all DMA.)
@@ -647,6 +688,62 @@ __device__ __forceinline__ void ring_barrier() {
 // LDS-visible barrier that leaves the DMA ring in flight.
 __device__ __forceinline__ void lds_barrier() { ring_barrier<63>(); }
 
+// DMA instruction Q (of LPS) of slab ks into stage `stage`: Q < B_PER_WAVE
+// is B instruction Q, the rest are the A instructions.
+template <class C, bool TAIL, int Q>
+__device__ __forceinline__ void issue_one(const TileJob& j, const TileDma<C>& d, int ks, int stage) {
+    const int wave = uniform_wave();
+    const int k0 = ks * BK;
+    if constexpr (Q < C::B_PER_WAVE) {
+        char* st = lds_ring<C>() + stage * C::STAGE + C::A_BYTES;
+        if constexpr (!TAIL) {
+            const char* base = d.b_base + (size_t)k0 * j.ldb * 2;
+            dma16(base + fresh(d.vb[Q]), st + (wave * C::B_PER_WAVE + Q) * 1024);
+        } else {
+            const int L0 = (wave * C::B_PER_WAVE + Q) * 64;
+            const int L = L0 + (threadIdx.x & 63);
+            const int k = L / C::CPR, p = L % C::CPR;
+            bool ok;
+            const int gcol = b_column(j, b_chunk<C>(k, p), ok);
+            const int gk = k0 + k;
+            dma16((ok && gk < j.K) ? j.B + (size_t)gk * j.ldb + gcol : j.zero, st + L0 * 16);
+        }
+    } else {
+        constexpr int QA = Q - C::B_PER_WAVE;
+        char* st = lds_ring<C>() + stage * C::STAGE;
+        if constexpr (!TAIL) {
+            const char* base = d.a_base + (size_t)k0 * 2;
+            dma16(base + fresh(d.va[QA]), st + (wave * C::A_PER_WAVE + QA) * 1024);
+        } else {
+            const int L0 = (wave * C::A_PER_WAVE + QA) * 64;
+            const int L = L0 + (threadIdx.x & 63);
+            const int r = L >> 3, c = a_chunk(r, L & 7);
+            const int gm = j.m0 + r, gk = k0 + c * 8;
+            dma16((gm < j.a_rows && gk < j.K) ? j.A + (size_t)gm * j.lda + gk : j.zero, st + L0 * 16);
+        }
+    }
+}
+
+// The MFMAs of fragments f with the LPS DMA instructions of slab ks (into
+// `stage`) issued one after every other MFMA, so that the DMA of all waves
+// is spread over the step instead of queueing up in one burst.
+template <class C, int DT, bool TAIL>
+__device__ __forceinline__ void mfma_block_dma(f32x4 (&acc)[C::FM][C::FN], const Frags<C>& f,
+                                               const TileJob& j, const TileDma<C>& d, int ks, int stage) {
+    constexpr int GAP = (C::FM * C::FN) / C::LPS >= 2 ? 2 : 1;
+    static_for<0, C::FM * C::FN>([&](auto i) {
+        constexpr int I = decltype(i)::value;
+        acc[I / C::FN][I % C::FN] = mfma16x16x32<DT>(f.a[I / C::FN], f.b[I % C::FN], acc[I / C::FN][I % C::FN]);
+        if constexpr (I % GAP == 0 && I / GAP < C::LPS) issue_one<C, TAIL, I / GAP>(j, d, ks, stage);
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr ((C::FM * C::FN + GAP - 1) / GAP < C::LPS) {
+        static_for<(C::FM * C::FN + GAP - 1) / GAP, C::LPS>([&](auto q) {
+            issue_one<C, TAIL, decltype(q)::value>(j, d, ks, stage);
+        });
+    }
+}
+
 template <class C, bool TAIL, class Wait>
 __device__ __forceinline__ void issue_slab(const TileJob& j, const TileDma<C>& d, int ks, int stage, Wait& wait) {
     issue_b<C, TAIL>(j, d, ks, stage);
@@ -656,42 +753,74 @@ __device__ __forceinline__ void issue_slab(const TileJob& j, const TileDma<C>& d
 
 // The K loop of one tile over slabs ks0 .. ks1-1.  `wait(ks)` is called
 // (uniformly) before the A-operand DMA of slab ks -- the consumer's
-// dependency on its producers; the B-operand (weight) DMA of that slab is
-// issued before the wait.  Slab ks0 + i lives in stage i % NS; slabs ks0 ..
-// ks0+NS-2 are requested before the first step.  One step per slab ks
-// (stage st): once slab ks has landed and every wave is done with the
-// previous stage, refill that stage with slab ks+NS-1, read both half slabs
-// of stage st, and run the first half's MFMAs while the second half's reads
-// are still in flight.  A slab's DMA has NS-1 steps to land.  In the last
-// NS-2 steps no slab is requested and the barrier waits for every
-// outstanding one.  The branches in a step are wave-uniform and hold only
-// waits and DMA issues, so the accumulators stay in place.  (Requesting the
-// next slab's first half slab during the second half's MFMAs, with the
-// barrier between the two MFMA groups, measured 4-10% more cycles per tile.)
+// dependency on its producers.  Slab ks0 + i lives in stage i % NS; slabs
+// ks0 .. ks0+NS-2 are requested before the first step.  One step per slab
+// ks (stage st):
+//   barrier: slab ks has landed and every wave is done with the stage of
+//     slab ks-1, which now takes slab ks+NS-1;
+//   issue the reads of the first half slab (f0);
+//   [not SPREAD: issue the DMA of slab ks+NS-1 -- it overlaps the reads]
+//   wait for f0, then its MFMAs, with one read of the second half slab (f1)
+//   issued after each of the first NREAD of them;
+//   wait for f1, then its MFMAs [SPREAD: with the LPS DMA instructions of
+//   slab ks+NS-1 issued after every other one].
+// Issuing every wave's DMA in one group right after the barrier stalled the
+// waves on the full memory queue for a large part of the step (measured with
+// s_memtime around each phase); spread over the MFMAs the queue drains while
+// the matrix cores work.  In the SPREAD form the step has no branch between
+// the MFMAs: past the part's end the last slab is fetched again (into a stage
+// that is never read), so the DMA count and the waits stay fixed; the other
+// form skips those slabs and waits for every outstanding one instead.  (With
+// the next slab's first half read during the second half's MFMAs and the
+// barrier between the two MFMA groups, a step took 4-10% more cycles.)
 template <class C, int DT, bool TAIL, class Wait>
 __device__ __forceinline__ void tile_kloop(const TileJob& j, f32x4 (&acc)[C::FM][C::FN], Wait& wait) {
     const FragBase<C> fb = frag_base<C>();
     const TileDma<C> d = tile_dma<C>(j);
     const int ks0 = j.ks0, ks1 = j.ks1;
 #pragma unroll
-    for (int i = 0; i < C::NS - 1; ++i)
-        if (ks0 + i < ks1) issue_slab<C, TAIL, Wait>(j, d, ks0 + i, i, wait);
+    for (int i = 0; i < C::NS - 1; ++i) {
+        if constexpr (!C::SPREAD) {
+            if (ks0 + i < ks1) issue_slab<C, TAIL, Wait>(j, d, ks0 + i, i, wait);
+        } else {
+            if (ks0 + i < ks1) wait(ks0 + i);
+            const int kd = ks0 + i < ks1 ? ks0 + i : ks1 - 1;
+            static_for<0, C::LPS>([&](auto q) { issue_one<C, TAIL, decltype(q)::value>(j, d, kd, i); });
+        }
+    }
     int st = 0;
     for (int ks = ks0; ks < ks1; ++ks) {
         const int pv = st == 0 ? C::NS - 1 : st - 1;
-        if (ks + C::NS - 1 <= ks1) ring_barrier<C::LPS * (C::NS - 2)>();
-        else ring_barrier<0>();
-        if (ks + C::NS - 1 < ks1) issue_slab<C, TAIL, Wait>(j, d, ks + C::NS - 1, pv, wait);
+        const int kn = ks + C::NS - 1;
         Frags<C> f0, f1;
-        frag_load<C, 0>(fb, (uint32_t)st * C::STAGE, f0);
-        frag_load<C, 1>(fb, (uint32_t)st * C::STAGE, f1);
-        lgkm_wait<C::NREAD>();
+        if constexpr (!C::SPREAD) {
+            // request slab ks+NS-1 right after this slab's first fragment
+            // reads, once it is known to exist
+            if (kn <= ks1) ring_barrier<C::LPS * (C::NS - 2)>();
+            else ring_barrier<0>();
+            frag_load<C, 0>(fb, (uint32_t)st * C::STAGE, f0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (kn < ks1) issue_slab<C, TAIL, Wait>(j, d, kn, pv, wait);
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            // slab ks+NS-1 goes into the stage of slab ks-1, its DMA spread
+            // over the second half slab's MFMAs; past the part's end the
+            // last slab is fetched again (never read), which keeps the DMA
+            // count per step and the waits fixed and the MFMA groups free of
+            // branches
+            if (kn < ks1) wait(kn);
+            ring_barrier<C::LPS * (C::NS - 2)>();
+            frag_load<C, 0>(fb, (uint32_t)st * C::STAGE, f0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        lgkm_wait<0>();
         frag_pin(f0);
-        mfma_block<C, DT>(acc, f0);
+        mfma_block_reading<C, DT, 1>(acc, f0, fb, (uint32_t)st * C::STAGE, f1);
         __builtin_amdgcn_sched_barrier(0);
         lgkm_wait<0>();
         frag_pin(f1);
-        mfma_block<C, DT>(acc, f1);
+        if constexpr (!C::SPREAD) mfma_block<C, DT>(acc, f1);
+        else mfma_block_dma<C, DT, TAIL>(acc, f1, j, d, kn < ks1 ? kn : ks1 - 1, pv);
         __builtin_amdgcn_sched_barrier(0);
         st = st + 1 == C::NS ? 0 : st + 1;
     }
