@@ -89,6 +89,8 @@ struct mlp_chain {
     int forced_cfg;
     int forced_s1, forced_s2;   // 0 = planner's split
     int forced_grid;            // 0 = planner's persistent grid
+    int forced_order;           // -1 = planner's tile order
+    uint32_t order;             // bit 0 / 1: GEMM1 / GEMM2 tiles column-major in each XCD block
     CfgInfo ci;
     uint32_t Mt, N1t, N2t, T1, T2;
     uint32_t S1, S2, ksp1, ksp2;  // K split of GEMM1 / GEMM2 tiles
@@ -153,6 +155,17 @@ constexpr uint32_t MIN_SLABS_SHARED = 32;    // 2048 K-elements
 // several row blocks read each weight panel): on the LLaMA-65 and Llama-2
 // shards (K = 2752 and 3584 for GEMM2) shorter parts lost more to the fp32
 // partial sums than the split gained.
+// Tile order inside each XCD's block of the tile grid (bit 0: GEMM1, bit 1:
+// GEMM2; set = column-major).  Does not change any output element.  Row-major
+// for both GEMMs and every policy: on the GPT-3 shard, column-major GEMM2
+// tiles cut the fused run's speed by 6% at M=2048 (an XCD's first consumers
+// then need all of its row blocks, not just the first) and gained the
+// stream-ordered pair at most 2% at M=2048 while losing 4% at M=1024.
+uint32_t plan_order(int policy) {
+    (void)policy;
+    return 0u;
+}
+
 uint32_t plan_split(uint32_t tiles, uint32_t nks, int cus, int64_t M, uint32_t Mt, uint32_t wg_per_cu) {
     uint32_t s;
     if (M < 256 && Mt == 1) {
@@ -199,6 +212,7 @@ int apply_plan(mlp_chain* h, int cfg) {
     }
     h->ksp1 = (nks1 + h->S1 - 1) / h->S1;
     h->ksp2 = (nks2 + h->S2 - 1) / h->S2;
+    h->order = h->forced_order >= 0 ? (uint32_t)h->forced_order : plan_order(h->policy);
     h->occ = 0;
     h->grid = 0;
     if (h->policy != MLP_POLICY_STREAM_ORDERED) {
@@ -307,6 +321,7 @@ mlpc::ChainArgs make_args(const mlp_chain* h, const void* x, const void* w1, con
     a.T1 = h->T1;
     a.T2 = h->T2;
     a.rx = h->Mt >= 2 ? 2u : 1u;
+    a.order = h->order;
     a.ticket = h->ticket;
     a.flags = h->flags;
     a.rowcnt = h->rowcnt;
@@ -397,6 +412,7 @@ mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype
     h->forced_cfg = -1;
     h->forced_s1 = 0;
     h->forced_grid = 0;
+    h->forced_order = -1;
     h->forced_s2 = 0;
     h->spin_limit = DEFAULT_SPIN_LIMIT;
     h->skip_producer = mlpc::NO_SKIP;
@@ -532,6 +548,13 @@ int mlp_chain_debug_set_grid(mlp_chain_t h, int grid) {
     if (!h) return fail(MLP_EINVAL, "NULL handle");
     if (grid < 0) return fail(MLP_EINVAL, "grid must be >= 0, got %d", grid);
     h->forced_grid = grid;
+    return apply_plan(h, h->cfg);
+}
+
+int mlp_chain_debug_set_order(mlp_chain_t h, int order) {
+    if (!h) return fail(MLP_EINVAL, "NULL handle");
+    if (order < -1 || order > 3) return fail(MLP_EINVAL, "order must be -1 (planned) or 0..3, got %d", order);
+    h->forced_order = order;
     return apply_plan(h, h->cfg);
 }
 

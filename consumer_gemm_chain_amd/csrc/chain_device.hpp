@@ -70,6 +70,7 @@ struct ChainArgs {
     int act;
     uint32_t Mt, N1t, N2t, T1, T2;
     uint32_t rx;            // XCD grid rows (1, 2, 4 or 8; the grid is rx x 8/rx)
+    uint32_t order;         // bit 0 / bit 1: GEMM1 / GEMM2 tiles walked column-major in each XCD block
     uint32_t* ticket;       // 8 tile-queue counters (one per XCD) and an exit counter, 64 words apart;
                             // zero when a run starts (the last workgroup of a run resets them)
     uint32_t* flags;        // [Mt * N1t] ready epochs (tile_sync)
@@ -203,14 +204,18 @@ __device__ __forceinline__ uint32_t xcd_chunked(uint32_t b, uint32_t n) {
 }
 
 // XCD partition of a GEMM's Mt x Nt tile grid (S parts per tile): the 8
-// XCDs form an Rx x (8/Rx) grid, XCD x owns a contiguous block of row
-// blocks and column blocks, and walks it row-major with the parts of a tile
-// adjacent.  Both GEMMs use the same row split, so the consumers of a row
-// block sit on the XCDs whose producers complete it, and each row block is
-// finished early (row-major) for its consumers; a block's weight panels and
-// activation rows are shared in that XCD's L2.
+// XCDs form an Rx x (8/Rx) grid and XCD x owns a contiguous block of row
+// blocks and column blocks, walked with the parts of a tile adjacent, either
+// row-major or column-major (CM).  Both GEMMs use the same row split, so the
+// consumers of a row block sit on the XCDs whose producers complete it.  A
+// block's weight panels and activation rows are shared in that XCD's L2 by
+// the tiles that run there together: row-major finishes each row block
+// early (for its consumers); column-major makes the ~32 tiles an XCD runs at
+// once a (block rows) x (32 / block rows) patch, which shares more panels
+// per K slab than one row of the block and a bit (for a 4 x 24 block of
+// 256 x 128 tiles: 256 KB of distinct operands per slab instead of 448 KB).
 struct XcdBlock {
-    uint32_t r0, c0, nc, len;    // first row block, first column block, columns, items
+    uint32_t r0, c0, nr, nc, len;    // first row block, first column block, rows, columns, items
 };
 
 __device__ __forceinline__ XcdBlock xcd_block(uint32_t Mt, uint32_t Nt, uint32_t S, uint32_t Rx, uint32_t x) {
@@ -218,25 +223,30 @@ __device__ __forceinline__ XcdBlock xcd_block(uint32_t Mt, uint32_t Nt, uint32_t
     const uint32_t rx = x / Cx, cx = x % Cx;
     const uint32_t r0 = rx * Mt / Rx, r1 = (rx + 1) * Mt / Rx;
     const uint32_t c0 = cx * Nt / Cx, c1 = (cx + 1) * Nt / Cx;
-    return XcdBlock{r0, c0, c1 - c0, (r1 - r0) * (c1 - c0) * S};
+    return XcdBlock{r0, c0, r1 - r0, c1 - c0, (r1 - r0) * (c1 - c0) * S};
 }
 
 // Item c of XCD block b -> tile (row block, column block) and part.
-__device__ __forceinline__ void xcd_item(const XcdBlock& b, uint32_t S, uint32_t c, uint32_t& mb, uint32_t& nb,
-                                         uint32_t& part) {
+__device__ __forceinline__ void xcd_item(const XcdBlock& b, uint32_t S, bool cm, uint32_t c, uint32_t& mb,
+                                         uint32_t& nb, uint32_t& part) {
     part = c % S;
     const uint32_t tc = c / S;
-    mb = b.r0 + tc / b.nc;
-    nb = b.c0 + tc % b.nc;
+    if (cm) {
+        mb = b.r0 + tc % b.nr;
+        nb = b.c0 + tc / b.nr;
+    } else {
+        mb = b.r0 + tc / b.nc;
+        nb = b.c0 + tc % b.nc;
+    }
 }
 
 // Position p of the concatenation of the 8 XCD blocks -> tile and part.
-__device__ __forceinline__ void xcd_position(uint32_t Mt, uint32_t Nt, uint32_t S, uint32_t Rx, uint32_t p,
+__device__ __forceinline__ void xcd_position(uint32_t Mt, uint32_t Nt, uint32_t S, uint32_t Rx, bool cm, uint32_t p,
                                              uint32_t& mb, uint32_t& nb, uint32_t& part) {
     for (uint32_t x = 0; x < 8; ++x) {
         const XcdBlock b = xcd_block(Mt, Nt, S, Rx, x);
         if (p < b.len) {
-            xcd_item(b, S, p, mb, nb, part);
+            xcd_item(b, S, cm, p, mb, nb, part);
             return;
         }
         p -= b.len;

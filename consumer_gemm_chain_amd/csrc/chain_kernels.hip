@@ -50,7 +50,7 @@ __global__ __launch_bounds__(C::NT) void gemm1_act_kernel(ChainArgs a) {
     __shared__ uint32_t s_flag;
     NoWait w;
     uint32_t mb, nb, part;
-    xcd_position(a.Mt, a.N1t, a.S1, a.rx, xcd_chunked(blockIdx.x, a.T1 * a.S1), mb, nb, part);
+    xcd_position(a.Mt, a.N1t, a.S1, a.rx, a.order & 1u, xcd_chunked(blockIdx.x, a.T1 * a.S1), mb, nb, part);
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     const bool wrote = run_tile<C, DT, 1>(a, mb, nb, part, &s_flag, w);
     if (a.trace && threadIdx.x == 0) trace_item(a, (mb * a.N1t + nb) * a.S1 + part, t0, t0, wrote);
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(C::NT) void gemm2_kernel(ChainArgs a) {
     __shared__ uint32_t s_flag;
     NoWait w;
     uint32_t mb, nb, part;
-    xcd_position(a.Mt, a.N2t, a.S2, a.rx, xcd_chunked(blockIdx.x, a.T2 * a.S2), mb, nb, part);
+    xcd_position(a.Mt, a.N2t, a.S2, a.rx, (a.order >> 1) & 1u, xcd_chunked(blockIdx.x, a.T2 * a.S2), mb, nb, part);
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     const bool wrote = run_tile<C, DT, 2>(a, mb, nb, part, &s_flag, w);
     if (a.trace && threadIdx.x == 0)
@@ -148,10 +148,10 @@ __device__ __forceinline__ uint32_t queue_item(const ChainArgs& a, const XcdBloc
                                                uint32_t P1, uint32_t c) {
     uint32_t mb, nb, part;
     if (c < bp.len) {
-        xcd_item(bp, a.S1, c, mb, nb, part);
+        xcd_item(bp, a.S1, a.order & 1u, c, mb, nb, part);
         return (mb * a.N1t + nb) * a.S1 + part;
     }
-    xcd_item(bc, a.S2, c - bp.len, mb, nb, part);
+    xcd_item(bc, a.S2, (a.order >> 1) & 1u, c - bp.len, mb, nb, part);
     return P1 + (mb * a.N2t + nb) * a.S2 + part;
 }
 
@@ -165,7 +165,7 @@ constexpr uint32_t NO_ITEM = 0xffffffffu;
 __device__ __forceinline__ uint32_t draw_item(const ChainArgs& a, Queues& q) {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t x = (q.own + lane) & 7;
-    XcdBlock bp{0, 0, 1, 0}, bc{0, 0, 1, 0};
+    XcdBlock bp{0, 0, 1, 1, 0}, bc{0, 0, 1, 1, 0};
     uint32_t len = 0, first = 0;
     if (lane < 8) {
         bp = xcd_block(a.Mt, a.N1t, a.S1, a.rx, x);

@@ -28,7 +28,7 @@ EXPORTS = ("mlp_chain_create", "mlp_chain_run", "mlp_chain_destroy", "mlp_chain_
            "mlp_chain_status", "mlp_chain_last_error", "mlp_chain_info",
            "mlp_chain_debug_set_spin_limit", "mlp_chain_debug_skip_producer",
            "mlp_chain_debug_set_config", "mlp_chain_debug_set_split", "mlp_chain_debug_set_grid",
-           "mlp_chain_debug_set_trace", "mlp_chain_debug_read_intermediate")
+           "mlp_chain_debug_set_order", "mlp_chain_debug_set_trace", "mlp_chain_debug_read_intermediate")
 
 INFO_FIELDS = ("BM", "BN1", "BN2", "BK", "Mt", "N1t", "N2t", "T1", "T2", "grid", "wg_per_cu",
                "threads", "cus", "epoch", "config", "workspace_bytes", "S1", "S2", "ksp1", "ksp2")
@@ -77,6 +77,8 @@ def load_library(path: str | None = None):
     lib.mlp_chain_debug_set_split.restype = ci
     lib.mlp_chain_debug_set_grid.argtypes = [vp, ci]
     lib.mlp_chain_debug_set_grid.restype = ci
+    lib.mlp_chain_debug_set_order.argtypes = [vp, ci]
+    lib.mlp_chain_debug_set_order.restype = ci
     lib.mlp_chain_debug_set_trace.argtypes = [vp, vp]
     lib.mlp_chain_debug_set_trace.restype = ci
     lib.mlp_chain_debug_read_intermediate.argtypes = [vp, vp, vp]
@@ -151,6 +153,10 @@ def mlp_chain_debug_set_split(h: int, s1: int, s2: int) -> int:
 
 def mlp_chain_debug_set_grid(h: int, grid: int) -> int:
     return _check(load_library().mlp_chain_debug_set_grid(h, int(grid)))
+
+
+def mlp_chain_debug_set_order(h: int, order: int) -> int:
+    return _check(load_library().mlp_chain_debug_set_order(h, int(order)))
 
 
 def mlp_chain_debug_set_trace(h: int, buffer: int | None) -> int:
@@ -235,6 +241,9 @@ class MlpChain:
 
     def set_grid(self, grid: int):
         mlp_chain_debug_set_grid(self.h, grid)
+
+    def set_order(self, order: int):
+        mlp_chain_debug_set_order(self.h, order)
 
     def set_spin_limit(self, limit: int):
         mlp_chain_debug_set_spin_limit(self.h, limit)

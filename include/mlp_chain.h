@@ -164,6 +164,15 @@ int mlp_chain_debug_set_split(mlp_chain_t h, int s1, int s2);
  * MLP_EINVAL for a NULL handle or a negative value. */
 int mlp_chain_debug_set_grid(mlp_chain_t h, int grid);
 
+/* Override the order in which each XCD walks its block of the tile grid:
+ * bit 0 for GEMM1, bit 1 for GEMM2, set = column-major (the tiles an XCD
+ * runs together form a patch of rows x columns rather than a run along one
+ * row); -1 restores the planner's choice.  The order changes which tiles
+ * share an XCD's L2 at a time and, for the fused policies, when each row
+ * block of T completes -- never any output value.  Takes effect on the next
+ * run.  Returns MLP_EINVAL for a NULL handle or a value outside -1..3. */
+int mlp_chain_debug_set_order(mlp_chain_t h, int order);
+
 /* Timeline trace of every policy (measurement of the non-overlapped share,
  * as the FLUX summary card advises in Interesting ideas, I3):
  * `buffer` is a DEVICE buffer of 4 * (T1*S1 + T2*S2) uint64 (see

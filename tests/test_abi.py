@@ -58,6 +58,7 @@ def test_null_handle_entry_points():
     assert lib.mlp_chain_debug_set_config(None, 0) == mc.MLP_EINVAL
     assert lib.mlp_chain_debug_set_split(None, 0, 0) == mc.MLP_EINVAL
     assert lib.mlp_chain_debug_set_grid(None, 0) == mc.MLP_EINVAL
+    assert lib.mlp_chain_debug_set_order(None, 0) == mc.MLP_EINVAL
     arr = (ctypes.c_int64 * 16)()
     assert lib.mlp_chain_info(None, arr, 16) == mc.MLP_EINVAL
 

@@ -293,3 +293,35 @@ def test_tile_configs_agree_bitwise(act, dtype):
                 if ref is None:
                     ref = y
                 assert np.array_equal(y, ref), (cfg, pol, s1, s2)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("policy", ["stream_ordered", "row_sync", "tile_sync"])
+def test_tile_orders_agree_bitwise(oracle_mod, policy):
+    """The order in which each XCD walks its tiles (row- or column-major, per
+    GEMM) moves no output bit, with and without a K split; checked on a
+    shape with several row blocks per XCD block and ragged edges."""
+    import torch
+    from consumer_gemm_chain_amd.mlp_chain import MlpChain
+    from tests._helpers import empty_dev, from_dev
+    M, H, I, act, dtype = 1000, 1544, 1288, "swiglu", "f16"
+    x, w1, w2 = _case(M, H, I, act, dtype, seed=47)
+    print(f"case M={M} H={H} I={I} act={act} dtype={dtype} policy={policy}", flush=True)
+    y_ref = oracle_mod.mlp_chain(x, w1, w2, act, dtype)
+    dev = (to_dev(x, dtype), to_dev(w1, dtype), to_dev(w2, dtype))
+    for split in ((1, 1), (2, 3)):
+        ref = None
+        for order in (0, 1, 2, 3, -1):
+            with MlpChain(M, H, I, act, dtype, policy) as ch:
+                ch.set_config(2)
+                ch.set_split(*split)
+                ch.set_order(order)
+                out = empty_dev((M, H), dtype)
+                ch.run(*dev, out)
+                torch.cuda.synchronize()
+                assert ch.status() == 0
+                y = from_dev(out)
+            if ref is None:
+                ref = y
+                check_against_oracle(y, y_ref, dtype, f"{policy} order {order} split {split}")
+            assert np.array_equal(y, ref), (policy, order, split)
