@@ -65,17 +65,15 @@ constexpr int CFG_DEEP = 4;     // 64 x 128, four stages, one workgroup per CU
 constexpr int CFG_WIDE = 3;     // 256 x 128, eight waves, three stages
 
 int plan_config(int64_t M, int64_t H, int64_t I, int act, int policy, int cus) {
+    (void)policy;
     if (M <= 16) return 0;
     if (M <= 256) {
         const int64_t mt = (M + 63) / 64;
         const int64_t t1 = mt * ((I + (act == MLP_ACT_SWIGLU ? 63 : 127)) / (act == MLP_ACT_SWIGLU ? 64 : 128));
         const int64_t t2 = mt * ((H + 127) / 128);
-        return t1 <= cus && t2 <= cus ? CFG_DEEP : 1;
+        if (t1 <= cus && t2 <= cus) return CFG_DEEP;
     }
-    const int64_t bn1 = act == MLP_ACT_SWIGLU ? 64 : 128;     // producer output columns of the wide config
-    const int64_t t1 = ((M + 255) / 256) * ((I + bn1 - 1) / bn1);
-    const int64_t need = policy == MLP_POLICY_STREAM_ORDERED ? cus : 3 * (int64_t)cus / 4;
-    return t1 >= need ? CFG_WIDE : 2;
+    return CFG_WIDE;
 }
 
 }  // namespace
@@ -168,7 +166,7 @@ uint32_t plan_order(int policy) {
 
 uint32_t plan_split(uint32_t tiles, uint32_t nks, int cus, int64_t M, uint32_t Mt, uint32_t wg_per_cu) {
     uint32_t s;
-    if (M < 256 && Mt == 1) {
+    if (Mt == 1) {
         s = (3u * (uint32_t)cus / 4u + tiles / 2) / tiles;
     } else if (M < 256) {
         s = (uint32_t)cus / tiles;

@@ -5,10 +5,10 @@
 
 #define MLPC_CONFIGS(X)                                                                        \
     X(0, 16, 64, 1, 2, 4, 2)     /* M <= 16: weight streaming, four stages */                 \
-    X(1, 64, 128, 2, 2, 2, 2)    /* M <= 256: two stages, up to three workgroups per CU */     \
-    X(2, 128, 128, 2, 2, 2, 2)   /* large M: two stages, two workgroups per CU */              \
-    X(3, 256, 128, 4, 2, 3, 2)   /* large M: eight waves of 64x64, three stages, one WG/CU */   \
-    X(4, 64, 128, 2, 2, 4, 1)    /* M <= 256: four stages, one workgroup per CU */            \
+    X(1, 64, 128, 2, 2, 2, 2)    /* measurements: two stages, up to three workgroups per CU */ \
+    X(2, 128, 128, 2, 2, 2, 2)   /* measurements: two stages, two workgroups per CU */         \
+    X(3, 256, 128, 4, 2, 3, 2)   /* M > 16 beyond one wave of 64x128 tiles: eight waves */      \
+    X(4, 64, 128, 2, 2, 4, 1)    /* M <= 256, one wave of tiles: four stages, one WG per CU */ \
     X(5, 256, 128, 2, 2, 3, 1)   /* measurements: four waves of 128x64 */                     \
     X(6, 128, 256, 2, 4, 3, 2)   /* measurements: eight waves of 64x64, 128 x 256 */
 
