@@ -110,7 +110,7 @@ struct TileCfg {
     static constexpr int FM = WTM / 16, FN = WTN / 16;
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16x16");
     static_assert(FN % 2 == 0, "SwiGLU tiles pair gate/up fragments within a wave");
-    static_assert(NS >= 2 && NS <= 4, "2 to 4 LDS stages");
+    static_assert(NS >= 2 && NS <= 14, "2 to 14 LDS stages");
     static constexpr int A_BYTES = BM * BK * 2;          // A slab: BM rows x 128 bytes
     static constexpr int B_BYTES = BK * BN * 2;          // B slab: 64 k-rows x BN columns
     static constexpr int STAGE = A_BYTES + B_BYTES;
@@ -171,14 +171,24 @@ __device__ __forceinline__ uint16_t to_storage(float v) {
     }
 }
 
+// GeLU, tanh form: 0.5 h (1 + tanh u) with u = sqrt(2/pi) (h + 0.044715 h^3),
+// evaluated as the identical h / (1 + exp(-2u)) through the hardware 2^x
+// (v_exp_f32) and reciprocal (v_rcp_f32), about 1 ulp each -- a few fp32
+// ulps in all, far below the rounding to the storage dtype that follows.
+// Large negative u gives exp = inf and the result -0, as the tanh form does.
 __device__ __forceinline__ float gelu_tanh(float h) {
     const float c = 0.7978845608028654f;   // sqrt(2/pi)
     const float k = 0.044715f;
-    float inner = c * (h + k * (h * h * h));
-    return 0.5f * h * (1.0f + tanhf(inner));
+    const float u = c * (h + k * (h * h * h));
+    const float e = __builtin_amdgcn_exp2f(u * -2.8853900817779268f);   // exp(-2u) = 2^(-2u log2 e)
+    return h * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+// SiLU g / (1 + exp(-g)), through the same hardware 2^x and reciprocal.
+__device__ __forceinline__ float silu(float g) {
+    const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);   // exp(-g)
+    return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
 
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
     return *reinterpret_cast<const u32x4*>(p);
@@ -867,6 +877,34 @@ __device__ __forceinline__ void tile_epilogue(const f32x4 (&acc)[C::FM][C::FN], 
     uint16_t* s = reinterpret_cast<uint16_t*>(smem);
     const int width = inter ? C::BN / 2 : C::BN;
     const int cpr = width / 8;                    // 16-byte chunks per row
+    // Activation and rounding of every fragment first, in every wave (the
+    // staging passes below only cover some waves' rows each), kept as packed
+    // 16-bit pairs: element i of fragment f in half i / 2 of pk[f][i / 2].
+    constexpr int NV = C::FN;                     // value fragments per row (halved for SwiGLU)
+    uint32_t pk[C::FM][NV][2];
+#pragma unroll
+    for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < NV; ++fn)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t lo = 0, hi = 0;
+                if (inter) {
+                    if (fn < NV / 2) {
+                        lo = to_storage<DT>(silu(acc[fm][2 * fn][2 * h]) * acc[fm][2 * fn + 1][2 * h]);
+                        hi = to_storage<DT>(silu(acc[fm][2 * fn][2 * h + 1]) * acc[fm][2 * fn + 1][2 * h + 1]);
+                    }
+                } else {
+                    float v0 = acc[fm][fn][2 * h], v1 = acc[fm][fn][2 * h + 1];
+                    if (act == ACT_GELU_TANH) {
+                        v0 = gelu_tanh(v0);
+                        v1 = gelu_tanh(v1);
+                    }
+                    lo = to_storage<DT>(v0);
+                    hi = to_storage<DT>(v1);
+                }
+                pk[fm][fn][h] = lo | (hi << 16);
+            }
 #pragma unroll
     for (int pass = 0; pass < C::EPI_PASSES; ++pass) {
         const int r0 = pass * C::EPI_ROWS;
@@ -874,27 +912,17 @@ __device__ __forceinline__ void tile_epilogue(const f32x4 (&acc)[C::FM][C::FN], 
         for (int fm = 0; fm < C::FM; ++fm) {
             const int rbase = wm * C::WTM + fm * 16;          // wave-uniform
             if (rbase < r0 || rbase >= r0 + C::EPI_ROWS) continue;
-            if (inter) {
+            const int nf = inter ? NV / 2 : NV;
 #pragma unroll
-                for (int fn = 0; fn < C::FN; fn += 2)
+            for (int fn = 0; fn < NV; ++fn) {
+                if (fn >= nf) continue;
+                const int col = inter ? (wn * C::WTN + 2 * fn * 16) / 2 + (lane & 15)
+                                      : wn * C::WTN + fn * 16 + (lane & 15);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float v = silu(acc[fm][fn][i]) * acc[fm][fn + 1][i];
-                        const int row = rbase - r0 + (lane >> 4) * 4 + i;
-                        const int col = (wn * C::WTN + fn * 16) / 2 + (lane & 15);
-                        s[row * LD + col] = to_storage<DT>(v);
-                    }
-            } else {
-#pragma unroll
-                for (int fn = 0; fn < C::FN; ++fn)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float v = acc[fm][fn][i];
-                        if (act == ACT_GELU_TANH) v = gelu_tanh(v);
-                        const int row = rbase - r0 + (lane >> 4) * 4 + i;
-                        const int col = wn * C::WTN + fn * 16 + (lane & 15);
-                        s[row * LD + col] = to_storage<DT>(v);
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    const int row = rbase - r0 + (lane >> 4) * 4 + i;
+                    s[row * LD + col] = (uint16_t)(pk[fm][fn][i >> 1] >> (16 * (i & 1)));
+                }
             }
         }
         lds_barrier();
@@ -974,17 +1002,28 @@ __device__ __forceinline__ bool split_reduce(f32x4 (&acc)[C::FM][C::FN], float* 
     }
     __syncthreads();
     if (__builtin_amdgcn_readfirstlane(*s_flag) == 0) return false;
+    // Sum in part order (p = 0, 1, .., S-1), every term read back from the
+    // partials (this part's own included: its stores completed before the
+    // release above, and they hold exactly the register values), so the
+    // accumulators are free to hold the sum.  Every fragment's load of one
+    // part is issued before any of them is used: a part costs one memory
+    // latency, not one per fragment.
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) {
-            f32x4 sum = s == 0 ? acc[fm][fn] : base[(size_t)(fm * C::FN + fn) * C::NT + tid];
-            for (uint32_t p = 1; p < S; ++p) {
-                const f32x4 v = p == s ? acc[fm][fn] : base[((size_t)p * NF + fm * C::FN + fn) * C::NT + tid];
-                sum = sum + v;
-            }
-            acc[fm][fn] = sum;
-        }
+        for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = base[(size_t)(fm * C::FN + fn) * C::NT + tid];
+    for (uint32_t p = 1; p < S; ++p) {
+        const f32x4* src = base + (size_t)p * NF * C::NT + tid;
+        f32x4 v[C::FM][C::FN];
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn) v[fm][fn] = src[(size_t)(fm * C::FN + fn) * C::NT];
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = acc[fm][fn] + v[fm][fn];
+    }
     return true;
 }
 
