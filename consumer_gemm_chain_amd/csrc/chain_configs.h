@@ -10,10 +10,7 @@
     X(3, 256, 128, 4, 2, 3, 2)   /* M > 16 beyond one wave of 64x128 tiles: eight waves */      \
     X(4, 64, 128, 2, 2, 4, 1)    /* M <= 256, one wave of tiles: four stages, one WG per CU */ \
     X(5, 256, 128, 2, 2, 3, 1)   /* measurements: four waves of 128x64 */                     \
-    X(6, 128, 256, 2, 4, 3, 2)   /* measurements: eight waves of 64x64, 128 x 256 */          \
-    X(7, 16, 64, 1, 2, 8, 2)     /* measurements: weight streaming, eight stages */           \
-    X(8, 16, 64, 1, 2, 12, 2)    /* measurements: weight streaming, twelve stages */          \
-    X(9, 64, 128, 2, 2, 6, 1)    /* measurements: 64x128, six stages */
+    X(6, 128, 256, 2, 4, 3, 2)   /* measurements: eight waves of 64x64, 128 x 256 */
 
 #define MLPC_COUNT_CFG(id, ...) +1
 constexpr int MLPC_NUM_CONFIGS = 0 MLPC_CONFIGS(MLPC_COUNT_CFG);
