@@ -63,9 +63,9 @@ uint32_t cdiv(int64_t a, int64_t b) { return (uint32_t)((a + b - 1) / b); }
 //     the producer kernel's last wave).
 constexpr int CFG_DEEP = 4;     // 64 x 128, four stages, one workgroup per CU
 constexpr int CFG_WIDE = 3;     // 256 x 128, eight waves, three stages
+constexpr int CFG_BIG = 7;      // 256 x 256, eight waves of 128 x 64, two stages
 
 int plan_config(int64_t M, int64_t H, int64_t I, int act, int policy, int cus) {
-    (void)policy;
     if (M <= 16) return 0;
     if (M <= 256) {
         const int64_t mt = (M + 63) / 64;
@@ -73,6 +73,13 @@ int plan_config(int64_t M, int64_t H, int64_t I, int act, int policy, int cus) {
         const int64_t t2 = mt * ((H + 127) / 128);
         if (t1 <= cus && t2 <= cus) return CFG_DEEP;
     }
+    // 256 x 256 tiles once they fill the GPU: for the stream-ordered pair when
+    // GEMM2 has a wave of them, for the fused policies when GEMM1 has 7/8 of
+    // one (with fewer producer tiles the consumers start early and wait)
+    const int64_t mt = (M + 255) / 256;
+    const int64_t t1 = mt * ((I + (act == MLP_ACT_SWIGLU ? 127 : 255)) / (act == MLP_ACT_SWIGLU ? 128 : 256));
+    const int64_t t2 = mt * ((H + 255) / 256);
+    if (policy == MLP_POLICY_STREAM_ORDERED ? t2 >= cus : 8 * t1 >= 7 * (int64_t)cus) return CFG_BIG;
     return CFG_WIDE;
 }
 

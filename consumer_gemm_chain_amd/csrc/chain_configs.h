@@ -10,7 +10,8 @@
     X(3, 256, 128, 4, 2, 3, 2)   /* M > 16 beyond one wave of 64x128 tiles: eight waves */      \
     X(4, 64, 128, 2, 2, 4, 1)    /* M <= 256, one wave of tiles: four stages, one WG per CU */ \
     X(5, 256, 128, 2, 2, 3, 1)   /* measurements: four waves of 128x64 */                     \
-    X(6, 128, 256, 2, 4, 3, 2)   /* measurements: eight waves of 64x64, 128 x 256 */
+    X(6, 128, 256, 2, 4, 3, 2)   /* measurements: eight waves of 64x64, 128 x 256 */          \
+    X(7, 256, 256, 2, 4, 2, 2)   /* large M once these tiles fill the GPU: eight waves of 128x64 */
 
 #define MLPC_COUNT_CFG(id, ...) +1
 constexpr int MLPC_NUM_CONFIGS = 0 MLPC_CONFIGS(MLPC_COUNT_CFG);

@@ -672,20 +672,86 @@ __device__ __forceinline__ void frag_read_one(const FragBase<C>& fb, uint32_t so
     }
 }
 
-// The MFMAs of fragments f, with the reads of half slab KK into g issued one
-// after each of the first NREAD MFMAs.
+// Order of the NREAD reads of the second half slab (frag_read_one numbering:
+// R < FM is A fragment R, the rest the B halves) among the first half's
+// MFMAs (row fm = MFMAs fm*FN .. fm*FN+FN-1): A fragment fm right after the
+// last MFMA of row fm -- the moment the first half's A fragment fm dies, so
+// the compiler can give the new one the same registers -- and the B halves
+// in the other slots, in order; B halves with no slot follow the block.
+template <class C>
+struct ReadPlan {
+    int after[C::FM * C::FN];   // read issued after MFMA I, or -1
+    int tail[C::NREAD];         // reads issued after the block
+    int ntail;
+    int pos[C::NREAD];          // issue position of each read
+};
+
+template <class C>
+constexpr ReadPlan<C> read_plan() {
+    ReadPlan<C> p{};
+    int nb = 0, n = 0;
+    for (int i = 0; i < C::FM * C::FN; ++i) {
+        int r = -1;
+        if (i % C::FN == C::FN - 1) r = i / C::FN;
+        else if (nb < 2 * C::FN) r = C::FM + nb++;
+        p.after[i] = r;
+        if (r >= 0) p.pos[r] = n++;
+    }
+    p.ntail = 0;
+    while (nb < 2 * C::FN) {
+        p.tail[p.ntail++] = C::FM + nb;
+        p.pos[C::FM + nb++] = n++;
+    }
+    return p;
+}
+
+// Reads of the second half slab still allowed in flight when row fm of its
+// MFMAs starts (it needs A fragment fm and every B half).
+template <class C>
+constexpr int rows_wait(int fm) {
+    constexpr ReadPlan<C> p = read_plan<C>();
+    int last = p.pos[fm];
+    for (int b = 0; b < 2 * C::FN; ++b)
+        if (p.pos[C::FM + b] > last) last = p.pos[C::FM + b];
+    return C::NREAD - 1 - last;
+}
+
+// The MFMAs of fragments f, with the reads of half slab KK into g issued
+// among them in read_plan order.
 template <class C, int DT, int KK>
 __device__ __forceinline__ void mfma_block_reading(f32x4 (&acc)[C::FM][C::FN], const Frags<C>& f,
                                                    const FragBase<C>& fb, uint32_t so, Frags<C>& g) {
+    constexpr ReadPlan<C> plan = read_plan<C>();
     static_for<0, C::FM * C::FN>([&](auto i) {
         constexpr int I = decltype(i)::value;
         acc[I / C::FN][I % C::FN] = mfma16x16x32<DT>(f.a[I / C::FN], f.b[I % C::FN], acc[I / C::FN][I % C::FN]);
-        if constexpr (I < C::NREAD) frag_read_one<C, KK, I>(fb, so, g);
+        if constexpr (plan.after[I] >= 0) frag_read_one<C, KK, plan.after[I]>(fb, so, g);
         __builtin_amdgcn_sched_barrier(0);
     });
-    if constexpr (C::FM * C::FN < C::NREAD) {
-        static_for<C::FM * C::FN, C::NREAD>([&](auto i) { frag_read_one<C, KK, decltype(i)::value>(fb, so, g); });
+    static_for<0, plan.ntail>([&](auto t) { frag_read_one<C, KK, plan.tail[decltype(t)::value]>(fb, so, g); });
+}
+
+// Before the first MFMA of row fm of fragments g (read by
+// mfma_block_reading): wait for what that row needs and make it available.
+template <class C, int FMROW>
+__device__ __forceinline__ void rows_ready(Frags<C>& g) {
+    lgkm_wait<rows_wait<C>(FMROW)>();
+    pin(g.a[FMROW]);
+    if constexpr (FMROW == 0) {
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) pin(g.b[fn]);
     }
+}
+
+// The MFMAs of fragments g as they arrive (row by row).
+template <class C, int DT>
+__device__ __forceinline__ void mfma_block_rows(f32x4 (&acc)[C::FM][C::FN], Frags<C>& g) {
+    static_for<0, C::FM * C::FN>([&](auto i) {
+        constexpr int I = decltype(i)::value;
+        if constexpr (I % C::FN == 0) rows_ready<C, I / C::FN>(g);
+        acc[I / C::FN][I % C::FN] = mfma16x16x32<DT>(g.a[I / C::FN], g.b[I % C::FN], acc[I / C::FN][I % C::FN]);
+        __builtin_amdgcn_sched_barrier(0);
+    });
 }
 
 // Wait until at most `n` DMA instructions of this wave are outstanding and
@@ -748,11 +814,12 @@ __device__ __forceinline__ void issue_one(const TileJob& j, const TileDma<C>& d,
 // `stage`) issued one after every other MFMA, so that the DMA of all waves
 // is spread over the step instead of queueing up in one burst.
 template <class C, int DT, bool TAIL>
-__device__ __forceinline__ void mfma_block_dma(f32x4 (&acc)[C::FM][C::FN], const Frags<C>& f,
+__device__ __forceinline__ void mfma_block_dma(f32x4 (&acc)[C::FM][C::FN], Frags<C>& f,
                                                const TileJob& j, const TileDma<C>& d, int ks, int stage) {
     constexpr int GAP = (C::FM * C::FN) / C::LPS >= 2 ? 2 : 1;
     static_for<0, C::FM * C::FN>([&](auto i) {
         constexpr int I = decltype(i)::value;
+        if constexpr (I % C::FN == 0) rows_ready<C, I / C::FN>(f);
         acc[I / C::FN][I % C::FN] = mfma16x16x32<DT>(f.a[I / C::FN], f.b[I % C::FN], acc[I / C::FN][I % C::FN]);
         if constexpr (I % GAP == 0 && I / GAP < C::LPS) issue_one<C, TAIL, I / GAP>(j, d, ks, stage);
         __builtin_amdgcn_sched_barrier(0);
@@ -837,9 +904,7 @@ __device__ __forceinline__ void tile_kloop(const TileJob& j, f32x4 (&acc)[C::FM]
         frag_pin(f0);
         mfma_block_reading<C, DT, 1>(acc, f0, fb, (uint32_t)st * C::STAGE, f1);
         __builtin_amdgcn_sched_barrier(0);
-        lgkm_wait<0>();
-        frag_pin(f1);
-        if constexpr (!C::SPREAD) mfma_block<C, DT>(acc, f1);
+        if constexpr (!C::SPREAD) mfma_block_rows<C, DT>(acc, f1);
         else mfma_block_dma<C, DT, TAIL>(acc, f1, j, d, kn < ks1 ? kn : ks1 - 1, pv);
         __builtin_amdgcn_sched_barrier(0);
         st = st + 1 == C::NS ? 0 : st + 1;
@@ -1006,23 +1071,30 @@ __device__ __forceinline__ bool split_reduce(f32x4 (&acc)[C::FM][C::FN], float* 
     // partials (this part's own included: its stores completed before the
     // release above, and they hold exactly the register values), so the
     // accumulators are free to hold the sum.  Every fragment's load of one
-    // part is issued before any of them is used: a part costs one memory
-    // latency, not one per fragment.
+    // part (chunk) is issued before any of them is used: a part costs one or
+    // two memory latencies, not one per fragment.
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = base[(size_t)(fm * C::FN + fn) * C::NT + tid];
+    // (in row chunks of at most 16 fragments, so the loaded values take at
+    // most 64 registers beside the accumulators)
+    constexpr int RC = 16 / C::FN < 1 ? 1 : (16 / C::FN < C::FM ? 16 / C::FN : C::FM);
+    static_assert(C::FM % RC == 0, "row chunks");
     for (uint32_t p = 1; p < S; ++p) {
         const f32x4* src = base + (size_t)p * NF * C::NT + tid;
-        f32x4 v[C::FM][C::FN];
 #pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
+        for (int r0 = 0; r0 < C::FM; r0 += RC) {
+            f32x4 v[RC][C::FN];
 #pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn) v[fm][fn] = src[(size_t)(fm * C::FN + fn) * C::NT];
+            for (int fm = 0; fm < RC; ++fm)
 #pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
+                for (int fn = 0; fn < C::FN; ++fn) v[fm][fn] = src[(size_t)((r0 + fm) * C::FN + fn) * C::NT];
 #pragma unroll
-            for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = acc[fm][fn] + v[fm][fn];
+            for (int fm = 0; fm < RC; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < C::FN; ++fn) acc[r0 + fm][fn] = acc[r0 + fm][fn] + v[fm][fn];
+        }
     }
     return true;
 }
