@@ -46,43 +46,6 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 uint32_t cdiv(int64_t a, int64_t b) { return (uint32_t)((a + b - 1) / b); }
 
-// Planner.  Tile configurations (chain_configs.h), chosen by M and tile
-// counts; crossovers measured on the GPT-3, LLaMA-65, Llama-2 and 8192^3
-// shards for M in 1..2048:
-//   * M <= 16: 16 x 64 tiles, four LDS stages (weight streaming);
-//   * M <= 256: 64 x 128 tiles -- with four stages and one workgroup per CU
-//     (three slabs of weights in flight per CU) when each GEMM has at most
-//     one tile per CU, else with two stages and up to three workgroups per
-//     CU;
-//   * above: 128 x 128 tiles with two workgroups per CU, or 256 x 128 tiles
-//     with one workgroup of eight waves per CU (about 5% more matrix-core
-//     throughput per CU, but half as many tiles) once there are enough of
-//     those tiles: for the stream-ordered pair when GEMM1 alone fills a wave
-//     of them, for the fused policies when it fills three quarters of a wave
-//     (the consumer tiles fill the rest -- the CuSync README's point about
-//     the producer kernel's last wave).
-constexpr int CFG_DEEP = 4;     // 64 x 128, four stages, one workgroup per CU
-constexpr int CFG_WIDE = 3;     // 256 x 128, eight waves, three stages
-constexpr int CFG_BIG = 7;      // 256 x 256, eight waves of 128 x 64, two stages
-
-int plan_config(int64_t M, int64_t H, int64_t I, int act, int policy, int cus) {
-    if (M <= 16) return 0;
-    if (M <= 256) {
-        const int64_t mt = (M + 63) / 64;
-        const int64_t t1 = mt * ((I + (act == MLP_ACT_SWIGLU ? 63 : 127)) / (act == MLP_ACT_SWIGLU ? 64 : 128));
-        const int64_t t2 = mt * ((H + 127) / 128);
-        if (t1 <= cus && t2 <= cus) return CFG_DEEP;
-    }
-    // 256 x 256 tiles once they fill the GPU: for the stream-ordered pair when
-    // GEMM2 has a wave of them, for the fused policies when GEMM1 has 7/8 of
-    // one (with fewer producer tiles the consumers start early and wait)
-    const int64_t mt = (M + 255) / 256;
-    const int64_t t1 = mt * ((I + (act == MLP_ACT_SWIGLU ? 127 : 255)) / (act == MLP_ACT_SWIGLU ? 128 : 256));
-    const int64_t t2 = mt * ((H + 255) / 256);
-    if (policy == MLP_POLICY_STREAM_ORDERED ? t2 >= cus : 8 * t1 >= 7 * (int64_t)cus) return CFG_BIG;
-    return CFG_WIDE;
-}
-
 }  // namespace
 
 struct mlp_chain {
@@ -189,6 +152,120 @@ uint32_t plan_split(uint32_t tiles, uint32_t nks, int cus, int64_t M, uint32_t M
     return (nks + ksp - 1) / ksp;
 }
 
+// Planner.  Tile configurations (chain_configs.h), chosen by M and tile
+// counts; crossovers measured on the GPT-3, LLaMA-65, Llama-2 and 8192^3
+// shards for M in 1..8192:
+//   * M <= 16: 16 x 64 tiles, four LDS stages (weight streaming);
+//   * M <= 256 while each GEMM has at most one 64 x 128 tile per CU: those
+//     tiles with four stages and one workgroup per CU (three slabs of
+//     weights in flight per CU);
+//   * otherwise 256 x 128 tiles (eight waves of 64 x 64, three stages) or
+//     256 x 256 tiles (eight waves of 128 x 64, two stages: a third fewer
+//     operand bytes per MFMA) once there are enough of those: for the
+//     stream-ordered pair when GEMM2 has a wave of them, for the fused
+//     policies when GEMM1 fills 7/8 of a wave (with fewer producer tiles the
+//     consumers start early and wait);
+//   * except where GEMM1 is split in two for the fused policies (below).
+constexpr int CFG_SMALL = 0;    // 16 x 64, four stages
+constexpr int CFG_DEEP = 4;     // 64 x 128, four stages, one workgroup per CU
+constexpr int CFG_WIDE = 3;     // 256 x 128, eight waves, three stages
+constexpr int CFG_BIG = 7;      // 256 x 256, eight waves of 128 x 64, two stages
+
+// Fused split of GEMM1.  When GEMM1's unsplit tiles make more than half a
+// wave and at most one, every producer tile runs at once, all of them finish
+// together, and the CUs without one idle until then (each consumer reads a
+// whole row block of T).  Split in two, the producer parts make 1.5 waves of
+// half-length items and the consumers of the first completed row blocks
+// fill the last half wave: the stream-ordered pair's GEMM1 cannot do that
+// (two rounds of half-length parts take as long as one of whole tiles).  It
+// pays only when each part keeps at least MIN_SLABS_FUSED_SPLIT slabs, so
+// that the fp32 partials and the reduction stay small against the K loop:
+// on the GPT-3 shard (H = 12288, 96-slab parts) the fused run took 323 us
+// instead of 370 at M = 1024 and 578 instead of 615 at M = 2048; on the
+// LLaMA-65 and Llama-2 shards (H = 8192, 64-slab parts) it lost 5-15%.  The
+// split is shared by every policy (bit-identical outputs), so the
+// stream-ordered pair runs it too, in its own best configuration for it.
+constexpr uint32_t MIN_SLABS_FUSED_SPLIT = 96;
+
+struct Tiling {
+    uint32_t mt, t1, t2;    // row blocks, GEMM1 tiles, GEMM2 tiles
+    uint32_t wg;            // workgroups per CU the configuration's LDS ring allows
+};
+
+Tiling tiling(int64_t M, int64_t H, int64_t I, int act, int cfg) {
+    const CfgInfo c = mlpc_config_info(cfg);
+    const uint32_t mt = cdiv(M, c.BM);
+    return {mt, mt * cdiv(I, act == MLP_ACT_SWIGLU ? c.BN / 2 : c.BN), mt * cdiv(H, c.BN),
+            (uint32_t)(LDS_PER_CU / c.lds)};
+}
+
+// The configuration GEMM1 is split in two for (fused policies), or -1; its
+// GEMM2 split in *s2.
+int fused_split_config(int64_t M, int64_t H, int64_t I, int act, int cus, uint32_t* s2) {
+    if (cdiv(H, mlpc::BK) < 2 * MIN_SLABS_FUSED_SPLIT) return -1;
+    for (int cfg : {CFG_BIG, CFG_WIDE}) {
+        const Tiling t = tiling(M, H, I, act, cfg);
+        if (2 * t.t1 > (uint32_t)cus && t.t1 <= (uint32_t)cus) {
+            *s2 = plan_split(t.t2, cdiv(I, mlpc::BK), cus, M, t.mt, t.wg);
+            return cfg;
+        }
+    }
+    return -1;
+}
+
+// Stream-ordered cost of a configuration under a given split: each kernel
+// takes one round per wave of its tile parts, each round as long as one
+// part's K slabs; a 256 x 128 slab step costs 0.625 of a 256 x 256 one
+// (its MFMA rate per flop is 80%: more operand bytes per MFMA).  This wave
+// rounding picked the faster configuration of the two in every measured
+// stream-ordered case with a 2-way GEMM1 split.
+double so_cost(int64_t M, int64_t H, int64_t I, int act, int cus, int cfg, uint32_t s1, uint32_t s2) {
+    const Tiling t = tiling(M, H, I, act, cfg);
+    const double slab = cfg == CFG_BIG ? 1.0 : 0.625;
+    const uint32_t wave = (uint32_t)cus * t.wg;
+    const uint32_t k1 = cdiv(cdiv(H, mlpc::BK), s1), k2 = cdiv(cdiv(I, mlpc::BK), s2);
+    return slab * ((double)cdiv((int64_t)t.t1 * s1, wave) * k1 + (double)cdiv((int64_t)t.t2 * s2, wave) * k2);
+}
+
+// The small-M configuration, or -1 where the large tiles apply.
+int small_config(int64_t M, int64_t H, int64_t I, int act, int cus) {
+    if (M <= 16) return CFG_SMALL;
+    if (M <= 256) {
+        const Tiling t = tiling(M, H, I, act, CFG_DEEP);
+        if (t.t1 <= (uint32_t)cus && t.t2 <= (uint32_t)cus) return CFG_DEEP;
+    }
+    return -1;
+}
+
+int plan_config(int64_t M, int64_t H, int64_t I, int act, int policy, int cus) {
+    const int sc = small_config(M, H, I, act, cus);
+    if (sc >= 0) return sc;
+    uint32_t s2 = 1;
+    const int fc = fused_split_config(M, H, I, act, cus, &s2);
+    if (fc >= 0) {
+        if (policy != MLP_POLICY_STREAM_ORDERED) return fc;
+        return so_cost(M, H, I, act, cus, CFG_BIG, 2, s2) <= so_cost(M, H, I, act, cus, CFG_WIDE, 2, s2)
+                   ? CFG_BIG : CFG_WIDE;
+    }
+    const Tiling t = tiling(M, H, I, act, CFG_BIG);
+    if (policy == MLP_POLICY_STREAM_ORDERED ? t.t2 >= (uint32_t)cus : 8 * t.t1 >= 7 * (uint32_t)cus)
+        return CFG_BIG;
+    return CFG_WIDE;
+}
+
+// The K split every policy uses for (M, H, I, act): the fused split of
+// GEMM1 where it applies, else the split rule above on the tiling of the
+// stream-ordered plan.
+void plan_shared_split(int64_t M, int64_t H, int64_t I, int act, int cus, uint32_t* s1, uint32_t* s2) {
+    if (small_config(M, H, I, act, cus) < 0 && fused_split_config(M, H, I, act, cus, s2) >= 0) {
+        *s1 = 2;
+        return;
+    }
+    const Tiling t = tiling(M, H, I, act, plan_config(M, H, I, act, MLP_POLICY_STREAM_ORDERED, cus));
+    *s1 = plan_split(t.t1, cdiv(H, mlpc::BK), cus, M, t.mt, t.wg);
+    *s2 = plan_split(t.t2, cdiv(I, mlpc::BK), cus, M, t.mt, t.wg);
+}
+
 // (Re)compute the tiling of a handle for configuration `cfg` and the splits.
 int apply_plan(mlp_chain* h, int cfg) {
     const CfgInfo ci = mlpc_config_info(cfg);
@@ -201,19 +278,16 @@ int apply_plan(mlp_chain* h, int cfg) {
     h->T1 = h->Mt * h->N1t;
     h->T2 = h->Mt * h->N2t;
     const uint32_t nks1 = cdiv(h->H, ci.BK), nks2 = cdiv(h->I, ci.BK);
-    // The split is planned on the tiling of the stream-ordered plan for M
-    // (not of `cfg`), so every policy splits K alike.  The tile shape does
-    // not change any output element's arithmetic (same MFMA sequence over
-    // the same slabs), the split does: equal splits keep the policies
-    // bit-identical while each uses its own tile configuration.
+    // The split does not depend on the policy or on `cfg`, so every policy
+    // splits K alike.  The tile shape does not change any output element's
+    // arithmetic (same MFMA sequence over the same slabs), the split does:
+    // equal splits keep the policies bit-identical while each uses its own
+    // tile configuration.
     {
-        const CfgInfo cs = mlpc_config_info(plan_config(h->M, h->H, h->I, h->act, MLP_POLICY_STREAM_ORDERED, h->cus));
-        const uint32_t mt = cdiv(h->M, cs.BM);
-        const uint32_t t1 = mt * cdiv(h->I, h->act == MLP_ACT_SWIGLU ? cs.BN / 2 : cs.BN);
-        const uint32_t t2 = mt * cdiv(h->H, cs.BN);
-        const uint32_t wg = (uint32_t)(LDS_PER_CU / cs.lds);          // workgroups per CU the ring allows
-        h->S1 = h->forced_s1 > 0 ? (uint32_t)h->forced_s1 : plan_split(t1, nks1, h->cus, h->M, mt, wg);
-        h->S2 = h->forced_s2 > 0 ? (uint32_t)h->forced_s2 : plan_split(t2, nks2, h->cus, h->M, mt, wg);
+        uint32_t s1 = 1, s2 = 1;
+        plan_shared_split(h->M, h->H, h->I, h->act, h->cus, &s1, &s2);
+        h->S1 = h->forced_s1 > 0 ? (uint32_t)h->forced_s1 : s1;
+        h->S2 = h->forced_s2 > 0 ? (uint32_t)h->forced_s2 : s2;
     }
     h->ksp1 = (nks1 + h->S1 - 1) / h->S1;
     h->ksp2 = (nks2 + h->S2 - 1) / h->S2;

@@ -93,7 +93,7 @@ def test_create_destroy_does_not_leak():
 
 
 def test_info_reports_plan():
-    with mc.MlpChain(2048, 12288, 6144, "gelu_tanh", "f16", "tile_sync") as ch:
+    with mc.MlpChain(4096, 8192, 3584, "swiglu", "bf16", "tile_sync") as ch:
         info = ch.info()
         assert info["cus"] >= 1 and info["grid"] >= 1 and info["wg_per_cu"] >= 1
         assert info["T1"] == info["Mt"] * info["N1t"] and info["T2"] == info["Mt"] * info["N2t"]
@@ -105,6 +105,29 @@ def test_info_reports_plan():
         assert info["ksp1"] * info["S1"] >= 8192 // 64 and info["ksp2"] * info["S2"] >= 4096 // 64
         assert (info["S1"] - 1) * info["ksp1"] < 8192 // 64  # no empty part
         assert info["ksp1"] >= 24 and info["ksp2"] >= 24
+
+
+def test_fused_split_plan_is_shared_by_every_policy():
+    """Where GEMM1's unsplit tiles make between half a wave and one wave and
+    each half keeps >= 96 K slabs (GPT-3 shard, M = 1024 and 2048), GEMM1 is
+    split in two for every policy; each policy keeps its own tile shape."""
+    cus = None
+    for M in (1024, 2048):
+        plans = {}
+        for pol in ("stream_ordered", "row_sync", "tile_sync"):
+            with mc.MlpChain(M, 12288, 6144, "gelu_tanh", "f16", pol) as ch:
+                plans[pol] = ch.info()
+                cus = plans[pol]["cus"]
+        if cus != 256:
+            pytest.skip(f"plan thresholds are for 256 CUs, this GPU has {cus}")
+        for pol, info in plans.items():
+            assert (info["S1"], info["S2"]) == (2, 1), (M, pol, info)
+        fused = plans["tile_sync"]
+        assert fused["BM"] == 256 and 128 < fused["T1"] <= 256, fused
+        assert plans["row_sync"]["config"] == fused["config"]
+    # the LLaMA-65 shard (64-slab halves) keeps the unsplit plan at M = 2048
+    with mc.MlpChain(2048, 8192, 2752, "swiglu", "f16", "tile_sync") as ch:
+        assert ch.info()["S1"] == 1
 
 
 @pytest.mark.parametrize("policy", ["row_sync", "tile_sync"])
