@@ -266,31 +266,52 @@ void plan_shared_split(int64_t M, int64_t H, int64_t I, int act, int cus, uint32
     *s2 = plan_split(t.t2, cdiv(I, mlpc::BK), cus, M, t.mt, t.wg);
 }
 
-// (Re)compute the tiling of a handle for configuration `cfg` and the splits.
-int apply_plan(mlp_chain* h, int cfg) {
-    const CfgInfo ci = mlpc_config_info(cfg);
-    if (ci.id < 0) return fail(MLP_EINVAL, "unknown tile configuration %d", cfg);
-    h->cfg = cfg;
-    h->ci = ci;
-    h->Mt = cdiv(h->M, ci.BM);
-    h->N1t = cdiv(h->I, h->act == MLP_ACT_SWIGLU ? ci.BN / 2 : ci.BN);
-    h->N2t = cdiv(h->H, ci.BN);
-    h->T1 = h->Mt * h->N1t;
-    h->T2 = h->Mt * h->N2t;
-    const uint32_t nks1 = cdiv(h->H, ci.BK), nks2 = cdiv(h->I, ci.BK);
+// The tiling and K split of configuration `cfg` for (M, H, I, act) on `cus`
+// CUs; forced splits (> 0) replace the planned ones.
+struct TilePlan {
+    CfgInfo ci;
+    uint32_t Mt, N1t, N2t, T1, T2;
+    uint32_t S1, S2, ksp1, ksp2;
+};
+
+TilePlan tile_plan(int64_t M, int64_t H, int64_t I, int act, int cus, int cfg, int forced_s1, int forced_s2) {
+    TilePlan p{};
+    p.ci = mlpc_config_info(cfg);
+    p.Mt = cdiv(M, p.ci.BM);
+    p.N1t = cdiv(I, act == MLP_ACT_SWIGLU ? p.ci.BN / 2 : p.ci.BN);
+    p.N2t = cdiv(H, p.ci.BN);
+    p.T1 = p.Mt * p.N1t;
+    p.T2 = p.Mt * p.N2t;
     // The split does not depend on the policy or on `cfg`, so every policy
     // splits K alike.  The tile shape does not change any output element's
     // arithmetic (same MFMA sequence over the same slabs), the split does:
     // equal splits keep the policies bit-identical while each uses its own
     // tile configuration.
-    {
-        uint32_t s1 = 1, s2 = 1;
-        plan_shared_split(h->M, h->H, h->I, h->act, h->cus, &s1, &s2);
-        h->S1 = h->forced_s1 > 0 ? (uint32_t)h->forced_s1 : s1;
-        h->S2 = h->forced_s2 > 0 ? (uint32_t)h->forced_s2 : s2;
-    }
-    h->ksp1 = (nks1 + h->S1 - 1) / h->S1;
-    h->ksp2 = (nks2 + h->S2 - 1) / h->S2;
+    uint32_t s1 = 1, s2 = 1;
+    plan_shared_split(M, H, I, act, cus, &s1, &s2);
+    p.S1 = forced_s1 > 0 ? (uint32_t)forced_s1 : s1;
+    p.S2 = forced_s2 > 0 ? (uint32_t)forced_s2 : s2;
+    const uint32_t nks1 = cdiv(H, mlpc::BK), nks2 = cdiv(I, mlpc::BK);
+    p.ksp1 = (nks1 + p.S1 - 1) / p.S1;
+    p.ksp2 = (nks2 + p.S2 - 1) / p.S2;
+    return p;
+}
+
+// (Re)compute the tiling of a handle for configuration `cfg` and the splits.
+int apply_plan(mlp_chain* h, int cfg) {
+    if (mlpc_config_info(cfg).id < 0) return fail(MLP_EINVAL, "unknown tile configuration %d", cfg);
+    const TilePlan p = tile_plan(h->M, h->H, h->I, h->act, h->cus, cfg, h->forced_s1, h->forced_s2);
+    h->cfg = cfg;
+    h->ci = p.ci;
+    h->Mt = p.Mt;
+    h->N1t = p.N1t;
+    h->N2t = p.N2t;
+    h->T1 = p.T1;
+    h->T2 = p.T2;
+    h->S1 = p.S1;
+    h->S2 = p.S2;
+    h->ksp1 = p.ksp1;
+    h->ksp2 = p.ksp2;
     h->order = h->forced_order >= 0 ? (uint32_t)h->forced_order : plan_order(h->policy);
     h->occ = 0;
     h->grid = 0;
@@ -425,6 +446,26 @@ mlpc::ChainArgs make_args(const mlp_chain* h, const void* x, const void* w1, con
     return a;
 }
 
+// Argument checks shared by create and plan.
+int check_chain_args(int64_t M, int64_t H, int64_t I, int act, int policy) {
+    if (M < 1 || H < 8 || I < 8)
+        return fail(MLP_EINVAL, "sizes must be M >= 1, H >= 8, I >= 8 (got M=%lld H=%lld I=%lld)",
+                    (long long)M, (long long)H, (long long)I);
+    if (H % 8 != 0 || I % 8 != 0)
+        return fail(MLP_EINVAL, "H and I must be multiples of 8 (16-byte rows), got H=%lld I=%lld",
+                    (long long)H, (long long)I);
+    // Every operand stays below 2^31 bytes and every row below 2^23 elements
+    // (32-bit element and byte offsets within an operand cannot wrap).
+    const int64_t lim = (int64_t)1 << 30;
+    if (M * H >= lim || M * I >= lim || H * I * 2 >= lim || M >= (1 << 24) || H > (1 << 22) || I > (1 << 22))
+        return fail(MLP_EINVAL, "sizes too large for 32-bit tile indexing (M=%lld H=%lld I=%lld)",
+                    (long long)M, (long long)H, (long long)I);
+    if (act < MLP_ACT_NONE || act > MLP_ACT_SWIGLU) return fail(MLP_EINVAL, "unknown activation %d", act);
+    if (policy < MLP_POLICY_STREAM_ORDERED || policy > MLP_POLICY_TILE_SYNC)
+        return fail(MLP_EINVAL, "unknown policy %d", policy);
+    return MLP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -433,34 +474,9 @@ const char* mlp_chain_last_error(void) { return g_err.c_str(); }
 
 mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype, int policy) {
     g_err.clear();
-    if (M < 1 || H < 8 || I < 8) {
-        fail(MLP_EINVAL, "sizes must be M >= 1, H >= 8, I >= 8 (got M=%lld H=%lld I=%lld)",
-             (long long)M, (long long)H, (long long)I);
-        return nullptr;
-    }
-    if (H % 8 != 0 || I % 8 != 0) {
-        fail(MLP_EINVAL, "H and I must be multiples of 8 (16-byte rows), got H=%lld I=%lld",
-             (long long)H, (long long)I);
-        return nullptr;
-    }
-    // Every operand stays below 2^31 bytes and every row below 2^23 elements
-    // (32-bit element and byte offsets within an operand cannot wrap).
-    const int64_t lim = (int64_t)1 << 30;
-    if (M * H >= lim || M * I >= lim || H * I * 2 >= lim || M >= (1 << 24) || H > (1 << 22) || I > (1 << 22)) {
-        fail(MLP_EINVAL, "sizes too large for 32-bit tile indexing (M=%lld H=%lld I=%lld)",
-             (long long)M, (long long)H, (long long)I);
-        return nullptr;
-    }
-    if (act < MLP_ACT_NONE || act > MLP_ACT_SWIGLU) {
-        fail(MLP_EINVAL, "unknown activation %d", act);
-        return nullptr;
-    }
+    if (check_chain_args(M, H, I, act, policy) != MLP_OK) return nullptr;
     if (dtype != MLP_DTYPE_F16 && dtype != MLP_DTYPE_BF16) {
         fail(MLP_EINVAL, "unknown dtype %d", dtype);
-        return nullptr;
-    }
-    if (policy < MLP_POLICY_STREAM_ORDERED || policy > MLP_POLICY_TILE_SYNC) {
-        fail(MLP_EINVAL, "unknown policy %d", policy);
         return nullptr;
     }
     int dev = 0;
@@ -597,6 +613,19 @@ int mlp_chain_info(mlp_chain_t h, int64_t* info, int n) {
 int mlp_chain_debug_set_spin_limit(mlp_chain_t h, uint32_t limit) {
     if (!h) return fail(MLP_EINVAL, "NULL handle");
     h->spin_limit = limit ? limit : DEFAULT_SPIN_LIMIT;
+    return MLP_OK;
+}
+
+int mlp_chain_plan(int64_t M, int64_t H, int64_t I, int act, int policy, int cus, int64_t* plan, int n) {
+    if (!plan || n < 3) return fail(MLP_EINVAL, "mlp_chain_plan needs an array of at least 3 slots");
+    if (cus < 8) return fail(MLP_EINVAL, "cus must be >= 8, got %d", cus);
+    const int rc = check_chain_args(M, H, I, act, policy);
+    if (rc != MLP_OK) return rc;
+    const int cfg = plan_config(M, H, I, act, policy, cus);
+    const TilePlan p = tile_plan(M, H, I, act, cus, cfg, 0, 0);
+    const int64_t bn1 = act == MLP_ACT_SWIGLU ? p.ci.BN / 2 : p.ci.BN;
+    const int64_t v[13] = {cfg, p.S1, p.S2, p.ci.BM, bn1, p.ci.BN, p.Mt, p.N1t, p.N2t, p.T1, p.T2, p.ksp1, p.ksp2};
+    for (int i = 0; i < n && i < 13; ++i) plan[i] = v[i];
     return MLP_OK;
 }
 

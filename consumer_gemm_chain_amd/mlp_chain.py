@@ -25,7 +25,7 @@ POLICIES = {"stream_ordered": MLP_POLICY_STREAM_ORDERED, "row_sync": MLP_POLICY_
             "tile_sync": MLP_POLICY_TILE_SYNC}
 
 EXPORTS = ("mlp_chain_create", "mlp_chain_run", "mlp_chain_destroy", "mlp_chain_run_phase",
-           "mlp_chain_status", "mlp_chain_last_error", "mlp_chain_info",
+           "mlp_chain_status", "mlp_chain_last_error", "mlp_chain_info", "mlp_chain_plan",
            "mlp_chain_debug_set_spin_limit", "mlp_chain_debug_skip_producer",
            "mlp_chain_debug_set_config", "mlp_chain_debug_set_split", "mlp_chain_debug_set_grid",
            "mlp_chain_debug_set_order", "mlp_chain_debug_set_trace", "mlp_chain_debug_read_intermediate")
@@ -67,6 +67,8 @@ def load_library(path: str | None = None):
     lib.mlp_chain_last_error.restype = ctypes.c_char_p
     lib.mlp_chain_info.argtypes = [vp, ctypes.POINTER(i64), ci]
     lib.mlp_chain_info.restype = ci
+    lib.mlp_chain_plan.argtypes = [i64, i64, i64, ci, ci, ci, ctypes.POINTER(ctypes.c_int64), ci]
+    lib.mlp_chain_plan.restype = ci
     lib.mlp_chain_debug_set_spin_limit.argtypes = [vp, u32]
     lib.mlp_chain_debug_set_spin_limit.restype = ci
     lib.mlp_chain_debug_skip_producer.argtypes = [vp, i64]
@@ -133,6 +135,17 @@ def mlp_chain_info(h: int) -> dict:
     arr = (ctypes.c_int64 * len(INFO_FIELDS))()
     _check(load_library().mlp_chain_info(h, arr, len(INFO_FIELDS)))
     return dict(zip(INFO_FIELDS, (int(v) for v in arr)))
+
+
+PLAN_FIELDS = ("config", "S1", "S2", "BM", "BN1", "BN2", "Mt", "N1t", "N2t", "T1", "T2", "ksp1", "ksp2")
+
+
+def mlp_chain_plan(M: int, H: int, I: int, act: int, policy: int, cus: int) -> dict:
+    """The plan mlp_chain_create would make on a GPU with `cus` CUs (host only)."""
+    arr = (ctypes.c_int64 * len(PLAN_FIELDS))()
+    _check(load_library().mlp_chain_plan(int(M), int(H), int(I), int(act), int(policy), int(cus), arr,
+                                         len(PLAN_FIELDS)))
+    return dict(zip(PLAN_FIELDS, (int(v) for v in arr)))
 
 
 def mlp_chain_debug_set_spin_limit(h: int, limit: int) -> int:

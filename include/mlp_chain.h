@@ -126,6 +126,21 @@ const char* mlp_chain_last_error(void);
  * Returns MLP_EINVAL for a NULL handle or array, or n < 16. */
 int mlp_chain_info(mlp_chain_t h, int64_t* info, int n);
 
+/* The plan mlp_chain_create would make for these sizes on a GPU with `cus`
+ * compute units, computed on the host alone (no device is touched): fills
+ * the first min(n, 13) of
+ *   { config id, S1, S2, BM, BN1, BN2, Mt, N1t, N2t, T1, T2,
+ *     K slabs per GEMM1 part, K slabs per GEMM2 part }.
+ * The K split (S1, S2) depends on the sizes and `cus` only, never on the
+ * policy, so all policies compute the same output bits; the tile
+ * configuration may differ per policy.  The planner fills the last wave of
+ * the GPU (the CuSync README, opening paragraph) by splitting K where a GEMM
+ * has fewer tiles than CUs, and for the fused policies splits GEMM1 in two
+ * where its tiles make between half a wave and one wave.  Returns MLP_EINVAL
+ * for sizes, act or policy that mlp_chain_create would reject, cus < 8, a
+ * NULL array or n < 3. */
+int mlp_chain_plan(int64_t M, int64_t H, int64_t I, int act, int policy, int cus, int64_t* plan, int n);
+
 /* Test hooks (never needed for normal use):
  * set the consumer spin limit (iterations of the back-off loop before a
  * consumer gives up; 0 restores the default), and make producer part
