@@ -275,24 +275,26 @@ def test_tile_configs_agree_bitwise(act, dtype):
     from consumer_gemm_chain_amd.mlp_chain import MlpChain
     from tests._helpers import empty_dev, from_dev
     from consumer_gemm_chain_amd import build as b
-    M, H, I = 200, 1032, 776
-    x, w1, w2 = _case(M, H, I, act, dtype, seed=31)
-    dev = (to_dev(x, dtype), to_dev(w1, dtype), to_dev(w2, dtype))
-    for s1, s2 in ((1, 1), (2, 3)):
-        ref = None
-        for cfg in range(b.num_configs()):
-            for pol in ("stream_ordered", "tile_sync"):
-                with MlpChain(M, H, I, act, dtype, pol) as ch:
-                    ch.set_config(cfg)
-                    ch.set_split(s1, s2)
-                    out = empty_dev((M, H), dtype)
-                    ch.run(*dev, out)
-                    torch.cuda.synchronize()
-                    assert ch.status() == 0
-                    y = from_dev(out)
-                if ref is None:
-                    ref = y
-                assert np.array_equal(y, ref), (cfg, pol, s1, s2)
+    # (K % 64 != 0 takes the K-tail loop in the last part; K % 64 == 0 the
+    # regular loop, with the L2 touch in the configurations that have one)
+    for M, H, I in ((200, 1032, 776), (300, 1024, 640)):
+        x, w1, w2 = _case(M, H, I, act, dtype, seed=31)
+        dev = (to_dev(x, dtype), to_dev(w1, dtype), to_dev(w2, dtype))
+        for s1, s2 in ((1, 1), (2, 3)):
+            ref = None
+            for cfg in range(b.num_configs()):
+                for pol in ("stream_ordered", "tile_sync"):
+                    with MlpChain(M, H, I, act, dtype, pol) as ch:
+                        ch.set_config(cfg)
+                        ch.set_split(s1, s2)
+                        out = empty_dev((M, H), dtype)
+                        ch.run(*dev, out)
+                        torch.cuda.synchronize()
+                        assert ch.status() == 0
+                        y = from_dev(out)
+                    if ref is None:
+                        ref = y
+                    assert np.array_equal(y, ref), (M, H, I, cfg, pol, s1, s2)
 
 
 @pytest.mark.gpu
