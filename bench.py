@@ -1,7 +1,7 @@
 """Benchmark of the tile-synchronized MLP GEMM chain on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1] [--M 2048]
-                    [--policy tile_sync] [--no-sweep] [--no-cpu]
+                    [--policy tile_sync] [--no-sweep] [--no-cpu] [--sweep-reps R]
 
 A step is one chain pass (GEMM1 + activation, then GEMM2) over one batch of
 M tokens, enqueued through the C ABI (mlp_chain_run) with inputs already
@@ -10,12 +10,15 @@ I=6144, fp16, GeLU; the pages' GPT-3 MLP under 8-way model parallelism) at
 M=2048 tokens with the tile_sync policy.  Next to it the script reports two
 stream-ordered two-kernel baselines: the planned pair, which shares the fused
 run's K split and is its bit-exact reference, and the fastest pair over tile
-configurations and K splits (the fair speed baseline); a sweep over M = 1..2048 for the three
-policies (time, TFLOP/s, fraction of the MFMA / HBM roofline, speedup over
-stream-ordered, and an overhead in the style of the FLUX summary card's
-Effective Communication Time: policy time minus the best isolated GEMM1 and
-GEMM2 times), the dominant kernel's roofline position measured with HIP
-events, and the CPU oracle timed on a bounded sample of rows.
+configurations and K splits (the fair speed baseline).  It also reports a
+sweep of the three policies over each workload's M list (GPT-3 up to --M,
+the LLaMA-65, Llama-2 and 8192^3 shapes in full): time hot and with the
+Infinity Cache flushed, TFLOP/s, fraction of the MFMA / HBM roofline,
+speedup over both stream-ordered baselines, and an overhead in the style of
+the FLUX summary card's Effective Communication Time (policy time minus the
+best isolated GEMM1 and GEMM2 times).  Then the dominant kernel's roofline
+position measured with HIP events, and the CPU oracle timed on a bounded
+sample of rows.
 
 Prints ONE JSON line.  Inputs are seeded synthetic data of the workload's
 shapes (no trained weights).
@@ -132,11 +135,14 @@ def event_times(fn, n, stream, flush=None):
 
 
 def sweep(runner, Ms, reps, stream, flush_buf):
-    """Per (M, policy): median event time, TFLOP/s, roofline fraction, speedup,
-    ECT-style overhead against the best isolated GEMM1 + GEMM2 times."""
+    """Per (M, policy): median event time hot (weights left in the caches by
+    the previous run) and cold (512 MB written between runs, so the 256 MB
+    Infinity Cache holds none of the weights), TFLOP/s, roofline fraction,
+    speedup over both stream-ordered baselines, and the ECT-style overhead
+    against the best isolated GEMM1 + GEMM2 times (hot)."""
     import torch
     w = runner.w
-    flush = (lambda: flush_buf.add_(1)) if flush_buf is not None else None
+    flush = lambda: flush_buf.add_(1)  # noqa: E731
     rows = []
     for M in Ms:
         x, w1, w2, out = runner.args(M)
@@ -146,37 +152,57 @@ def sweep(runner, Ms, reps, stream, flush_buf):
                 so.run_phase(1, x=x, w1=w1)
                 so.run_phase(2, w2=w2, out=out)
             torch.cuda.synchronize()
-            g1 = np.median(event_times(lambda: so.run_phase(1, x=x, w1=w1), reps, stream, flush))
-            g2 = np.median(event_times(lambda: so.run_phase(2, w2=w2, out=out), reps, stream, flush))
+            g1 = np.median(event_times(lambda: so.run_phase(1, x=x, w1=w1), reps, stream))
+            g2 = np.median(event_times(lambda: so.run_phase(2, w2=w2, out=out), reps, stream))
         for pol in POLICIES:
             with runner.chain(M, pol) as ch:
                 for _ in range(3):
                     ch.run(x, w1, w2, out)
                 torch.cuda.synchronize()
-                ts = event_times(lambda: ch.run(x, w1, w2, out), reps, stream, flush)
+                ts = event_times(lambda: ch.run(x, w1, w2, out), reps, stream)
+                tc = event_times(lambda: ch.run(x, w1, w2, out), reps, stream, flush)
                 assert ch.status() == 0
                 info = ch.info()
-            res[pol] = (float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90)), info)
+            res[pol] = (float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90)),
+                        float(np.median(tc)), info)
         t_roof, bound = roofline_time_us(w, M, w.dtype)
-        t_so = res["stream_ordered"][0]
-        t_best, b_cfg, b_s1, b_s2 = best_stream_ordered(runner, M, stream, max(5, reps // 2), flush)
+        t_so, t_so_cold = res["stream_ordered"][0], res["stream_ordered"][3]
+        t_best, b_cfg, b_s1, b_s2 = best_stream_ordered(runner, M, stream, max(5, reps // 2))
+        with runner.chain(M, "stream_ordered") as sb:
+            sb.set_config(b_cfg)
+            sb.set_split(b_s1, b_s2)
+            sb.run(x, w1, w2, out)
+            t_best = min(t_best, float(np.median(event_times(lambda: sb.run(x, w1, w2, out), reps, stream))))
+            t_best_cold = float(np.median(event_times(lambda: sb.run(x, w1, w2, out), reps, stream, flush)))
+        # the planned pair is one of the searched plans: the fastest is never slower than it
+        so_info = res["stream_ordered"][4]
+        if t_so < t_best:
+            t_best, b_cfg, b_s1, b_s2 = t_so, so_info["config"], so_info["S1"], so_info["S2"]
+        t_best_cold = min(t_best_cold, t_so_cold)
         for pol in POLICIES:
-            t, p10, p90, info = res[pol]
+            t, p10, p90, tcold, info = res[pol]
             rows.append({
                 "M": M, "policy": pol, "us": round(t, 2), "p10_us": round(p10, 2), "p90_us": round(p90, 2),
+                "us_cold": round(tcold, 2),
                 "tflops": round(w.flops(M) / (t * 1e-6) / 1e12, 2),
                 "gbs": round(w.bytes(M) / (t * 1e-6) / 1e9, 1),
-                "roofline_frac": round(t_roof / t, 4), "bound": bound,
+                "gbs_cold": round(w.bytes(M) / (tcold * 1e-6) / 1e9, 1),
+                "roofline_frac": round(t_roof / t, 4), "roofline_frac_cold": round(t_roof / tcold, 4),
+                "bound": bound,
                 "speedup_vs_stream_ordered": round(t_so / t, 4),
                 "speedup_vs_stream_ordered_best": round(t_best / t, 4),
-                "stream_ordered_best": {"us": round(t_best, 2), "config": b_cfg, "S1": b_s1, "S2": b_s2},
+                "speedup_vs_stream_ordered_cold": round(t_so_cold / tcold, 4),
+                "speedup_vs_stream_ordered_best_cold": round(t_best_cold / tcold, 4),
+                "stream_ordered_best": {"us": round(t_best, 2), "us_cold": round(t_best_cold, 2),
+                                        "config": b_cfg, "S1": b_s1, "S2": b_s2},
                 "overhead_vs_best_unsplit_us": round(t - (g1 + g2), 2),
                 "tiles": [info["T1"], info["T2"]], "tile": [info["BM"], info["BN1"]],
                 "split": [info["S1"], info["S2"]],
             })
         log(f"M={M:5d} g1={g1:8.1f}us g2={g2:8.1f}us  " + "  ".join(
-            f"{p}={res[p][0]:8.1f}us" for p in POLICIES)
-            + f"  best stream_ordered={t_best:8.1f}us (config {b_cfg}, split {b_s1},{b_s2})")
+            f"{p}={res[p][0]:8.1f}/{res[p][3]:8.1f}us" for p in POLICIES)
+            + f"  best stream_ordered={t_best:8.1f}/{t_best_cold:8.1f}us (config {b_cfg}, split {b_s1},{b_s2})"
+            + "  (hot/cold)")
     return rows
 
 
@@ -188,7 +214,7 @@ def so_search_configs(M):
     return (0, 4) if M <= 16 else (3, 4, 7) if M <= 256 else (3, 7)
 
 
-def best_stream_ordered(runner, M, stream, reps, flush=None):
+def best_stream_ordered(runner, M, stream, reps):
     """The fastest stream-ordered pair over tile configurations x K splits
     (S1 in 1..4, S2 in 1..2, plus the planned split): (median event us,
     config, S1, S2).  Every one of these plans is a valid stream-ordered
@@ -207,7 +233,7 @@ def best_stream_ordered(runner, M, stream, reps, flush=None):
                 for _ in range(2):
                     so.run(x, w1, w2, out)
                 torch.cuda.synchronize()
-                t = float(np.median(event_times(lambda: so.run(x, w1, w2, out), reps, stream, flush)))
+                t = float(np.median(event_times(lambda: so.run(x, w1, w2, out), reps, stream)))
                 assert so.status() == 0
             if best is None or t < best[0]:
                 best = (t, cfg, s1, s2)
@@ -243,9 +269,10 @@ def main():
     ap.add_argument("--M", type=int, default=2048)
     ap.add_argument("--policy", default="tile_sync", choices=POLICIES)
     ap.add_argument("--sweep-reps", type=int, default=20)
+    ap.add_argument("--sweep-workloads", default="1,2,3,4",
+                    help="workloads swept over their M lists (the headline workload up to --M)")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--flush", action="store_true", help="flush the MALL between sweep runs")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -318,6 +345,10 @@ def main():
     so_tflops = F / (wall_so / args.steps) / 1e12
     wall_sb = (wall_sb_a + wall_sb_b) / 2
     kern_sb = np.concatenate([kern_sb_a, kern_sb_b])
+    if wall_so < wall_sb:
+        # the planned pair is one of the searched plans: the fastest is never slower than it
+        wall_sb, kern_sb = wall_so, kern_so
+        bcfg, bs1, bs2 = so_info["config"], so_info["S1"], so_info["S2"]
     sb_tflops = F / (wall_sb / args.steps) / 1e12
 
     t_roof, bound = roofline_time_us(w, M, w.dtype)
@@ -340,12 +371,22 @@ def main():
                          "frac": round(gbs / PEAK_HBM_GBS, 4)})
 
     rows = []
+    flush_buf = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda") if not args.no_sweep else None
     if sweep_Ms:
-        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device="cuda") if args.flush else None
-        rows = sweep(runner, sweep_Ms, args.sweep_reps, stream, flush_buf)
-        del flush_buf
+        rows = [{"workload": w.name, **r} for r in sweep(runner, sweep_Ms, args.sweep_reps, stream, flush_buf)]
 
     cpu = None if args.no_cpu else cpu_baseline(runner, M)
+
+    if not args.no_sweep:
+        for wl in (int(v) for v in args.sweep_workloads.split(",") if v.strip()):
+            if wl == args.workload:
+                continue
+            del runner
+            torch.cuda.empty_cache()
+            ws = gen.WORKLOADS[wl]
+            runner = Runner(ws, ws.max_M)
+            rows += [{"workload": ws.name, **r} for r in sweep(runner, list(ws.Ms), args.sweep_reps, stream, flush_buf)]
+    del flush_buf
 
     line = {
         "metric": "MLP-chain TFLOP/s and % roofline vs stream-ordered 2-kernel, M=1..2048",
