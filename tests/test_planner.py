@@ -46,7 +46,13 @@ def test_small_m_configurations():
             assert (p["BM"], p["BN2"]) == (16, 64)
             assert p["S1"] * p["T1"] <= CUS and p["S1"] > 1     # weight streaming: split K
     p = plan(64, w.H, w.I, w.act, mc.MLP_POLICY_TILE_SYNC)
-    assert (p["BM"], p["BN2"]) == (64, 128) and p["T1"] <= CUS and p["T2"] <= CUS
+    assert (p["BM"], p["BN2"]) == (64, 128) and p["T1"] <= CUS and p["T2"] < CUS
+    # LLaMA-65 at M = 256: GEMM2 would have exactly one wave of 64 x 128
+    # tiles -- the 256-row tiles with a K split take over
+    w = gen.WORKLOADS[2]
+    for pol in POLS:
+        p = plan(256, w.H, w.I, w.act, pol)
+        assert p["BM"] == 256 and (p["S1"], p["S2"]) == (4, 1), p
 
 
 @pytest.mark.parametrize("M,fused_tile,so_tile", [(1024, (256, 128), (256, 256)), (2048, (256, 256), (256, 128))])
