@@ -1,17 +1,17 @@
 // chain_api.cpp -- the C ABI declared in include/mlp_chain.h: argument
 // checks, tile planning, workspace ownership, epochs and launches.
 //
-// Per-run synchronization state lives in the workspace and is never reset
-// between runs (no memset on the run path, so a run is a single kernel for
-// the fused policies):
-//   * the 8 tile-queue counters only grow: per run, queue x advances by its
-//     length plus the grid (every item once, one failed draw per workgroup),
-//     so the kernel derives each queue's base from the epoch;
+// Per-run synchronization state lives in the workspace and is never cleared
+// from the host between runs (no memset on the run path, so a run is a
+// single kernel for the fused policies):
+//   * the 8 tile-queue counters start every run at zero: the last workgroup
+//     of a run (its exit count reaches the grid) resets them;
 //   * tile flags hold the epoch of the run that last published them, and a
 //     consumer waits for (int32)(flag - epoch) >= 0;
 //   * row counters grow by N1t per run; a consumer of run e waits for
-//     (int32)(count - e * N1t) >= 0.
-// All of it is modular 32-bit arithmetic, so wrap-around is harmless.
+//     (int32)(count - e * N1t) >= 0;
+//   * split-K arrival counters grow by S per execution of their GEMM.
+// The epoch arithmetic is modular 32-bit, so wrap-around is harmless.
 #include <hip/hip_runtime.h>
 
 #include <stdarg.h>
