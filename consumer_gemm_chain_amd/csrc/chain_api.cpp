@@ -4,8 +4,9 @@
 // Per-run synchronization state lives in the workspace and is never cleared
 // from the host between runs (no memset on the run path, so a run is a
 // single kernel for the fused policies):
-//   * the 8 tile-queue counters start every run at zero: the last workgroup
-//     of a run (its exit count reaches the grid) resets them;
+//   * two sets of 8 tile-queue counters alternate by epoch parity: a run
+//     uses one (zero when it starts) and its workgroup 0 zeroes the other,
+//     which the next run takes;
 //   * tile flags hold the epoch of the run that last published them, and a
 //     consumer waits for (int32)(flag - epoch) >= 0;
 //   * row counters grow by N1t per run; a consumer of run e waits for
@@ -103,6 +104,7 @@ struct DeviceGuard {
 };
 
 constexpr int LDS_PER_CU = 160 * 1024;        // gfx950
+constexpr size_t TICKET_BYTES = 2 * 8 * 256;  // two sets of 8 tile-queue counters, one per 256 bytes
 constexpr uint32_t MIN_SLABS_PER_PART = 24;  // 1536 K-elements: keeps the partial traffic small
 constexpr uint32_t MIN_SLABS_SHARED = 32;    // 2048 K-elements
 
@@ -377,7 +379,7 @@ int build_workspace(mlp_chain* h) {
     const size_t c2_b = align_up((size_t)h->T2 * 4, 256);
     const size_t p1_b = h->S1 > 1 ? align_up((size_t)h->T1 * h->S1 * acc_bytes, 256) : 0;
     const size_t p2_b = h->S2 > 1 ? align_up((size_t)h->T2 * h->S2 * acc_bytes, 256) : 0;
-    h->sync_bytes = f_b + r_b + c1_b + c2_b + 2304 + 2 * 256;
+    h->sync_bytes = f_b + r_b + c1_b + c2_b + TICKET_BYTES + 2 * 256;
     h->ws_bytes = t_b + h->sync_bytes + p1_b + p2_b;
     hipError_t e = hipMalloc(&h->ws, h->ws_bytes);
     if (e != hipSuccess) {
@@ -395,10 +397,10 @@ int build_workspace(mlp_chain* h) {
     p += c1_b;
     h->cnt2 = reinterpret_cast<uint32_t*>(p);
     p += c2_b;
-    h->ticket = reinterpret_cast<uint32_t*>(p);            // 8 queue counters + exit counter, 256 B apart
-    h->status = reinterpret_cast<uint32_t*>(p + 2304);
-    h->zero = reinterpret_cast<uint16_t*>(p + 2304 + 256);
-    p += 2304 + 2 * 256;
+    h->ticket = reinterpret_cast<uint32_t*>(p);            // 2 sets of 8 queue counters, 256 B apart
+    h->status = reinterpret_cast<uint32_t*>(p + TICKET_BYTES);
+    h->zero = reinterpret_cast<uint16_t*>(p + TICKET_BYTES + 256);
+    p += TICKET_BYTES + 2 * 256;
     h->part1 = p1_b ? reinterpret_cast<float*>(p) : nullptr;
     p += p1_b;
     h->part2 = p2_b ? reinterpret_cast<float*>(p) : nullptr;
@@ -425,7 +427,8 @@ mlpc::ChainArgs make_args(const mlp_chain* h, const void* x, const void* w1, con
     a.T2 = h->T2;
     a.rx = h->Mt >= 2 ? 2u : 1u;
     a.order = h->order;
-    a.ticket = h->ticket;
+    a.ticket = h->ticket + 512 * (h->epoch & 1u);
+    a.ticket_next = h->ticket + 512 * ((h->epoch & 1u) ^ 1u);
     a.flags = h->flags;
     a.rowcnt = h->rowcnt;
     a.status = h->status;

@@ -71,8 +71,9 @@ struct ChainArgs {
     uint32_t Mt, N1t, N2t, T1, T2;
     uint32_t rx;            // XCD grid rows (1, 2, 4 or 8; the grid is rx x 8/rx)
     uint32_t order;         // bit 0 / bit 1: GEMM1 / GEMM2 tiles walked column-major in each XCD block
-    uint32_t* ticket;       // 8 tile-queue counters (one per XCD) and an exit counter, 64 words apart;
-                            // zero when a run starts (the last workgroup of a run resets them)
+    uint32_t* ticket;       // this run's 8 tile-queue counters (one per XCD), 64 words apart; zero when
+                            // the run starts
+    uint32_t* ticket_next;  // the other set of 8 (used by the next run): workgroup 0 zeroes it
     uint32_t* flags;        // [Mt * N1t] ready epochs (tile_sync)
     uint32_t* rowcnt;       // [Mt] producer completions (row_sync)
     uint32_t* status;       // sticky watchdog status (nonzero = a consumer gave up)

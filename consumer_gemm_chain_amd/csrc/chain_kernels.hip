@@ -128,8 +128,11 @@ struct ChainWait {
 // loads reads the counters of all queues not yet seen dry, and an atomic
 // draws from the first of them, in the order own queue, then the next ones
 // -- so a workgroup takes its own queue's remaining items before stealing.
-// The last workgroup to find every queue dry resets the counters, so every
-// run starts from zero with no clearing launch.  Items are numbered for
+// Runs alternate between two sets of counters (epoch parity): workgroup 0
+// zeroes the set the previous run used, which the next run takes, so every
+// run starts from zero with no clearing launch and no exit count at the end
+// (stream order: the previous run has finished, and this one never touches
+// that set).  Items are numbered for
 // flags, trace and test hooks as GEMM1 parts (mb * N1t + nb) * S1 + part,
 // then GEMM2 parts P1 + (mb * N2t + nb) * S2 + part.
 // Deadlock freedom: a queue hands out its items in order, producers first,
@@ -202,6 +205,8 @@ void chain_persistent_kernel(ChainArgs a) {
     const int bn1 = a.act == ACT_SWIGLU ? C::BN / 2 : C::BN;
     Queues q{blockIdx.x & 7u, 0u, P1};
     uint32_t item = NO_ITEM;
+    if (blockIdx.x == 0 && threadIdx.x < 8)
+        __hip_atomic_store(a.ticket_next + 64 * threadIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     {
         // the launch-time item: position blockIdx / 8 of the own queue
         const XcdBlock bp = xcd_block(a.Mt, a.N1t, a.S1, a.rx, q.own);
@@ -269,16 +274,6 @@ void chain_persistent_kernel(ChainArgs a) {
         // the other threads re-read the old ticket at the barriers while
         // thread 0 waits to draw the next one, which never ends.
         __syncthreads();
-    }
-    // every queue is dry for this workgroup; the last one to get here resets
-    // the counters for the next run (no workgroup draws after its exit count)
-    if (threadIdx.x == 0) {
-        uint32_t* exits = a.ticket + 64 * 8;
-        if (__hip_atomic_fetch_add(exits, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.grid - 1) {
-            for (int x = 0; x < 8; ++x)
-                __hip_atomic_store(a.ticket + 64 * x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(exits, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
     }
 }
 
