@@ -11,7 +11,9 @@
 //     consumer waits for (int32)(flag - epoch) >= 0;
 //   * row counters grow by N1t per run; a consumer of run e waits for
 //     (int32)(count - e * N1t) >= 0;
-//   * split-K arrival counters grow by S per execution of their GEMM.
+//   * split-K arrival counters are set back to zero by the last part of
+//     each tile, so the stream-ordered launches depend on nothing the host
+//     changes between runs (they can be captured in a HIP graph).
 // The epoch arithmetic is modular 32-bit, so wrap-around is harmless.
 #include <hip/hip_runtime.h>
 
@@ -81,7 +83,6 @@ struct mlp_chain {
     float* part2;
     // run state
     uint32_t epoch;             // fused runs
-    uint32_t gen1, gen2;        // GEMM1 / GEMM2 executions (split arrival targets)
     uint32_t spin_limit;
     uint32_t skip_producer;
     uint64_t* trace;            // caller's timeline buffer (debug), or nullptr
@@ -357,8 +358,6 @@ int zero_workspace(mlp_chain* h) {
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return fail(MLP_EHIP, "hipDeviceSynchronize failed: %s", hipGetErrorString(e));
     h->epoch = 0;
-    h->gen1 = 0;
-    h->gen2 = 0;
     return MLP_OK;
 }
 
@@ -441,8 +440,6 @@ mlpc::ChainArgs make_args(const mlp_chain* h, const void* x, const void* w1, con
     a.part2 = h->part2;
     a.cnt1 = h->cnt1;
     a.cnt2 = h->cnt2;
-    a.gen1 = h->gen1;
-    a.gen2 = h->gen2;
     a.epoch = h->epoch;
     a.grid = h->grid;
     a.spin_limit = h->spin_limit;
@@ -553,8 +550,6 @@ int mlp_chain_run(mlp_chain_t h, const void* x, const void* w1, const void* w2, 
     if (!g.ok) return fail(MLP_EHIP, "cannot select the handle's device %d", h->device);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     h->last_stream = s;
-    h->gen1 += 1u;
-    h->gen2 += 1u;
     if (h->policy == MLP_POLICY_STREAM_ORDERED) {
         const mlpc::ChainArgs a = make_args(h, x, w1, w2, out);
         int rc = launch_phase(h, LAUNCH_GEMM1, a, s);
@@ -566,8 +561,6 @@ int mlp_chain_run(mlp_chain_t h, const void* x, const void* w1, const void* w2, 
     int rc = launch_phase(h, h->policy == MLP_POLICY_ROW_SYNC ? LAUNCH_ROW : LAUNCH_TILE, a, s);
     if (rc != MLP_OK) {
         h->epoch -= 1u;
-        h->gen1 -= 1u;
-        h->gen2 -= 1u;
         return rc;
     }
     return MLP_OK;
@@ -585,7 +578,6 @@ int mlp_chain_run_phase(mlp_chain_t h, int phase, const void* x, const void* w1,
     if (!g.ok) return fail(MLP_EHIP, "cannot select the handle's device %d", h->device);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     h->last_stream = s;
-    if (phase == 1) h->gen1 += 1u; else h->gen2 += 1u;
     const mlpc::ChainArgs a = make_args(h, x, w1, w2, out);
     return launch_phase(h, phase == 1 ? LAUNCH_GEMM1 : LAUNCH_GEMM2, a, s);
 }

@@ -80,14 +80,14 @@ struct ChainArgs {
     const uint16_t* zero;   // >= 16 zero bytes: the source of every out-of-range chunk
     // deterministic split of each tile's K range (S1 parts per GEMM1 tile, S2
     // per GEMM2 tile; S = 1: no split).  Parts write fp32 partials; the last
-    // part to arrive (per-tile counter) sums them in part order 0..S-1.
+    // part to arrive (per-tile counter, which it sets back to zero) sums them
+    // in part order 0..S-1.
     uint32_t S1, S2;        // parts per tile
     uint32_t ksp1, ksp2;    // K slabs per part
     float* part1;           // [T1][S1][tile accumulators] (S1 > 1)
     float* part2;           // [T2][S2][tile accumulators] (S2 > 1)
-    uint32_t* cnt1;         // [T1] part arrivals (S1 > 1)
-    uint32_t* cnt2;         // [T2] part arrivals (S2 > 1)
-    uint32_t gen1, gen2;    // this run's GEMM1 / GEMM2 generation (arrival targets gen * S)
+    uint32_t* cnt1;         // [T1] part arrivals (S1 > 1), zero between executions
+    uint32_t* cnt2;         // [T2] part arrivals (S2 > 1), zero between executions
     uint64_t* trace;        // optional timeline: 4 words per ticket (nullptr = off)
     uint32_t epoch;         // this run's epoch (mod 2^32)
     uint32_t grid;          // persistent workgroups
@@ -1043,12 +1043,14 @@ __device__ __forceinline__ TileJob consumer_job(const ChainArgs& a, uint32_t mb,
 // Split-K: store this part's accumulators (fp32, in register order so every
 // thread writes and later reads its own 16-byte slots), count the part in
 // with an agent-scope acquire-release, and, in the part that arrives last,
+// set the tile's counter back to zero (every part of this execution has
+// counted in, so the next execution starts from zero: no host-side
+// generation, and a captured stream-ordered graph replays correctly) and
 // replace the accumulators by the sum of all S partials in part order.
 // Returns true in the last part (which then runs the epilogue).
 template <class C>
 __device__ __forceinline__ bool split_reduce(f32x4 (&acc)[C::FM][C::FN], float* part, uint32_t* cnt,
-                                             uint32_t tile, uint32_t s, uint32_t S, uint32_t target,
-                                             uint32_t* s_flag) {
+                                             uint32_t tile, uint32_t s, uint32_t S, uint32_t* s_flag) {
     constexpr int NF = C::FM * C::FN;
     const int tid = threadIdx.x;
     f32x4* base = reinterpret_cast<f32x4*>(part) + (size_t)tile * S * NF * C::NT;
@@ -1063,7 +1065,9 @@ __device__ __forceinline__ bool split_reduce(f32x4 (&acc)[C::FM][C::FN], float* 
     if (tid == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         const uint32_t old = __hip_atomic_fetch_add(cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        *s_flag = (old + 1u == target) ? 1u : 0u;
+        const bool last = old + 1u == S;
+        if (last) __hip_atomic_store(cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = last ? 1u : 0u;
         handoff_acquire();
     }
     __syncthreads();
@@ -1116,8 +1120,8 @@ __device__ __forceinline__ bool run_tile(const ChainArgs& a, uint32_t mb, uint32
     tile_mainloop<C, DT>(j, acc, wait);
     const uint32_t S = ROLE == 1 ? a.S1 : a.S2;
     if (S > 1) {
-        const bool last = ROLE == 1 ? split_reduce<C>(acc, a.part1, a.cnt1, tile, s, S, a.gen1 * S, s_flag)
-                                    : split_reduce<C>(acc, a.part2, a.cnt2, tile, s, S, a.gen2 * S, s_flag);
+        const bool last = ROLE == 1 ? split_reduce<C>(acc, a.part1, a.cnt1, tile, s, S, s_flag)
+                                    : split_reduce<C>(acc, a.part2, a.cnt2, tile, s, S, s_flag);
         if (!last) return false;
     }
     if constexpr (ROLE == 1)

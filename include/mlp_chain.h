@@ -86,6 +86,10 @@ mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype
  * fails.  A consumer tile that waits longer than the spin limit for its
  * producer gives up and records MLP_ETIMEOUT in the handle's status word
  * (see mlp_chain_status); its output is then undefined.
+ * A stream-ordered handle's launches depend on nothing the host changes
+ * between runs, so they may be captured into a HIP graph and replayed (the
+ * same pointers each replay).  The fused policies' launches carry a new
+ * epoch for their ready flags each run and must not be captured.
  * (CuSync README, opening and MLP paragraphs.) */
 int mlp_chain_run(mlp_chain_t h, const void* x, const void* w1, const void* w2, void* out,
                   void* hip_stream);
