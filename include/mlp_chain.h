@@ -21,8 +21,10 @@
  *                              chunk by K chunk, only for the GEMM1 tile that
  *                              produced that chunk.
  *
- * All three compute bit-identical outputs (same tiles, same accumulation
- * order); they differ only in when tiles run.
+ * All three compute bit-identical outputs: they share the K split and the
+ * accumulation order of every output element (each may use its own tile
+ * shape, which changes no element's arithmetic); they differ only in when
+ * tiles run.
  *
  * Numerics: inputs and outputs are fp16 or bf16; products accumulate in fp32
  * on the matrix cores; the activation is applied to the fp32 accumulator(s);
@@ -45,9 +47,9 @@
  * Pointers: x, w1, w2 and out are DEVICE pointers owned by the caller.  The
  * stream argument is a hipStream_t passed as void* (NULL = default stream).
  * The handle owns a device workspace (the intermediate T [M, I], per-tile
- * ready flags, per-row-block counters, a ticket counter, a status word, and
- * for split tiles fp32 partials and per-tile arrival counters), allocated
- * by create and freed by destroy.
+ * ready flags, per-row-block counters, two sets of per-XCD tile-queue
+ * counters, a status word, and for split tiles fp32 partials and per-tile
+ * arrival counters), allocated by create and freed by destroy.
  *
  * Concurrency: runs on one handle must be ordered on one stream (they share
  * the workspace); separate handles are independent.  All entry points are
