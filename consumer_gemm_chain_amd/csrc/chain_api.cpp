@@ -76,6 +76,8 @@ struct mlp_chain {
     uint32_t* rowcnt;
     uint32_t* cnt1;
     uint32_t* cnt2;
+    uint32_t* rdy1;
+    uint32_t* rdy2;
     uint32_t* ticket;
     uint32_t* status;
     uint16_t* zero;
@@ -362,7 +364,7 @@ int zero_workspace(mlp_chain* h) {
 }
 
 // Allocate (or re-allocate) and zero the workspace for the current plan:
-//   T [M, I] | flags | rowcnt | cnt1 | cnt2 | ticket | status | zero page | part1 | part2
+//   T [M, I] | flags | rowcnt | cnt1 | cnt2 | rdy1 | rdy2 | ticket | status | zero page | part1 | part2
 // (flags .. zero page is the region zeroed on create and after a timeout).
 int build_workspace(mlp_chain* h) {
     if (h->ws) {
@@ -378,7 +380,9 @@ int build_workspace(mlp_chain* h) {
     const size_t c2_b = align_up((size_t)h->T2 * 4, 256);
     const size_t p1_b = h->S1 > 1 ? align_up((size_t)h->T1 * h->S1 * acc_bytes, 256) : 0;
     const size_t p2_b = h->S2 > 1 ? align_up((size_t)h->T2 * h->S2 * acc_bytes, 256) : 0;
-    h->sync_bytes = f_b + r_b + c1_b + c2_b + TICKET_BYTES + 2 * 256;
+    const size_t y1_b = align_up((size_t)h->T1 * h->S1 * 4, 256);
+    const size_t y2_b = align_up((size_t)h->T2 * h->S2 * 4, 256);
+    h->sync_bytes = f_b + r_b + c1_b + c2_b + y1_b + y2_b + TICKET_BYTES + 2 * 256;
     h->ws_bytes = t_b + h->sync_bytes + p1_b + p2_b;
     hipError_t e = hipMalloc(&h->ws, h->ws_bytes);
     if (e != hipSuccess) {
@@ -396,6 +400,10 @@ int build_workspace(mlp_chain* h) {
     p += c1_b;
     h->cnt2 = reinterpret_cast<uint32_t*>(p);
     p += c2_b;
+    h->rdy1 = reinterpret_cast<uint32_t*>(p);
+    p += y1_b;
+    h->rdy2 = reinterpret_cast<uint32_t*>(p);
+    p += y2_b;
     h->ticket = reinterpret_cast<uint32_t*>(p);            // 2 sets of 8 queue counters, 256 B apart
     h->status = reinterpret_cast<uint32_t*>(p + TICKET_BYTES);
     h->zero = reinterpret_cast<uint16_t*>(p + TICKET_BYTES + 256);
@@ -440,6 +448,8 @@ mlpc::ChainArgs make_args(const mlp_chain* h, const void* x, const void* w1, con
     a.part2 = h->part2;
     a.cnt1 = h->cnt1;
     a.cnt2 = h->cnt2;
+    a.rdy1 = h->rdy1;
+    a.rdy2 = h->rdy2;
     a.epoch = h->epoch;
     a.grid = h->grid;
     a.spin_limit = h->spin_limit;

@@ -88,6 +88,8 @@ struct ChainArgs {
     float* part2;           // [T2][S2][tile accumulators] (S2 > 1)
     uint32_t* cnt1;         // [T1] part arrivals (S1 > 1), zero between executions
     uint32_t* cnt2;         // [T2] part arrivals (S2 > 1), zero between executions
+    uint32_t* rdy1;         // [T1 * S1] part published (S1 > 1), zero between executions
+    uint32_t* rdy2;         // [T2 * S2] part published (S2 > 1), zero between executions
     uint64_t* trace;        // optional timeline: 4 words per ticket (nullptr = off)
     uint32_t epoch;         // this run's epoch (mod 2^32)
     uint32_t grid;          // persistent workgroups
@@ -1040,16 +1042,18 @@ __device__ __forceinline__ TileJob consumer_job(const ChainArgs& a, uint32_t mb,
                    a.I, ks0, ks1, false};
 }
 
-// Split-K: store this part's accumulators (fp32, in register order so every
-// thread writes and later reads its own 16-byte slots), count the part in
-// with an agent-scope acquire-release, and, in the part that arrives last,
-// set the tile's counter back to zero (every part of this execution has
-// counted in, so the next execution starts from zero: no host-side
-// generation, and a captured stream-ordered graph replays correctly) and
-// replace the accumulators by the sum of all S partials in part order.
-// Returns true in the last part (which then runs the epilogue).
+// Split-K for tiles of more than 16 fragments per thread, whose
+// accumulators leave no room for a running sum beside them: every part
+// stores its accumulators (fp32, in register order so every thread writes
+// and later reads its own 16-byte slots) and counts in with an agent-scope
+// release; the part that arrives last sets the tile's counter back to zero
+// (every part of this execution has counted in, so the next execution
+// starts from zero: no host-side generation, and a captured stream-ordered
+// graph replays correctly) and replaces the accumulators by the sum of all
+// S partials in part order.  Returns true in the last part (which then runs
+// the epilogue).  (The ready-word form below was 4% slower on these tiles.)
 template <class C>
-__device__ __forceinline__ bool split_reduce(f32x4 (&acc)[C::FM][C::FN], float* part, uint32_t* cnt,
+__device__ __forceinline__ bool split_reduce_release(f32x4 (&acc)[C::FM][C::FN], float* part, uint32_t* cnt,
                                              uint32_t tile, uint32_t s, uint32_t S, uint32_t* s_flag) {
     constexpr int NF = C::FM * C::FN;
     const int tid = threadIdx.x;
@@ -1104,6 +1108,116 @@ __device__ __forceinline__ bool split_reduce(f32x4 (&acc)[C::FM][C::FN], float* 
     return true;
 }
 
+// Split-K for tiles of at most 16 fragments per thread.  Every part first
+// counts in (relaxed atomic add on the tile's counter); the part that
+// brings the count to S is the reducing part and
+// sets the counter back to zero (every part of this execution has counted
+// in, so the next execution starts from zero: no host-side generation, and a
+// captured stream-ordered graph replays correctly).  Each other part stores
+// its accumulators (fp32, in register order so every thread writes and the
+// reducing part's same thread reads its own 16-byte slots), releases them at
+// agent scope (the L2 write-back that makes them visible to any XCD) and
+// sets its ready word.  The reducing part waits for the S-1 ready words
+// (those parts have counted in, so they are running and publish without
+// waiting on anything), sets them back to zero, and sums all S partials in
+// part order with its own accumulators in their place: the same values in
+// the same order as summing S stored partials, so every policy and split
+// placement gives the same bits.  Only S-1 parts per tile store and write
+// back, and the reducing part never does.  Returns true in the reducing
+// part (which then runs the epilogue).  The publishing parts finish within
+// a few microseconds of each other, so the reducing part polls at most
+// every 4 x 64 clocks.
+constexpr uint32_t READY_POLL_MAX_UNITS = 4;
+
+template <class C>
+__device__ __forceinline__ bool split_reduce(f32x4 (&acc)[C::FM][C::FN], float* part, uint32_t* cnt, uint32_t* rdy,
+                                             uint32_t tile, uint32_t s, uint32_t S, uint32_t* s_flag,
+                                             uint32_t* status, uint32_t limit) {
+    constexpr int NF = C::FM * C::FN;
+    if constexpr (NF > 16) {
+        (void)rdy; (void)status; (void)limit;
+        return split_reduce_release<C>(acc, part, cnt, tile, s, S, s_flag);
+    }
+    const int tid = threadIdx.x;
+    f32x4* base = reinterpret_cast<f32x4*>(part) + (size_t)tile * S * NF * C::NT;
+    uint32_t* ready = rdy + (size_t)tile * S;
+    if (tid == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = old + 1u == S;
+        if (last) __hip_atomic_store(cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *s_flag = last ? 1u : 0u;
+    }
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(*s_flag) == 0) {
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn)
+                base[((size_t)s * NF + fm * C::FN + fn) * C::NT + tid] = acc[fm][fn];
+        // every thread's partial happens before thread 0's agent-scope release
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __syncthreads();
+        if (tid == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __hip_atomic_store(ready + s, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        return false;
+    }
+    if ((tid >> 6) == 0) {
+        // wave 0: lane p waits for part p's ready word (p != s), with back-off;
+        // gives up only if the watchdog fires (status records it)
+        const uint32_t p = tid & 63;
+        const bool mine = p < S && p != s;
+        uint32_t polls = 0, units = 1;
+        for (;;) {
+            const bool ok = !mine || __hip_atomic_load(ready + p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+            if (__ballot(!ok) == 0) break;
+            if (++polls >= limit || atomic_load_relaxed(status) != 0) {
+                if (tid == 0) __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            for (uint32_t i = 0; i < units; ++i) __builtin_amdgcn_s_sleep(1);
+            if (units < READY_POLL_MAX_UNITS) units <<= 1;
+        }
+        if (mine) __hip_atomic_store(ready + p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        handoff_acquire();
+    }
+    __syncthreads();
+    // Sum in part order (p = 0, 1, .., S-1), in row groups of at most 8
+    // fragments: the running sum and one group of loaded values beside the
+    // accumulators.  Every load of a group is issued before any is used.
+    constexpr int GR = 8 / C::FN < 1 ? 1 : (8 / C::FN < C::FM ? 8 / C::FN : C::FM);
+    static_assert(C::FM % GR == 0, "row groups");
+#pragma unroll
+    for (int r0 = 0; r0 < C::FM; r0 += GR) {
+        f32x4 sum[GR][C::FN];
+        for (uint32_t p = 0; p < S; ++p) {
+            f32x4 v[GR][C::FN];
+            if (p == s) {
+#pragma unroll
+                for (int r = 0; r < GR; ++r)
+#pragma unroll
+                    for (int fn = 0; fn < C::FN; ++fn) v[r][fn] = acc[r0 + r][fn];
+            } else {
+                const f32x4* src = base + (size_t)p * NF * C::NT + tid;
+#pragma unroll
+                for (int r = 0; r < GR; ++r)
+#pragma unroll
+                    for (int fn = 0; fn < C::FN; ++fn) v[r][fn] = src[(size_t)((r0 + r) * C::FN + fn) * C::NT];
+            }
+#pragma unroll
+            for (int r = 0; r < GR; ++r)
+#pragma unroll
+                for (int fn = 0; fn < C::FN; ++fn) sum[r][fn] = p == 0 ? v[r][fn] : sum[r][fn] + v[r][fn];
+        }
+#pragma unroll
+        for (int r = 0; r < GR; ++r)
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn) acc[r0 + r][fn] = sum[r][fn];
+    }
+    return true;
+}
+
 // One tile part of either GEMM.  ROLE 1 = producer (X W1 -> act -> T),
 // 2 = consumer (T W2 -> Y); `wait` is only exercised by consumers.  The role
 // is a template parameter so that each role gets its own main loop compiled
@@ -1120,8 +1234,8 @@ __device__ __forceinline__ bool run_tile(const ChainArgs& a, uint32_t mb, uint32
     tile_mainloop<C, DT>(j, acc, wait);
     const uint32_t S = ROLE == 1 ? a.S1 : a.S2;
     if (S > 1) {
-        const bool last = ROLE == 1 ? split_reduce<C>(acc, a.part1, a.cnt1, tile, s, S, s_flag)
-                                    : split_reduce<C>(acc, a.part2, a.cnt2, tile, s, S, s_flag);
+        const bool last = ROLE == 1 ? split_reduce<C>(acc, a.part1, a.cnt1, a.rdy1, tile, s, S, s_flag, a.status, a.spin_limit)
+                                    : split_reduce<C>(acc, a.part2, a.cnt2, a.rdy2, tile, s, S, s_flag, a.status, a.spin_limit);
         if (!last) return false;
     }
     if constexpr (ROLE == 1)
