@@ -48,8 +48,9 @@
  * stream argument is a hipStream_t passed as void* (NULL = default stream).
  * The handle owns a device workspace (the intermediate T [M, I], per-tile
  * ready flags, per-row-block counters, two sets of per-XCD tile-queue
- * counters, a status word, and for split tiles fp32 partials and per-tile
- * arrival counters), allocated by create and freed by destroy.
+ * counters, a status word, and for split tiles fp32 partials, per-tile
+ * arrival counters and per-part ready words), allocated by create and freed
+ * by destroy.
  *
  * Concurrency: runs on one handle must be ordered on one stream (they share
  * the workspace); separate handles are independent.  All entry points are
