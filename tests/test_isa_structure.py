@@ -126,3 +126,30 @@ def test_k_loops_keep_accumulators_in_place_and_use_scalar_base_dma(asm):
                 assert "v_accvgpr_mov" not in text and "v_accvgpr_read" not in text, name
                 assert "scratch_" not in text, name
             assert re.search(r"global_load_lds_dwordx4 v\d+, s\[\d+:\d+\]", body), name
+
+
+# Register spills per kernel, from the code-object metadata.  Only the
+# persistent kernel of the 256 x 256 configuration spills (per-tile setup and
+# epilogue, outside its K loops: about 120 VGPRs); a change that makes any
+# other kernel spill, or this one spill much more, has been seen to halve the
+# kernel's speed with every output still correct.
+SPILL_CAP_PERSISTENT_256x256 = 160
+
+
+def _spills(text):
+    for m in re.finditer(r"- \.agpr_count:.*?\.wavefront_size:", text, flags=re.S):
+        entry = m.group(0)
+        name = re.search(r"\.name:\s+(\S+)", entry)
+        spill = re.search(r"\.vgpr_spill_count:\s+(\d+)", entry)
+        if name and spill:
+            yield name.group(1), int(spill.group(1))
+
+
+def test_register_spills_stay_bounded(asm):
+    seen = 0
+    for name, spill in _spills(asm):
+        seen += 1
+        big = "chain_persistent_kernel" in name and "TileCfgILi256ELi256E" in name
+        cap = SPILL_CAP_PERSISTENT_256x256 if big else 0
+        assert spill <= cap, (name, spill, cap)
+    assert seen > 0, "no kernel metadata found"
