@@ -21,8 +21,18 @@ best isolated GEMM1 and GEMM2 times).  Then the dominant kernel's roofline
 position measured with HIP events, and the CPU oracle timed on a bounded
 sample of rows.
 
-Prints ONE JSON line.  Inputs are seeded synthetic data of the workload's
-shapes (no trained weights).
+Prints ONE short JSON line on stdout (a few KB: the headline, the
+baselines, the roofline position, the CPU baseline and a compact table of
+the sweep); the full per-policy sweep rows go to stderr, one JSON object per
+line, and to --sweep-out if given.  Inputs are seeded synthetic data of the
+workload's shapes (no trained weights).
+
+    python bench.py --kernels-only     only the headline policy and the planned
+                                       stream-ordered pair (for profiler runs)
+    python bench.py --copy-mib 1024    only a device copy of that size, three
+                                       times (calibration of the memory-traffic
+                                       counters: FETCH_SIZE / WRITE_SIZE of a
+                                       copy of known size)
 """
 from __future__ import annotations
 
@@ -135,6 +145,14 @@ def event_times(fn, n, stream, flush=None):
     return np.array(ts)
 
 
+def sweep_reps(M, reps):
+    """Timed runs per point: at least 50 where a run is short (M <= 512),
+    20 otherwise, unless --sweep-reps fixes the count."""
+    if reps > 0:
+        return reps
+    return 50 if M <= 512 else 20
+
+
 def sweep(runner, Ms, reps, stream, flush_buf):
     """Per (M, policy): median event time hot (weights left in the caches by
     the previous run) and cold (512 MB written between runs, so the 256 MB
@@ -146,6 +164,7 @@ def sweep(runner, Ms, reps, stream, flush_buf):
     flush = lambda: flush_buf.add_(1)  # noqa: E731
     rows = []
     for M in Ms:
+        n = sweep_reps(M, reps)
         x, w1, w2, out = runner.args(M)
         res = {}
         with runner.chain(M, "stream_ordered") as so:
@@ -153,28 +172,28 @@ def sweep(runner, Ms, reps, stream, flush_buf):
                 so.run_phase(1, x=x, w1=w1)
                 so.run_phase(2, w2=w2, out=out)
             torch.cuda.synchronize()
-            g1 = np.median(event_times(lambda: so.run_phase(1, x=x, w1=w1), reps, stream))
-            g2 = np.median(event_times(lambda: so.run_phase(2, w2=w2, out=out), reps, stream))
+            g1 = np.median(event_times(lambda: so.run_phase(1, x=x, w1=w1), n, stream))
+            g2 = np.median(event_times(lambda: so.run_phase(2, w2=w2, out=out), n, stream))
         for pol in POLICIES:
             with runner.chain(M, pol) as ch:
                 for _ in range(3):
                     ch.run(x, w1, w2, out)
                 torch.cuda.synchronize()
-                ts = event_times(lambda: ch.run(x, w1, w2, out), reps, stream)
-                tc = event_times(lambda: ch.run(x, w1, w2, out), reps, stream, flush)
+                ts = event_times(lambda: ch.run(x, w1, w2, out), n, stream)
+                tc = event_times(lambda: ch.run(x, w1, w2, out), n, stream, flush)
                 assert ch.status() == 0
                 info = ch.info()
             res[pol] = (float(np.median(ts)), float(np.percentile(ts, 10)), float(np.percentile(ts, 90)),
                         float(np.median(tc)), info)
         t_roof, bound = roofline_time_us(w, M, w.dtype)
         t_so, t_so_cold = res["stream_ordered"][0], res["stream_ordered"][3]
-        t_best, b_cfg, b_s1, b_s2 = best_stream_ordered(runner, M, stream, max(5, reps // 2))
+        t_best, b_cfg, b_s1, b_s2 = best_stream_ordered(runner, M, stream, max(5, n // 4))
         with runner.chain(M, "stream_ordered") as sb:
             sb.set_config(b_cfg)
             sb.set_split(b_s1, b_s2)
             sb.run(x, w1, w2, out)
-            t_best = min(t_best, float(np.median(event_times(lambda: sb.run(x, w1, w2, out), reps, stream))))
-            t_best_cold = float(np.median(event_times(lambda: sb.run(x, w1, w2, out), reps, stream, flush)))
+            t_best = min(t_best, float(np.median(event_times(lambda: sb.run(x, w1, w2, out), n, stream))))
+            t_best_cold = float(np.median(event_times(lambda: sb.run(x, w1, w2, out), n, stream, flush)))
         # the planned pair is one of the searched plans: the fastest is never slower than it
         so_info = res["stream_ordered"][4]
         if t_so < t_best:
@@ -183,9 +202,11 @@ def sweep(runner, Ms, reps, stream, flush_buf):
         for pol in POLICIES:
             t, p10, p90, tcold, info = res[pol]
             rows.append({
-                "M": M, "policy": pol, "us": round(t, 2), "p10_us": round(p10, 2), "p90_us": round(p90, 2),
+                "workload": w.name, "M": M, "policy": pol, "reps": n,
+                "us": round(t, 2), "p10_us": round(p10, 2), "p90_us": round(p90, 2),
                 "us_cold": round(tcold, 2),
                 "tflops": round(w.flops(M) / (t * 1e-6) / 1e12, 2),
+                "tflops_cold": round(w.flops(M) / (tcold * 1e-6) / 1e12, 2),
                 "gbs": round(w.bytes(M) / (t * 1e-6) / 1e9, 1),
                 "gbs_cold": round(w.bytes(M) / (tcold * 1e-6) / 1e9, 1),
                 "roofline_frac": round(t_roof / t, 4), "roofline_frac_cold": round(t_roof / tcold, 4),
@@ -198,13 +219,36 @@ def sweep(runner, Ms, reps, stream, flush_buf):
                                         "config": b_cfg, "S1": b_s1, "S2": b_s2},
                 "overhead_vs_best_unsplit_us": round(t - (g1 + g2), 2),
                 "tiles": [info["T1"], info["T2"]], "tile": [info["BM"], info["BN1"]],
-                "split": [info["S1"], info["S2"]],
+                "config": info["config"], "split": [info["S1"], info["S2"]],
             })
-        log(f"M={M:5d} g1={g1:8.1f}us g2={g2:8.1f}us  " + "  ".join(
+            log(json.dumps(rows[-1]))
+        log(f"{w.name} M={M:5d} g1={g1:8.1f}us g2={g2:8.1f}us  " + "  ".join(
             f"{p}={res[p][0]:8.1f}/{res[p][3]:8.1f}us" for p in POLICIES)
             + f"  best stream_ordered={t_best:8.1f}/{t_best_cold:8.1f}us (config {b_cfg}, split {b_s1},{b_s2})"
             + "  (hot/cold)")
     return rows
+
+
+# Columns of the compact sweep table in the stdout line (one row per
+# workload and M, for the tile_sync policy).
+SUMMARY_COLUMNS = ("workload", "M", "tile_sync_us", "tile_sync_us_cold", "best_pair_us", "best_pair_us_cold",
+                   "speedup_vs_best_pair", "speedup_vs_best_pair_cold", "speedup_vs_same_split_pair",
+                   "roofline_frac_cold", "bound")
+SHORT_NAMES = {"tiny_gelu_f16": "tiny", "gpt3_175b_mlp_tp8_f16": "gpt3", "llama65b_swiglu_tp8_f16": "llama65",
+               "llama2_70b_swiglu_tp8_bf16": "llama2", "stress_square_chain_bf16": "stress8192"}
+
+
+def sweep_summary(rows):
+    out = []
+    for r in rows:
+        if r["policy"] != "tile_sync":
+            continue
+        b = r["stream_ordered_best"]
+        out.append([SHORT_NAMES.get(r["workload"], r["workload"]), r["M"], round(r["us"], 1),
+                    round(r["us_cold"], 1), round(b["us"], 1), round(b["us_cold"], 1),
+                    round(r["speedup_vs_stream_ordered_best"], 3), round(r["speedup_vs_stream_ordered_best_cold"], 3),
+                    round(r["speedup_vs_stream_ordered"], 3), round(r["roofline_frac_cold"], 3), r["bound"]])
+    return out
 
 
 SO_SPLITS = tuple((s1, s2) for s1 in (1, 2, 3, 4) for s2 in (1, 2))
@@ -241,6 +285,26 @@ def best_stream_ordered(runner, M, stream, reps):
     return best
 
 
+def host_cpu_model() -> str:
+    """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(runner, M, budget_s=12.0):
     """The oracle as it stands, on a bounded sample of the workload's rows."""
     from oracle import oracle
@@ -256,9 +320,98 @@ def cpu_baseline(runner, M, budget_s=12.0):
             break
         R = min(M, R * 2)
     tflops = w.flops(R) / dt / 1e12
-    return {"value": tflops, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": round(tflops, 5), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "nproc": os.cpu_count(), "cpu_model": host_cpu_model(),
             "sample": f"{w.name}: first {R} of {M} rows in one call ({dt:.2f} s, weights widened "
                       f"inside the call), throughput scaled per row"}
+
+
+def copy_calibration(mib: int, reps: int = 3) -> None:
+    """A plain device-to-device copy of `mib` MiB, `reps` times: under
+    rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) each copy dispatch reads and
+    writes exactly that many bytes, which calibrates the counters."""
+    import torch
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copied {mib} MiB x {reps}")
+
+
+def timed_loop(ch, args, steps, stream):
+    """Host wall time of `steps` back-to-back runs, and each run's event time."""
+    import torch
+    x, w1, w2, out = args
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        ch.run(x, w1, w2, out)
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    return wall, kern
+
+
+def roofline_entry(w, M, policy, info, kern_us):
+    """Roofline position of the dominant kernel from its mean event time."""
+    F = w.flops(M)
+    t_roof, bound = roofline_time_us(w, M, w.dtype)
+    achieved = F / (kern_us * 1e-6) / 1e12
+    roof = {"bound": bound,
+            "kernel": f"chain_persistent_kernel ({policy})" if policy != "stream_ordered"
+            else "gemm1_act_kernel + gemm2_kernel",
+            "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS[w.dtype], "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_MFMA_TFLOPS[w.dtype], 4),
+            "kernel_us": round(kern_us, 2),
+            "traffic": measured_traffic("chain_persistent_kernel" if policy != "stream_ordered" else "gemm_pair",
+                                        w.name, M, f"config {info['config']} split {info['S1']},{info['S2']}"),
+            "algorithmic_flops_per_launch": F, "algorithmic_bytes_per_launch": w.bytes(M),
+            "roofline_time_us": round(t_roof, 2), "frac_of_roofline_time": round(t_roof / kern_us, 4)}
+    if bound == "hbm":
+        gbs = w.bytes(M) / (kern_us * 1e-6) / 1e9
+        roof.update({"achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4)})
+    return roof
+
+
+def graph_replay_time(runner, M, plan, steps, warmup, stream):
+    """Wall time of `steps` replays of the stream-ordered pair of `plan`
+    (config, S1, S2) captured as a HIP graph: the same two kernels without
+    host launch gaps (the stream-ordered launches depend on nothing the host
+    changes per run)."""
+    import torch
+    x, w1, w2, out = runner.args(M)
+    with runner.chain(M, "stream_ordered") as sg:
+        sg.set_config(plan[0])
+        sg.set_split(plan[1], plan[2])
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                sg.run(x, w1, w2, out)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            sg.run(x, w1, w2, out)
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        assert sg.status() == 0
+        del graph
+    return wall
 
 
 def main():
@@ -269,11 +422,19 @@ def main():
     ap.add_argument("--workload", type=int, default=1)
     ap.add_argument("--M", type=int, default=2048)
     ap.add_argument("--policy", default="tile_sync", choices=POLICIES)
-    ap.add_argument("--sweep-reps", type=int, default=20)
+    ap.add_argument("--sweep-reps", type=int, default=0,
+                    help="timed runs per sweep point (0: 50 for M <= 512, else 20)")
     ap.add_argument("--sweep-workloads", default="1,2,3,4",
                     help="workloads swept over their M lists (the headline workload up to --M)")
+    ap.add_argument("--sweep-out", default=None, help="also write the full sweep rows to this JSON file")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work the CPU baseline aims at (bounded sample of rows)")
+    ap.add_argument("--kernels-only", action="store_true",
+                    help="only the headline policy and the planned stream-ordered pair (profiler runs)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only a device copy of this many MiB, three times (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -287,135 +448,72 @@ def main():
     load_library()   # fails loudly if the HIP library is not built
     assert torch.cuda.is_available(), "bench.py needs a GPU"
 
+    if args.copy_mib > 0:
+        copy_calibration(args.copy_mib)
+        return
+
     w = gen.WORKLOADS[args.workload]
     M = args.M
-    sweep_Ms = [m for m in w.Ms if m <= M] if not args.no_sweep else []
+    quick = args.kernels_only
+    sweep_Ms = [m for m in w.Ms if m <= M] if not (args.no_sweep or quick) else []
     runner = Runner(w, max(M, max(sweep_Ms) if sweep_Ms else M))
     stream = torch.cuda.current_stream()
-    x, w1, w2, out = runner.args(M)
+    hargs = runner.args(M)
+    x, w1, w2, out = hargs
 
-    def timed_loop(ch, steps):
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        t0 = time.perf_counter()
-        for a, b in ev:
-            a.record(stream)
-            ch.run(x, w1, w2, out)
-            b.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        kern = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
-        return wall, kern
-
-    # The stream-ordered two-kernel baseline is timed both before and after
-    # the headline block and averaged: the GPU clock drifts with power and
-    # temperature over a run (1.7 - 2.1 GHz measured), which would otherwise
-    # favour whichever policy runs first.
-    # The fastest stream-ordered plan (any tile configuration and K split)
-    # is the fair baseline; the planned one shares the fused policies' split
-    # and is their bit-exact reference.
-    _, bcfg, bs1, bs2 = best_stream_ordered(runner, M, stream, 10)
-    so_best = runner.chain(M, "stream_ordered")
-    so_best.set_config(bcfg)
-    so_best.set_split(bs1, bs2)
+    # The stream-ordered two-kernel baselines are timed both before and
+    # after the headline block and averaged: the GPU clock drifts with power
+    # and temperature over a run (1.7 - 2.1 GHz measured), which would
+    # otherwise favour whichever policy runs first.  The fastest
+    # stream-ordered plan (any tile configuration and K split) is the fair
+    # baseline; the planned one shares the fused policies' split and is
+    # their bit-exact reference.
     so = runner.chain(M, "stream_ordered")
+    so_best = None
+    if not quick:
+        _, bcfg, bs1, bs2 = best_stream_ordered(runner, M, stream, 10)
+        so_best = runner.chain(M, "stream_ordered")
+        so_best.set_config(bcfg)
+        so_best.set_split(bs1, bs2)
     for _ in range(args.warmup):
-        so.run(x, w1, w2, out)
-        so_best.run(x, w1, w2, out)
-    wall_so_a, kern_so_a = timed_loop(so, args.steps)
-    wall_sb_a, kern_sb_a = timed_loop(so_best, args.steps)
+        so.run(*hargs)
+        if so_best:
+            so_best.run(*hargs)
+    wall_so_a, kern_so_a = timed_loop(so, hargs, args.steps, stream)
+    if so_best:
+        wall_sb_a, kern_sb_a = timed_loop(so_best, hargs, args.steps, stream)
 
     # headline: the chosen policy, K timed steps after W warmup steps
     with runner.chain(M, args.policy) as ch:
         for _ in range(args.warmup):
-            ch.run(x, w1, w2, out)
-        wall, kern = timed_loop(ch, args.steps)
+            ch.run(*hargs)
+        wall, kern = timed_loop(ch, hargs, args.steps, stream)
         assert ch.status() == 0, "device watchdog fired during the timed steps"
         info = ch.info()
     ms_per_step = wall / args.steps * 1e3
     F = w.flops(M)
     value = F / (ms_per_step * 1e-3) / 1e12
 
-    wall_sb_b, kern_sb_b = timed_loop(so_best, args.steps)
-    wall_so_b, kern_so_b = timed_loop(so, args.steps)
+    wall_so_b, kern_so_b = timed_loop(so, hargs, args.steps, stream)
     so_info = so.info()
     so.close()
-    so_best.close()
     wall_so = (wall_so_a + wall_so_b) / 2
     kern_so = np.concatenate([kern_so_a, kern_so_b])
     so_tflops = F / (wall_so / args.steps) / 1e12
-    wall_sb = (wall_sb_a + wall_sb_b) / 2
-    kern_sb = np.concatenate([kern_sb_a, kern_sb_b])
-    if wall_so < wall_sb:
-        # the planned pair is one of the searched plans: the fastest is never slower than it
-        wall_sb, kern_sb = wall_so, kern_so
-        bcfg, bs1, bs2 = so_info["config"], so_info["S1"], so_info["S2"]
-    sb_tflops = F / (wall_sb / args.steps) / 1e12
+    if so_best:
+        wall_sb_b, kern_sb_b = timed_loop(so_best, hargs, args.steps, stream)
+        so_best.close()
+        wall_sb = (wall_sb_a + wall_sb_b) / 2
+        kern_sb = np.concatenate([kern_sb_a, kern_sb_b])
+        if wall_so < wall_sb:
+            # the planned pair is one of the searched plans: the fastest is never slower than it
+            wall_sb, kern_sb = wall_so, kern_so
+            bcfg, bs1, bs2 = so_info["config"], so_info["S1"], so_info["S2"]
+        sb_tflops = F / (wall_sb / args.steps) / 1e12
 
-    t_roof, bound = roofline_time_us(w, M, w.dtype)
-    kern_us = float(np.mean(kern))
-    achieved = F / (kern_us * 1e-6) / 1e12
-    roofline = {"bound": "mfma" if bound == "mfma" else "hbm",
-                "kernel": f"chain_persistent_kernel ({args.policy})" if args.policy != "stream_ordered"
-                else "gemm1_act_kernel + gemm2_kernel",
-                "achieved": round(achieved, 2), "peak": PEAK_MFMA_TFLOPS[w.dtype], "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_MFMA_TFLOPS[w.dtype], 4),
-                "kernel_us": round(kern_us, 2),
-                "traffic": measured_traffic("chain_persistent_kernel" if args.policy != "stream_ordered"
-                                            else "gemm_pair", w.name, M,
-                                            f"config {info['config']} split {info['S1']},{info['S2']}"),
-                "algorithmic_flops_per_launch": F, "algorithmic_bytes_per_launch": w.bytes(M),
-                "roofline_time_us": round(t_roof, 2), "frac_of_roofline_time": round(t_roof / kern_us, 4)}
-    if bound == "hbm":
-        gbs = w.bytes(M) / (kern_us * 1e-6) / 1e9
-        roofline.update({"achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs / PEAK_HBM_GBS, 4)})
-
-    # The fastest stream-ordered plan again, captured as a HIP graph and
-    # replayed: the same two kernels without the host launch gaps (the
-    # stream-ordered launches depend on nothing the host changes per run).
-    with runner.chain(M, "stream_ordered") as sg:
-        sg.set_config(bcfg)
-        sg.set_split(bs1, bs2)
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            for _ in range(3):
-                sg.run(x, w1, w2, out)
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            sg.run(x, w1, w2, out)
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        wall_sgraph = time.perf_counter() - t0
-        assert sg.status() == 0
-        del graph
-    sgraph_tflops = F / (wall_sgraph / args.steps) / 1e12
-
-    rows = []
-    flush_buf = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda") if not args.no_sweep else None
-    if sweep_Ms:
-        rows = [{"workload": w.name, **r} for r in sweep(runner, sweep_Ms, args.sweep_reps, stream, flush_buf)]
-
-    cpu = None if args.no_cpu else cpu_baseline(runner, M)
-
-    if not args.no_sweep:
-        for wl in (int(v) for v in args.sweep_workloads.split(",") if v.strip()):
-            if wl == args.workload:
-                continue
-            del runner
-            torch.cuda.empty_cache()
-            ws = gen.WORKLOADS[wl]
-            runner = Runner(ws, ws.max_M)
-            rows += [{"workload": ws.name, **r} for r in sweep(runner, list(ws.Ms), args.sweep_reps, stream, flush_buf)]
-    del flush_buf
+    roofline = roofline_entry(w, M, args.policy, info, float(np.mean(kern)))
+    roofline["kernel_us_p10_p90"] = [round(float(np.percentile(kern, 10)), 2),
+                                     round(float(np.percentile(kern, 90)), 2)]
 
     line = {
         "metric": "MLP-chain TFLOP/s and % roofline vs stream-ordered 2-kernel, M=1..2048",
@@ -424,30 +522,58 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "M": M, "H": w.H, "I": w.I, "act": w.act, "policy": args.policy,
                    "tile": [info["BM"], info["BN1"], info["BK"]], "tiles": [info["T1"], info["T2"]],
-                   "split": [info["S1"], info["S2"]],
+                   "tile_config": info["config"], "split": [info["S1"], info["S2"]],
                    "grid": info["grid"], "parallelism": "single GPU"},
         "stream_ordered": {"value": round(so_tflops, 2), "ms_per_step": round(wall_so / args.steps * 1e3, 4),
                            "kernel_pair_us": round(float(np.mean(kern_so)), 2),
-                           "plan": {"config": so_info["config"], "S1": so_info["S1"], "S2": so_info["S2"]},
-                           "note": "planned stream-ordered pair: same K split as the fused run (bit-exact reference)"},
+                           "plan": [so_info["config"], so_info["S1"], so_info["S2"]],
+                           "note": "planned pair [config, S1, S2]: the fused run's K split (bit-exact reference)"},
         "speedup_vs_stream_ordered": round(value / so_tflops, 4),
-        "stream_ordered_best": {"value": round(sb_tflops, 2), "ms_per_step": round(wall_sb / args.steps * 1e3, 4),
-                                "kernel_pair_us": round(float(np.mean(kern_sb)), 2),
-                                "plan": {"config": bcfg, "S1": bs1, "S2": bs2},
-                                "note": "fastest stream-ordered pair over tile configurations "
-                                        f"{list(so_search_configs(M))} x splits S1 in 1..4, S2 in 1..2"},
-        "speedup_vs_stream_ordered_best": round(value / sb_tflops, 4),
-        "stream_ordered_graph": {"value": round(sgraph_tflops, 2),
-                                 "ms_per_step": round(wall_sgraph / args.steps * 1e3, 4),
-                                 "plan": {"config": bcfg, "S1": bs1, "S2": bs2},
-                                 "note": "the fastest stream-ordered pair captured as a HIP graph and replayed "
-                                         "(no host launch gaps)"},
-        "speedup_vs_stream_ordered_graph": round(value / sgraph_tflops, 4),
         "roofline": roofline,
-        "cpu_baseline": cpu,
-        "sweep": rows,
     }
-    print(json.dumps(line), flush=True)
+
+    if not quick:
+        line["stream_ordered_best"] = {
+            "value": round(sb_tflops, 2), "ms_per_step": round(wall_sb / args.steps * 1e3, 4),
+            "kernel_pair_us": round(float(np.mean(kern_sb)), 2), "plan": [bcfg, bs1, bs2],
+            "note": f"fastest pair over configs {list(so_search_configs(M))} x splits S1 1..4, S2 1..2"}
+        line["speedup_vs_stream_ordered_best"] = round(value / sb_tflops, 4)
+        wall_sgraph = graph_replay_time(runner, M, (bcfg, bs1, bs2), args.steps, args.warmup, stream)
+        sgraph_tflops = F / (wall_sgraph / args.steps) / 1e12
+        line["stream_ordered_graph"] = {"value": round(sgraph_tflops, 2),
+                                        "ms_per_step": round(wall_sgraph / args.steps * 1e3, 4),
+                                        "plan": [bcfg, bs1, bs2],
+                                        "note": "fastest pair captured as a HIP graph and replayed"}
+        line["speedup_vs_stream_ordered_graph"] = round(value / sgraph_tflops, 4)
+
+    rows = []
+    flush_buf = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda") if sweep_Ms else None
+    if sweep_Ms:
+        rows += sweep(runner, sweep_Ms, args.sweep_reps, stream, flush_buf)
+
+    line["cpu_baseline"] = None if (args.no_cpu or quick) else cpu_baseline(runner, M, args.cpu_budget)
+
+    if sweep_Ms:
+        for wl in (int(v) for v in args.sweep_workloads.split(",") if v.strip()):
+            if wl == args.workload:
+                continue
+            del runner
+            torch.cuda.empty_cache()
+            ws = gen.WORKLOADS[wl]
+            runner = Runner(ws, ws.max_M)
+            rows += sweep(runner, list(ws.Ms), args.sweep_reps, stream, flush_buf)
+    del flush_buf
+
+    if rows:
+        line["sweep_columns"] = list(SUMMARY_COLUMNS)
+        line["sweep"] = sweep_summary(rows)
+        line["sweep_note"] = ("tile_sync per workload and M: event medians hot / cold (512 MB written between "
+                              "runs); best pair = fastest stream-ordered plan over configs x splits; "
+                              "full rows of all policies on stderr")
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as fh:
+            json.dump(rows, fh, indent=1)
+    print(json.dumps(line, separators=(",", ":")), flush=True)
 
 
 if __name__ == "__main__":

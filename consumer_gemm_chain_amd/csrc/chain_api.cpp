@@ -53,6 +53,7 @@ uint32_t cdiv(int64_t a, int64_t b) { return (uint32_t)((a + b - 1) / b); }
 
 struct mlp_chain {
     int64_t M, H, I;
+    int64_t ldt;                // row stride of T: I rounded up to 64 elements
     int act, dtype, policy;
     int device;
     int cus;
@@ -364,7 +365,7 @@ int zero_workspace(mlp_chain* h) {
 }
 
 // Allocate (or re-allocate) and zero the workspace for the current plan:
-//   T [M, I] | flags | rowcnt | cnt1 | cnt2 | rdy1 | rdy2 | ticket | status | zero page | part1 | part2
+//   T [M, ldt] | flags | rowcnt | cnt1 | cnt2 | rdy1 | rdy2 | ticket | status | zero page | part1 | part2
 // (flags .. zero page is the region zeroed on create and after a timeout).
 int build_workspace(mlp_chain* h) {
     if (h->ws) {
@@ -373,7 +374,7 @@ int build_workspace(mlp_chain* h) {
         h->ws = nullptr;
     }
     const size_t acc_bytes = (size_t)h->ci.BM * h->ci.BN * 4;     // one tile's fp32 accumulators
-    const size_t t_b = align_up((size_t)h->M * (size_t)h->I * 2, 256);
+    const size_t t_b = align_up((size_t)h->M * (size_t)h->ldt * 2, 256);
     const size_t f_b = align_up((size_t)h->T1 * 4, 256);
     const size_t r_b = align_up((size_t)h->Mt * 4, 256);
     const size_t c1_b = align_up((size_t)h->T1 * 4, 256);
@@ -426,7 +427,10 @@ mlpc::ChainArgs make_args(const mlp_chain* h, const void* x, const void* w1, con
     a.M = (int)h->M;
     a.H = (int)h->H;
     a.I = (int)h->I;
+    a.ldt = (int)h->ldt;
     a.act = h->act;
+    // producer tiles narrower than 64 columns share 128-byte lines of T
+    a.acq_agent = ((h->act == MLP_ACT_SWIGLU ? h->ci.BN / 2 : h->ci.BN) % 64) != 0 ? 1u : 0u;
     a.Mt = h->Mt;
     a.N1t = h->N1t;
     a.N2t = h->N2t;
@@ -512,6 +516,7 @@ mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype
     h->M = M;
     h->H = H;
     h->I = I;
+    h->ldt = (I + 63) / 64 * 64;
     h->act = act;
     h->dtype = dtype;
     h->policy = policy;
@@ -538,7 +543,8 @@ mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype
 int mlp_chain_destroy(mlp_chain_t h) {
     if (!h) return MLP_OK;
     DeviceGuard g(h->device);
-    hipError_t e1 = hipDeviceSynchronize();
+    // the handle's work is ordered on the stream of its last run
+    hipError_t e1 = hipStreamSynchronize(h->last_stream);
     hipError_t e2 = hipFree(h->ws);
     delete h;
     if (e1 != hipSuccess || e2 != hipSuccess)
@@ -595,10 +601,11 @@ int mlp_chain_run_phase(mlp_chain_t h, int phase, const void* x, const void* w1,
 int mlp_chain_status(mlp_chain_t h) {
     if (!h) return fail(MLP_EINVAL, "NULL handle");
     DeviceGuard g(h->device);
-    hipError_t e = hipDeviceSynchronize();
-    if (e != hipSuccess) return fail(MLP_EHIP, "device error: %s", hipGetErrorString(e));
+    // the status word is read on the stream of the handle's last run, after
+    // that run: other streams of the process are not waited for
     uint32_t st = 0;
-    e = hipMemcpy(&st, h->status, sizeof st, hipMemcpyDeviceToHost);
+    hipError_t e = hipMemcpyAsync(&st, h->status, sizeof st, hipMemcpyDeviceToHost, h->last_stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(h->last_stream);
     if (e != hipSuccess) return fail(MLP_EHIP, "reading status failed: %s", hipGetErrorString(e));
     if (st != 0) {
         int rc = zero_workspace(h);
@@ -691,8 +698,8 @@ int mlp_chain_debug_set_trace(mlp_chain_t h, void* buffer) {
 int mlp_chain_debug_read_intermediate(mlp_chain_t h, void* dst, void* hip_stream) {
     if (!h || !dst) return fail(MLP_EINVAL, "mlp_chain_debug_read_intermediate needs a handle and a buffer");
     DeviceGuard g(h->device);
-    hipError_t e = hipMemcpyAsync(dst, h->t, (size_t)h->M * (size_t)h->I * 2, hipMemcpyDeviceToDevice,
-                                  static_cast<hipStream_t>(hip_stream));
+    hipError_t e = hipMemcpy2DAsync(dst, (size_t)h->I * 2, h->t, (size_t)h->ldt * 2, (size_t)h->I * 2,
+                                    (size_t)h->M, hipMemcpyDeviceToDevice, static_cast<hipStream_t>(hip_stream));
     if (e != hipSuccess) return fail(MLP_EHIP, "copy of the intermediate failed: %s", hipGetErrorString(e));
     return MLP_OK;
 }

@@ -37,7 +37,9 @@
 //   * Tile synchronization (CuSync README, opening paragraph): producer tiles
 //     publish per-tile ready flags with agent-scope release; consumer tiles
 //     poll them with relaxed agent-scope loads and s_sleep back-off, then take
-//     an agent-scope acquire fence before reading the intermediate.
+//     the hand-off acquire (handoff_acquire: ordered loads, and an L2
+//     invalidation only where producer tiles share 128-byte lines of the
+//     intermediate) before reading it.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -64,10 +66,12 @@ struct ChainArgs {
     const uint16_t* x;      // [M, H]
     const uint16_t* w1;     // [H, g*I]
     const uint16_t* w2;     // [I, H]
-    uint16_t* t;            // [M, I] intermediate (workspace)
+    uint16_t* t;            // [M, ldt] intermediate (workspace)
     uint16_t* y;            // [M, H]
     int M, H, I;
+    int ldt;                // row stride of T: I rounded up to 64 elements (whole 128-byte lines per row)
     int act;
+    uint32_t acq_agent;     // 1: producer tiles share 128-byte lines of T, hand-offs invalidate the L2
     uint32_t Mt, N1t, N2t, T1, T2;
     uint32_t rx;            // XCD grid rows (1, 2, 4 or 8; the grid is rx x 8/rx)
     uint32_t order;         // bit 0 / bit 1: GEMM1 / GEMM2 tiles walked column-major in each XCD block
@@ -296,16 +300,29 @@ __device__ __forceinline__ uint32_t wave_count_ready(const uint32_t* flags, uint
 // Acquire side of a producer -> consumer hand-off inside one launch.  The
 // producer's release (agent scope) writes its data back to memory before it
 // publishes the flag or count.  The consumer then only needs its own loads
-// ordered after the flag load it observed, not an L2 invalidation: every
-// buffer handed off this way (the intermediate T, the split-K partials) is
-// written exactly once per launch, each 128-byte line of it by exactly one
-// workgroup, and read only after that workgroup's release; the kernel
-// dispatch invalidates the caches, so no line of such a buffer from an
-// earlier launch can be cached, and no line of it is read before it is
-// written.  An agent-scope acquire fence (buffer_inv sc1) would also drop
-// every other line of the XCD's L2 -- the weight panels and activation rows
-// the co-running tiles share -- once per hand-off.
+// ordered after the flag load it observed, not an L2 invalidation, for a
+// buffer that is written exactly once per launch, each 128-byte line of it
+// by exactly one workgroup, and read only after that workgroup's release:
+// the kernel dispatch invalidates the caches, so no line of such a buffer
+// from an earlier launch can be cached, and no line of it is read before it
+// is written.  The split-K partials always qualify (each part's region is a
+// whole number of lines).  The intermediate T qualifies when each producer
+// tile's columns cover whole lines: its row stride is a multiple of 64
+// elements (the workspace pads it), so this holds when the producer tile is
+// a multiple of 64 columns wide.  Narrower producer tiles (32 columns: the
+// 16 x 64 configuration with SwiGLU) put two producers, possibly on two
+// XCDs, in one line; an XCD whose L2 holds one producer's half of a line
+// must not serve the other half from it, so those hand-offs (`agent`) take
+// the agent-scope acquire (buffer_inv sc1: the XCD's L2 is invalidated).
+// Elsewhere that invalidation would drop every other line of the XCD's L2
+// -- the weight panels and activation rows the co-running tiles share --
+// once per hand-off.
 __device__ __forceinline__ void handoff_acquire() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup"); }
+
+__device__ __forceinline__ void handoff_acquire(uint32_t agent) {
+    if (agent) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
 
 // Poll back-off: sleep `units` x 64 clocks, then double the interval up to
 // POLL_MAX_UNITS (about 1 us).  Every consumer of a row block polls the
@@ -326,7 +343,7 @@ __device__ __forceinline__ void poll_backoff(uint32_t& units) {
 // ready (> need), or n if the wait gave up (status records it).
 __device__ __forceinline__ uint32_t wave_acquire_flags(const uint32_t* flags, uint32_t from, uint32_t need,
                                                        uint32_t n, uint32_t epoch, uint32_t* status,
-                                                       uint32_t limit) {
+                                                       uint32_t limit, uint32_t agent) {
     uint32_t r = wave_count_ready(flags, from, n, epoch);
     uint32_t polls = 0, units = 1;
     while (r <= need) {
@@ -339,14 +356,14 @@ __device__ __forceinline__ uint32_t wave_acquire_flags(const uint32_t* flags, ui
             break;
         }
     }
-    handoff_acquire();
+    handoff_acquire(agent);
     return r;
 }
 
 // Called by ONE whole wave: wait until the counter reaches `target`
 // ((int32)(count - target) >= 0), then acquire.  Returns false on timeout.
 __device__ __forceinline__ bool wave_acquire_count(const uint32_t* cnt, uint32_t target, uint32_t* status,
-                                                   uint32_t limit) {
+                                                   uint32_t limit, uint32_t agent) {
     bool ok = true;
     uint32_t polls = 0, units = 1;
     while ((int32_t)(atomic_load_relaxed(cnt) - target) < 0) {
@@ -358,7 +375,7 @@ __device__ __forceinline__ bool wave_acquire_count(const uint32_t* cnt, uint32_t
             break;
         }
     }
-    handoff_acquire();
+    handoff_acquire(agent);
     return ok;
 }
 
@@ -1038,7 +1055,7 @@ template <class C>
 __device__ __forceinline__ TileJob consumer_job(const ChainArgs& a, uint32_t mb, uint32_t nb, uint32_t s) {
     int ks0, ks1;
     part_range((a.I + BK - 1) / BK, s, a.ksp2, ks0, ks1);
-    return TileJob{a.t, a.w2, a.zero, a.I, a.M, (int)mb * C::BM, a.H, a.H, (int)nb * C::BN, 0,
+    return TileJob{a.t, a.w2, a.zero, a.ldt, a.M, (int)mb * C::BM, a.H, a.H, (int)nb * C::BN, 0,
                    a.I, ks0, ks1, false};
 }
 
@@ -1239,7 +1256,7 @@ __device__ __forceinline__ bool run_tile(const ChainArgs& a, uint32_t mb, uint32
         if (!last) return false;
     }
     if constexpr (ROLE == 1)
-        tile_epilogue<C, DT>(acc, a.act, j.inter, a.t, a.I, a.M, a.I, j.m0, j.n0);
+        tile_epilogue<C, DT>(acc, a.act, j.inter, a.t, a.ldt, a.M, a.I, j.m0, j.n0);
     else
         tile_epilogue<C, DT>(acc, ACT_NONE, false, a.y, a.H, a.M, a.H, j.m0, j.n0);
     return true;

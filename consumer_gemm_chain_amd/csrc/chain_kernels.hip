@@ -68,12 +68,10 @@ __global__ __launch_bounds__(C::NT) void gemm2_kernel(ChainArgs a) {
         trace_item(a, a.T1 * a.S1 + (mb * a.N2t + nb) * a.S2 + part, t0, t0, wrote);
 }
 
-// Consumer-side wait of the persistent kernel.  One functor type serves
-// producer tiles (inactive) and consumer tiles, so the kernel holds a single
-// inlined copy of the tile main loop.  Only wave 0 polls and takes the
-// acquire fence; the result reaches the other waves through LDS behind a
-// barrier that leaves the DMA ring in flight, so one L2 invalidation covers
-// the whole workgroup.
+// Consumer-side wait of the persistent kernel.  Only wave 0 polls and takes
+// the hand-off acquire (handoff_acquire); the result reaches the other waves
+// through LDS behind a barrier that leaves the DMA ring in flight, and every
+// wave's later operand loads follow that barrier.
 //   row_sync:  before the first slab of the part, wait until all N1t
 //              producer tiles of the row block have counted themselves in
 //              for this epoch;
@@ -92,6 +90,7 @@ struct ChainWait {
     int bn1;                 // output columns per producer tile
     uint32_t* status;
     uint32_t limit;
+    uint32_t agent;          // hand-offs invalidate the L2 (producer tiles share lines of T)
     uint32_t* s_ready;       // LDS broadcast slot
     uint32_t ready;          // tile_sync: blocks below this are acquired or not needed (uniform)
     bool waited;             // row_sync: the part's single wait is done (uniform)
@@ -101,7 +100,7 @@ struct ChainWait {
         if constexpr (POL == POL_ROW) {
             if (waited) return;
             waited = true;
-            if ((threadIdx.x >> 6) == 0) wave_acquire_count(cnt, target, status, limit);
+            if ((threadIdx.x >> 6) == 0) wave_acquire_count(cnt, target, status, limit, agent);
             lds_barrier();
             t_waited = __builtin_amdgcn_s_memrealtime();
         } else {
@@ -109,7 +108,7 @@ struct ChainWait {
             if (need > n1t - 1) need = n1t - 1;
             if (need < ready) return;
             if ((threadIdx.x >> 6) == 0) {
-                const uint32_t r = wave_acquire_flags(flags, ready, need, n1t, target, status, limit);
+                const uint32_t r = wave_acquire_flags(flags, ready, need, n1t, target, status, limit, agent);
                 if (threadIdx.x == 0) *s_ready = r;
             }
             lds_barrier();
@@ -245,7 +244,7 @@ void chain_persistent_kernel(ChainArgs a) {
             const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
             ChainWait<POL> w{!prod, a.flags + mb * a.N1t, a.rowcnt + mb, a.N1t,
                              POL == POL_ROW ? a.epoch * a.N1t : a.epoch, bn1, a.status, a.spin_limit,
-                             &s_ready, first, false, t_start};
+                             a.acq_agent, &s_ready, first, false, t_start};
             bool wrote;
             if (prod) {
                 NoWait nw;

@@ -46,7 +46,9 @@
  *
  * Pointers: x, w1, w2 and out are DEVICE pointers owned by the caller.  The
  * stream argument is a hipStream_t passed as void* (NULL = default stream).
- * The handle owns a device workspace (the intermediate T [M, I], per-tile
+ * The handle owns a device workspace (the intermediate T [M, I], stored
+ * with its rows padded to a multiple of 64 elements so that every 128-byte
+ * line of it lies in one row, per-tile
  * ready flags, per-row-block counters, two sets of per-XCD tile-queue
  * counters, a status word, and for split tiles fp32 partials, per-tile
  * arrival counters and per-part ready words), allocated by create and freed
@@ -97,8 +99,12 @@ mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype
 int mlp_chain_run(mlp_chain_t h, const void* x, const void* w1, const void* w2, void* out,
                   void* hip_stream);
 
-/* Release the handle and its workspace (waits for the device first).
- * NULL-safe; returns MLP_OK, or MLP_EHIP if freeing failed. */
+/* Release the handle and its workspace.  Waits first for the stream of the
+ * handle's last run (that stream must still exist; other streams are not
+ * waited for).  NULL-safe; returns MLP_OK, or MLP_EHIP if the wait or the
+ * free failed.  (No page defines handle lifetime: create / run / destroy
+ * with policy in {stream_ordered, row_sync, tile_sync} is the interface the
+ * task statement fixes for this library.) */
 int mlp_chain_destroy(mlp_chain_t h);
 
 /* Enqueue one phase alone, with the same kernels and tiles as the
@@ -112,15 +118,21 @@ int mlp_chain_destroy(mlp_chain_t h);
 int mlp_chain_run_phase(mlp_chain_t h, int phase, const void* x, const void* w1, const void* w2,
                         void* out, void* hip_stream);
 
-/* Wait for the device to finish the handle's work, then return the sticky
- * device status: MLP_OK, or MLP_ETIMEOUT if a consumer tile gave up waiting
- * since the last call.  Reading an error also clears it and re-zeroes the
- * handle's flags and counters so that the next run starts clean.  Returns
- * MLP_EINVAL for a NULL handle and MLP_EHIP if the device reports an error. */
+/* Read the sticky device status after the handle's work: the status word
+ * is copied on the stream of the handle's last run, which is then
+ * synchronized (that stream must still exist; other streams of the process
+ * are not waited for).  Returns MLP_OK, or MLP_ETIMEOUT if a consumer tile
+ * gave up waiting since the last call.  Reading an error also clears it and
+ * re-zeroes the handle's flags and counters (a device-wide synchronization,
+ * on this recovery path only) so that the next run starts clean.  Returns
+ * MLP_EINVAL for a NULL handle and MLP_EHIP if the device reports an error.
+ * (The pages give no failure model; the watchdog and this status word are
+ * this library's own, as the benchmark spec's error contract asks.) */
 int mlp_chain_status(mlp_chain_t h);
 
 /* Message describing the last failed call on this thread ("" if none).  The
- * string is owned by the library and valid until the next call on the thread. */
+ * string is owned by the library and valid until the next call on the thread.
+ * (Part of the error contract the benchmark spec fixes; no page defines it.) */
 const char* mlp_chain_last_error(void);
 
 /* Plan and launch facts of a handle, for tests and measurement; fills the
@@ -209,7 +221,8 @@ int mlp_chain_debug_set_trace(mlp_chain_t h, void* buffer);
 
 /* Copy the handle's intermediate T [M, I] (as left by the last run on the
  * handle) into the caller's device buffer `dst` (M * I elements of the
- * storage dtype), enqueued on `hip_stream` after the handle's work.  For
+ * storage dtype, rows contiguous: the workspace's row padding is dropped),
+ * enqueued on `hip_stream` after the handle's work.  For
  * tests that check the intermediate itself.  Returns MLP_EINVAL for a NULL
  * handle or buffer, MLP_EHIP if the copy cannot be enqueued. */
 int mlp_chain_debug_read_intermediate(mlp_chain_t h, void* dst, void* hip_stream);

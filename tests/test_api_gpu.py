@@ -160,21 +160,24 @@ def test_watchdog_with_split_producer(policy):
 
 
 @pytest.mark.parametrize("split", [(1, 1), (3, 2)])
-def test_stream_ordered_graph_replays_match_eager(split):
+def test_stream_ordered_graph_replays_match_eager(oracle_mod, split):
     """The stream-ordered pair captured in a HIP graph (torch.cuda.CUDAGraph)
     and replayed: every replay -- with eager runs of the same handle and host
-    synchronizations in between -- gives the eager result bit for bit.  With
-    a K split this relies on the split-K arrival counters returning to zero
-    after every execution."""
+    synchronizations in between -- gives the eager result bit for bit, and
+    that result agrees with the oracle.  With a K split this relies on the
+    split-K arrival counters returning to zero after every execution."""
     import torch
+    from tests._helpers import check_against_oracle
     M, H, I = 96, 1024, 640
     x, w1, w2, dev = _inputs(M=M, H=H, I=I)
+    y_ref = oracle_mod.mlp_chain(x, w1, w2, "gelu_tanh", "f16")
     with mc.MlpChain(M, H, I, "gelu_tanh", "f16", "stream_ordered") as ch:
         ch.set_split(*split)
         ref_out = empty_dev((M, H), "f16")
         ch.run(*dev, ref_out)
         torch.cuda.synchronize()
         ref = from_dev(ref_out)
+        check_against_oracle(ref, y_ref, "f16", f"graph split {split}")
         out = empty_dev((M, H), "f16")
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())

@@ -57,3 +57,29 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_sweep_summary_of_every_workload_stays_small():
+    """The stdout line carries one compact row per (workload, M) of the
+    tile_sync sweep; with every workload's M list it stays well under the
+    few KB the driver reads back."""
+    import json
+    rows = []
+    for wl in (1, 2, 3, 4):
+        w = gen.WORKLOADS[wl]
+        for M in w.Ms:
+            for pol in ("stream_ordered", "row_sync", "tile_sync"):
+                rows.append({"workload": w.name, "M": M, "policy": pol, "us": 1234.5678, "us_cold": 1234.5678,
+                             "stream_ordered_best": {"us": 1234.5678, "us_cold": 1234.5678},
+                             "speedup_vs_stream_ordered_best": 1.02345, "speedup_vs_stream_ordered_best_cold": 1.02345,
+                             "speedup_vs_stream_ordered": 1.02345, "roofline_frac_cold": 0.43219, "bound": "mfma"})
+    s = bench.sweep_summary(rows)
+    assert len(s) == sum(len(gen.WORKLOADS[wl].Ms) for wl in (1, 2, 3, 4))
+    assert all(len(r) == len(bench.SUMMARY_COLUMNS) for r in s)
+    assert len(json.dumps(s, separators=(",", ":"))) < 2000
+
+
+def test_sweep_reps_follow_the_timing_protocol():
+    assert bench.sweep_reps(1, 0) >= 50 and bench.sweep_reps(512, 0) >= 50
+    assert bench.sweep_reps(2048, 0) >= 10
+    assert bench.sweep_reps(2048, 7) == 7
