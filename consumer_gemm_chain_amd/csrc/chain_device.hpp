@@ -143,6 +143,18 @@ struct TileCfg {
 
 // ------------------------------------------------------------------ helpers
 
+// The thread's index in the workgroup, read afresh at each use: the empty
+// volatile asm hands the compiler a new value each time, so nothing computed
+// from it can be hoisted out of the persistent kernel's item loop.  (Hoisted,
+// the per-lane DMA offsets, fragment addresses and epilogue indices of both
+// tile roles stay live across every item and the 256 x 256 configuration
+// spills them; recomputed per item they cost a few VALU instructions.)
+__device__ __forceinline__ uint32_t thread_index() {
+    uint32_t t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
 // f(std::integral_constant<int, i>) for i = I .. N-1 (compile-time indices).
 template <int I, int N, class F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -283,7 +295,7 @@ __device__ __forceinline__ uint32_t atomic_load_relaxed(const uint32_t* p) {
 // `epoch`.  Windows of 64 flags are scanned until one is not full.
 __device__ __forceinline__ uint32_t wave_count_ready(const uint32_t* flags, uint32_t from, uint32_t n,
                                                      uint32_t epoch) {
-    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t lane = thread_index() & 63;
     uint32_t r = from;
     while (r < n) {
         const uint32_t idx = r + lane;
@@ -350,7 +362,7 @@ __device__ __forceinline__ uint32_t wave_acquire_flags(const uint32_t* flags, ui
         poll_backoff(units);
         r = wave_count_ready(flags, r, n, epoch);
         if (r <= need && (++polls >= limit || atomic_load_relaxed(status) != 0)) {
-            if ((threadIdx.x & 63) == 0)
+            if ((thread_index() & 63) == 0)
                 __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             r = n;
             break;
@@ -369,7 +381,7 @@ __device__ __forceinline__ bool wave_acquire_count(const uint32_t* cnt, uint32_t
     while ((int32_t)(atomic_load_relaxed(cnt) - target) < 0) {
         poll_backoff(units);
         if (++polls >= limit || atomic_load_relaxed(status) != 0) {
-            if ((threadIdx.x & 63) == 0)
+            if ((thread_index() & 63) == 0)
                 __hip_atomic_fetch_or(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             ok = false;
             break;
@@ -494,7 +506,7 @@ struct TileDma {
 template <class C>
 __device__ __forceinline__ TileDma<C> tile_dma(const TileJob& j) {
     TileDma<C> d;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = thread_index() & 63, wave = thread_index() >> 6;
     d.a_base = reinterpret_cast<const char*>(j.A + (size_t)j.m0 * j.lda);
     d.b_base = reinterpret_cast<const char*>(j.B);
 #pragma unroll
@@ -530,7 +542,7 @@ __device__ __forceinline__ void issue_b(const TileJob& j, const TileDma<C>& d, i
         for (int q = 0; q < C::B_PER_WAVE; ++q)
             dma16(base + fresh(d.vb[q]), st + (wave * C::B_PER_WAVE + q) * 1024);
     } else {
-        const int lane = threadIdx.x & 63;
+        const int lane = thread_index() & 63;
 #pragma unroll
         for (int q = 0; q < C::B_PER_WAVE; ++q) {
             const int L0 = (wave * C::B_PER_WAVE + q) * 64;
@@ -557,7 +569,7 @@ __device__ __forceinline__ void issue_a(const TileJob& j, const TileDma<C>& d, i
         for (int q = 0; q < C::A_PER_WAVE; ++q)
             dma16(base + fresh(d.va[q]), st + (wave * C::A_PER_WAVE + q) * 1024);
     } else {
-        const int lane = threadIdx.x & 63;
+        const int lane = thread_index() & 63;
 #pragma unroll
         for (int q = 0; q < C::A_PER_WAVE; ++q) {
             const int L0 = (wave * C::A_PER_WAVE + q) * 64;
@@ -620,7 +632,7 @@ template <class C>
 __device__ __forceinline__ FragBase<C> frag_base() {
     FragBase<C> f;
     const uint32_t ring = lds_addr(lds_ring<C>());
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = thread_index() & 63, wave = thread_index() >> 6;
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int g = lane >> 4, jj = lane & 15;
     const int r = wm * C::WTM + jj;
@@ -807,7 +819,7 @@ __device__ __forceinline__ void issue_one(const TileJob& j, const TileDma<C>& d,
             dma16(base + fresh(d.vb[Q]), st + (wave * C::B_PER_WAVE + Q) * 1024);
         } else {
             const int L0 = (wave * C::B_PER_WAVE + Q) * 64;
-            const int L = L0 + (threadIdx.x & 63);
+            const int L = L0 + (thread_index() & 63);
             const int k = L / C::CPR, p = L % C::CPR;
             bool ok;
             const int gcol = b_column(j, b_chunk<C>(k, p), ok);
@@ -822,7 +834,7 @@ __device__ __forceinline__ void issue_one(const TileJob& j, const TileDma<C>& d,
             dma16(base + fresh(d.va[QA]), st + (wave * C::A_PER_WAVE + QA) * 1024);
         } else {
             const int L0 = (wave * C::A_PER_WAVE + QA) * 64;
-            const int L = L0 + (threadIdx.x & 63);
+            const int L = L0 + (thread_index() & 63);
             const int r = L >> 3, c = a_chunk(r, L & 7);
             const int gm = j.m0 + r, gk = k0 + c * 8;
             dma16((gm < j.a_rows && gk < j.K) ? j.A + (size_t)gm * j.lda + gk : j.zero, st + L0 * 16);
@@ -955,8 +967,8 @@ template <class C, int DT>
 __device__ __forceinline__ void tile_epilogue(const f32x4 (&acc)[C::FM][C::FN], int act, bool inter,
                                               uint16_t* D, int ldd, int rows, int cols, int m0, int n0) {
     char* smem = lds_ring<C>();
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int lane = thread_index() & 63;
+    const int wave = thread_index() >> 6;
     const int wm = wave / C::WN, wn = wave % C::WN;
     constexpr int LD = C::BN + 8;     // padded LDS row (elements)
     uint16_t* s = reinterpret_cast<uint16_t*>(smem);
@@ -1011,7 +1023,7 @@ __device__ __forceinline__ void tile_epilogue(const f32x4 (&acc)[C::FM][C::FN], 
             }
         }
         lds_barrier();
-        for (int q = threadIdx.x; q < C::EPI_ROWS * cpr; q += C::NT) {
+        for (int q = thread_index(); q < C::EPI_ROWS * cpr; q += C::NT) {
             const int row = q / cpr, c = q % cpr;
             const int gm = m0 + r0 + row, gn = n0 + c * 8;
             if (gm < rows && gn < cols) {
@@ -1073,7 +1085,7 @@ template <class C>
 __device__ __forceinline__ bool split_reduce_release(f32x4 (&acc)[C::FM][C::FN], float* part, uint32_t* cnt,
                                              uint32_t tile, uint32_t s, uint32_t S, uint32_t* s_flag) {
     constexpr int NF = C::FM * C::FN;
-    const int tid = threadIdx.x;
+    const int tid = thread_index();
     f32x4* base = reinterpret_cast<f32x4*>(part) + (size_t)tile * S * NF * C::NT;
 #pragma unroll
     for (int fm = 0; fm < C::FM; ++fm)
@@ -1155,7 +1167,7 @@ __device__ __forceinline__ bool split_reduce(f32x4 (&acc)[C::FM][C::FN], float* 
         (void)rdy; (void)status; (void)limit;
         return split_reduce_release<C>(acc, part, cnt, tile, s, S, s_flag);
     }
-    const int tid = threadIdx.x;
+    const int tid = thread_index();
     f32x4* base = reinterpret_cast<f32x4*>(part) + (size_t)tile * S * NF * C::NT;
     uint32_t* ready = rdy + (size_t)tile * S;
     if (tid == 0) {
