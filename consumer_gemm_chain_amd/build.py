@@ -22,7 +22,7 @@ LIB = os.path.join(LIBDIR, "libmlp_chain.so")
 BUILD = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["chain_api.cpp", "chain_dispatch.cpp"]
+SOURCES = ["chain_api.cpp", "chain_dispatch.cpp", "chain_scratch.hip"]
 KERNELS = "chain_kernels.hip"     # compiled once per tile configuration
 
 

@@ -364,15 +364,11 @@ int zero_workspace(mlp_chain* h) {
     return MLP_OK;
 }
 
-// Allocate (or re-allocate) and zero the workspace for the current plan:
+// Workspace layout of the current plan at `base` (nullptr: sizes only):
 //   T [M, ldt] | flags | rowcnt | cnt1 | cnt2 | rdy1 | rdy2 | ticket | status | zero page | part1 | part2
-// (flags .. zero page is the region zeroed on create and after a timeout).
-int build_workspace(mlp_chain* h) {
-    if (h->ws) {
-        (void)hipDeviceSynchronize();
-        (void)hipFree(h->ws);
-        h->ws = nullptr;
-    }
+// (flags .. zero page, sync_bytes long, is the region that starts at zero).
+// Sets ws_bytes and sync_bytes; with a base also every buffer pointer.
+void layout_workspace(mlp_chain* h, char* base) {
     const size_t acc_bytes = (size_t)h->ci.BM * h->ci.BN * 4;     // one tile's fp32 accumulators
     const size_t t_b = align_up((size_t)h->M * (size_t)h->ldt * 2, 256);
     const size_t f_b = align_up((size_t)h->T1 * 4, 256);
@@ -385,12 +381,8 @@ int build_workspace(mlp_chain* h) {
     const size_t y2_b = align_up((size_t)h->T2 * h->S2 * 4, 256);
     h->sync_bytes = f_b + r_b + c1_b + c2_b + y1_b + y2_b + TICKET_BYTES + 2 * 256;
     h->ws_bytes = t_b + h->sync_bytes + p1_b + p2_b;
-    hipError_t e = hipMalloc(&h->ws, h->ws_bytes);
-    if (e != hipSuccess) {
-        h->ws = nullptr;
-        return fail(MLP_ENOMEM, "hipMalloc of %zu workspace bytes failed: %s", h->ws_bytes, hipGetErrorString(e));
-    }
-    char* p = static_cast<char*>(h->ws);
+    if (!base) return;
+    char* p = base;
     h->t = reinterpret_cast<uint16_t*>(p);
     p += t_b;
     h->flags = reinterpret_cast<uint32_t*>(p);
@@ -412,6 +404,22 @@ int build_workspace(mlp_chain* h) {
     h->part1 = p1_b ? reinterpret_cast<float*>(p) : nullptr;
     p += p1_b;
     h->part2 = p2_b ? reinterpret_cast<float*>(p) : nullptr;
+}
+
+// Allocate (or re-allocate) and zero the workspace for the current plan.
+int build_workspace(mlp_chain* h) {
+    if (h->ws) {
+        (void)hipDeviceSynchronize();
+        (void)hipFree(h->ws);
+        h->ws = nullptr;
+    }
+    layout_workspace(h, nullptr);
+    hipError_t e = hipMalloc(&h->ws, h->ws_bytes);
+    if (e != hipSuccess) {
+        h->ws = nullptr;
+        return fail(MLP_ENOMEM, "hipMalloc of %zu workspace bytes failed: %s", h->ws_bytes, hipGetErrorString(e));
+    }
+    layout_workspace(h, static_cast<char*>(h->ws));
     return zero_workspace(h);
 }
 
@@ -461,6 +469,29 @@ mlpc::ChainArgs make_args(const mlp_chain* h, const void* x, const void* w1, con
     a.trace = h->trace;
     a.policy = h->policy;
     return a;
+}
+
+// The handle's sizes and defaults (no plan, no workspace yet).
+void init_handle(mlp_chain* h, int64_t M, int64_t H, int64_t I, int act, int dtype, int policy, int dev, int cus) {
+    h->M = M;
+    h->H = H;
+    h->I = I;
+    h->ldt = (I + 63) / 64 * 64;
+    h->act = act;
+    h->dtype = dtype;
+    h->policy = policy;
+    h->device = dev;
+    h->cus = cus;
+    h->forced_cfg = -1;
+    h->forced_s1 = 0;
+    h->forced_grid = 0;
+    h->forced_order = -1;
+    h->forced_s2 = 0;
+    h->spin_limit = DEFAULT_SPIN_LIMIT;
+    h->skip_producer = mlpc::NO_SKIP;
+    h->trace = nullptr;
+    h->last_stream = nullptr;
+    h->ws = nullptr;
 }
 
 // Argument checks shared by create and plan.
@@ -513,25 +544,7 @@ mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype
         fail(MLP_ENOMEM, "out of host memory");
         return nullptr;
     }
-    h->M = M;
-    h->H = H;
-    h->I = I;
-    h->ldt = (I + 63) / 64 * 64;
-    h->act = act;
-    h->dtype = dtype;
-    h->policy = policy;
-    h->device = dev;
-    h->cus = prop.multiProcessorCount;
-    h->forced_cfg = -1;
-    h->forced_s1 = 0;
-    h->forced_grid = 0;
-    h->forced_order = -1;
-    h->forced_s2 = 0;
-    h->spin_limit = DEFAULT_SPIN_LIMIT;
-    h->skip_producer = mlpc::NO_SKIP;
-    h->trace = nullptr;
-    h->last_stream = nullptr;
-    h->ws = nullptr;
+    init_handle(h, M, H, I, act, dtype, policy, dev, prop.multiProcessorCount);
     if (apply_plan(h, plan_config(M, H, I, act, policy, h->cus)) != MLP_OK || build_workspace(h) != MLP_OK) {
         if (h->ws) (void)hipFree(h->ws);
         delete h;
@@ -580,6 +593,49 @@ int mlp_chain_run(mlp_chain_t h, const void* x, const void* w1, const void* w2, 
         return rc;
     }
     return MLP_OK;
+}
+
+int mlp_chain_run_noalloc(int64_t M, int64_t H, int64_t I, int act, int dtype, int policy, const void* x,
+                          const void* w1, const void* w2, void* out, void* status, void* hip_stream) {
+    if (check_chain_args(M, H, I, act, policy) != MLP_OK) return MLP_EINVAL;
+    if (dtype != MLP_DTYPE_F16 && dtype != MLP_DTYPE_BF16) return fail(MLP_EINVAL, "unknown dtype %d", dtype);
+    if (bad_ptr(x) || bad_ptr(w1) || bad_ptr(w2) || bad_ptr(out))
+        return fail(MLP_EINVAL, "x, w1, w2 and out must be non-NULL 16-byte aligned device pointers");
+    if (((uintptr_t)status & 3u) != 0) return fail(MLP_EINVAL, "status must be a 4-byte aligned device pointer or NULL");
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return fail(MLP_EHIP, "no HIP device: %s", hipGetErrorString(e));
+    void* base = nullptr;
+    e = mlpc_scratch_address(dev, &base);
+    if (e != hipSuccess) return fail(MLP_EHIP, "device %d: scratch address lookup failed: %s", dev, hipGetErrorString(e));
+    // A handle on the stack: the same plan mlp_chain_create makes, with its
+    // workspace laid out in the static scratch instead of an allocation.
+    mlp_chain h{};
+    init_handle(&h, M, H, I, act, dtype, policy, dev, cus);
+    const int rc = apply_plan(&h, plan_config(M, H, I, act, policy, cus));
+    if (rc != MLP_OK) return rc;
+    layout_workspace(&h, nullptr);
+    if (h.ws_bytes > MLPC_SCRATCH_BYTES)
+        return fail(MLP_EINVAL, "M=%lld H=%lld I=%lld needs %zu bytes of workspace; the static scratch holds %zu "
+                    "(use mlp_chain_create / mlp_chain_run)", (long long)M, (long long)H, (long long)I,
+                    h.ws_bytes, (size_t)MLPC_SCRATCH_BYTES);
+    layout_workspace(&h, static_cast<char*>(base));
+    if (status) h.status = static_cast<uint32_t*>(status);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    // Every call starts from zeroed synchronization words (flags, counters,
+    // ready words, queue counters, status, zero page) and epoch 1, whatever
+    // an earlier call on this device left there.
+    e = mlpc_zero_words(h.flags, h.sync_bytes, h.status, s);
+    if (e != hipSuccess) return fail(MLP_EHIP, "clearing the scratch failed: %s", hipGetErrorString(e));
+    h.epoch = 1u;
+    const mlpc::ChainArgs a = make_args(&h, x, w1, w2, out);
+    if (policy == MLP_POLICY_STREAM_ORDERED) {
+        int r = launch_phase(&h, LAUNCH_GEMM1, a, s);
+        if (r == MLP_OK) r = launch_phase(&h, LAUNCH_GEMM2, a, s);
+        return r;
+    }
+    return launch_phase(&h, policy == MLP_POLICY_ROW_SYNC ? LAUNCH_ROW : LAUNCH_TILE, a, s);
 }
 
 int mlp_chain_run_phase(mlp_chain_t h, int phase, const void* x, const void* w1, const void* w2, void* out,

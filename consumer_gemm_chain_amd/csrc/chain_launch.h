@@ -23,3 +23,16 @@ hipError_t mlpc_launch(const mlpc::ChainArgs& a, int cfg, int dtype, int what, i
 
 // Resident workgroups per CU of the persistent kernel for a configuration.
 hipError_t mlpc_persistent_occupancy(int cfg, int dtype, int policy, int* per_cu);
+
+// The static device scratch of the entry point that allocates nothing
+// (chain_scratch.hip): 128 MiB per device.
+#define MLPC_SCRATCH_BYTES ((size_t)128 << 20)
+
+// Address of `device`'s copy of the scratch (looked up once per device; the
+// device must be current).
+hipError_t mlpc_scratch_address(int device, void** ptr);
+
+// Enqueue a kernel that zeroes `bytes` (a multiple of 16) at the 16-byte
+// aligned device address p, and *status if non-null (no memset node, so the
+// call may be captured into a graph).
+hipError_t mlpc_zero_words(void* p, size_t bytes, uint32_t* status, hipStream_t s);

@@ -28,7 +28,8 @@ EXPORTS = ("mlp_chain_create", "mlp_chain_run", "mlp_chain_destroy", "mlp_chain_
            "mlp_chain_status", "mlp_chain_last_error", "mlp_chain_info", "mlp_chain_plan",
            "mlp_chain_debug_set_spin_limit", "mlp_chain_debug_skip_producer",
            "mlp_chain_debug_set_config", "mlp_chain_debug_set_split", "mlp_chain_debug_set_grid",
-           "mlp_chain_debug_set_order", "mlp_chain_debug_set_trace", "mlp_chain_debug_read_intermediate")
+           "mlp_chain_debug_set_order", "mlp_chain_debug_set_trace", "mlp_chain_debug_read_intermediate",
+           "mlp_chain_run_noalloc")
 
 INFO_FIELDS = ("BM", "BN1", "BN2", "BK", "Mt", "N1t", "N2t", "T1", "T2", "grid", "wg_per_cu",
                "threads", "cus", "epoch", "config", "workspace_bytes", "S1", "S2", "ksp1", "ksp2")
@@ -85,6 +86,8 @@ def load_library(path: str | None = None):
     lib.mlp_chain_debug_set_trace.restype = ci
     lib.mlp_chain_debug_read_intermediate.argtypes = [vp, vp, vp]
     lib.mlp_chain_debug_read_intermediate.restype = ci
+    lib.mlp_chain_run_noalloc.argtypes = [i64, i64, i64, ci, ci, ci, vp, vp, vp, vp, vp, vp]
+    lib.mlp_chain_run_noalloc.restype = ci
     _lib = lib
     return lib
 
@@ -178,6 +181,14 @@ def mlp_chain_debug_set_trace(h: int, buffer: int | None) -> int:
 
 def mlp_chain_debug_read_intermediate(h: int, dst: int, hip_stream: int | None) -> int:
     return _check(load_library().mlp_chain_debug_read_intermediate(h, dst, hip_stream or None))
+
+
+def mlp_chain_run_noalloc(M: int, H: int, I: int, act: int, dtype: int, policy: int, x: int, w1: int, w2: int,
+                          out: int, status: int | None, hip_stream: int | None) -> int:
+    """One chain pass with the workspace in the library's static scratch (no
+    handle, no allocation after the first call on a device)."""
+    return _check(load_library().mlp_chain_run_noalloc(int(M), int(H), int(I), int(act), int(dtype), int(policy),
+                                                       x, w1, w2, out, status, hip_stream or None))
 
 
 # ---- convenience wrapper over torch tensors -------------------------------------

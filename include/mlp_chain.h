@@ -107,6 +107,29 @@ int mlp_chain_run(mlp_chain_t h, const void* x, const void* w1, const void* w2, 
  * task statement fixes for this library.) */
 int mlp_chain_destroy(mlp_chain_t h);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): one chain
+ * pass Y = act(X W1) W2 like mlp_chain_create + mlp_chain_run + destroy,
+ * with the same plan (so the same output bits as mlp_chain_run), but with
+ * no handle and no allocation: the workspace lives in a static device
+ * scratch of 128 MiB that the library holds on each device it runs on from
+ * the first call there until the process ends.  The first call on a device
+ * looks the scratch up (make it outside any graph capture); later calls
+ * call no allocating routine.  Each call first clears the scratch's
+ * synchronization words with a small kernel on `hip_stream` (no memset), so
+ * it does not depend on what an earlier call left there.  Calls that
+ * overlap on one device race on the scratch and must be ordered (one
+ * stream, or events).  Arguments as mlp_chain_create and mlp_chain_run;
+ * `status` is NULL or a 4-byte aligned device uint32 owned by the caller:
+ * it is zeroed when the pass starts and nonzero after it if a consumer tile
+ * gave up waiting (output then undefined).  Asynchronous.  Returns
+ * MLP_EINVAL for bad sizes, enums or pointers, or when the plan's
+ * workspace exceeds the scratch (the message gives both sizes; the
+ * 8192^3 chain's intermediate alone fills it), MLP_EHIP if the scratch
+ * lookup or a launch fails. */
+int mlp_chain_run_noalloc(int64_t M, int64_t H, int64_t I, int act, int dtype, int policy, const void* x,
+                          const void* w1, const void* w2, void* out, void* status, void* hip_stream);
+
 /* Enqueue one phase alone, with the same kernels and tiles as the
  * stream-ordered policy: phase 1 = GEMM1 + activation, writing the handle's
  * intermediate T; phase 2 = GEMM2, reading the handle's T and writing out.
