@@ -269,8 +269,9 @@ def best_stream_ordered(runner, M, stream, reps):
     x, w1, w2, out = runner.args(M)
     with runner.chain(M, "stream_ordered") as so:
         planned = (so.info()["S1"], so.info()["S2"])
+        planned_cfg = so.info()["config"]
     best = None
-    for cfg in so_search_configs(M):
+    for cfg in sorted(set(so_search_configs(M)) | {planned_cfg}):
         for s1, s2 in sorted(set(SO_SPLITS) | {planned}):
             with runner.chain(M, "stream_ordered") as so:
                 so.set_config(cfg)

@@ -246,7 +246,44 @@ int small_config(int64_t M, int64_t H, int64_t I, int act, int cus) {
     return -1;
 }
 
+// Measured plans of the benchmarked shapes (tuned_plans.inc, written by
+// consumer_gemm_chain_amd/tune.py on the GPU): one K split per shape shared
+// by every policy, and each policy's fastest tile configuration under it.
+// A plan applies only to the exact sizes and CU count it was measured on;
+// every other shape is planned by the rules below.
+struct TunedPlan {
+    int64_t M, H, I;
+    int act, cus;
+    uint32_t s1, s2;
+    int cfg[3];   // per policy: stream_ordered, row_sync, tile_sync
+};
+
+const TunedPlan TUNED[] = {
+#define MLPC_TUNED(m, h, i, act, cus, s1, s2, c0, c1, c2) {m, h, i, act, cus, s1, s2, {c0, c1, c2}},
+#include "tuned_plans.inc"
+#undef MLPC_TUNED
+    {0, 0, 0, -1, 0, 1, 1, {-1, -1, -1}},   // end of the table
+};
+
+// While set on this thread, the planner ignores the tuned table (host-only
+// plans of the rules, for tests).
+thread_local bool g_rules_only = false;
+
+struct RulesOnly {
+    bool prev;
+    explicit RulesOnly(bool on) : prev(g_rules_only) { g_rules_only = on; }
+    ~RulesOnly() { g_rules_only = prev; }
+};
+
+const TunedPlan* tuned_plan(int64_t M, int64_t H, int64_t I, int act, int cus) {
+    if (g_rules_only) return nullptr;
+    for (const TunedPlan& t : TUNED)
+        if (t.M == M && t.H == H && t.I == I && t.act == act && t.cus == cus) return &t;
+    return nullptr;
+}
+
 int plan_config(int64_t M, int64_t H, int64_t I, int act, int policy, int cus) {
+    if (const TunedPlan* tp = tuned_plan(M, H, I, act, cus)) return tp->cfg[policy];
     const int sc = small_config(M, H, I, act, cus);
     if (sc >= 0) return sc;
     uint32_t s2 = 1;
@@ -266,6 +303,11 @@ int plan_config(int64_t M, int64_t H, int64_t I, int act, int policy, int cus) {
 // GEMM1 where it applies, else the split rule above on the tiling of the
 // stream-ordered plan.
 void plan_shared_split(int64_t M, int64_t H, int64_t I, int act, int cus, uint32_t* s1, uint32_t* s2) {
+    if (const TunedPlan* tp = tuned_plan(M, H, I, act, cus)) {
+        *s1 = tp->s1;
+        *s2 = tp->s2;
+        return;
+    }
     if (small_config(M, H, I, act, cus) < 0 && fused_split_config(M, H, I, act, cus, s2) >= 0) {
         *s1 = 2;
         return;
@@ -689,14 +731,19 @@ int mlp_chain_debug_set_spin_limit(mlp_chain_t h, uint32_t limit) {
 
 int mlp_chain_plan(int64_t M, int64_t H, int64_t I, int act, int policy, int cus, int64_t* plan, int n) {
     if (!plan || n < 3) return fail(MLP_EINVAL, "mlp_chain_plan needs an array of at least 3 slots");
-    if (cus < 8) return fail(MLP_EINVAL, "cus must be >= 8, got %d", cus);
+    // cus < 0: the rules alone for -cus CUs (no tuned plan)
+    const bool rules_only = cus < 0;
+    if (rules_only) cus = -cus;
+    if (cus < 8) return fail(MLP_EINVAL, "cus must be >= 8 (or <= -8), got %d", rules_only ? -cus : cus);
+    RulesOnly scope(rules_only);
     const int rc = check_chain_args(M, H, I, act, policy);
     if (rc != MLP_OK) return rc;
     const int cfg = plan_config(M, H, I, act, policy, cus);
     const TilePlan p = tile_plan(M, H, I, act, cus, cfg, 0, 0);
     const int64_t bn1 = act == MLP_ACT_SWIGLU ? p.ci.BN / 2 : p.ci.BN;
-    const int64_t v[13] = {cfg, p.S1, p.S2, p.ci.BM, bn1, p.ci.BN, p.Mt, p.N1t, p.N2t, p.T1, p.T2, p.ksp1, p.ksp2};
-    for (int i = 0; i < n && i < 13; ++i) plan[i] = v[i];
+    const int64_t v[14] = {cfg, p.S1, p.S2, p.ci.BM, bn1, p.ci.BN, p.Mt, p.N1t, p.N2t, p.T1, p.T2, p.ksp1, p.ksp2,
+                           tuned_plan(M, H, I, act, cus) ? 1 : 0};
+    for (int i = 0; i < n && i < 14; ++i) plan[i] = v[i];
     return MLP_OK;
 }
 

@@ -140,11 +140,12 @@ def mlp_chain_info(h: int) -> dict:
     return dict(zip(INFO_FIELDS, (int(v) for v in arr)))
 
 
-PLAN_FIELDS = ("config", "S1", "S2", "BM", "BN1", "BN2", "Mt", "N1t", "N2t", "T1", "T2", "ksp1", "ksp2")
+PLAN_FIELDS = ("config", "S1", "S2", "BM", "BN1", "BN2", "Mt", "N1t", "N2t", "T1", "T2", "ksp1", "ksp2", "tuned")
 
 
 def mlp_chain_plan(M: int, H: int, I: int, act: int, policy: int, cus: int) -> dict:
-    """The plan mlp_chain_create would make on a GPU with `cus` CUs (host only)."""
+    """The plan mlp_chain_create would make on a GPU with `cus` CUs (host
+    only); a negative `cus` gives the rules' plan for -cus CUs."""
     arr = (ctypes.c_int64 * len(PLAN_FIELDS))()
     _check(load_library().mlp_chain_plan(int(M), int(H), int(I), int(act), int(policy), int(cus), arr,
                                          len(PLAN_FIELDS)))

@@ -170,16 +170,22 @@ int mlp_chain_info(mlp_chain_t h, int64_t* info, int n);
 
 /* The plan mlp_chain_create would make for these sizes on a GPU with `cus`
  * compute units, computed on the host alone (no device is touched): fills
- * the first min(n, 13) of
+ * the first min(n, 14) of
  *   { config id, S1, S2, BM, BN1, BN2, Mt, N1t, N2t, T1, T2,
- *     K slabs per GEMM1 part, K slabs per GEMM2 part }.
+ *     K slabs per GEMM1 part, K slabs per GEMM2 part,
+ *     1 if the plan comes from the tuned table, else 0 }.
+ * Shapes measured by the tuner (the library's table of tuned plans, for an
+ * exact size and CU count; the FLUX summary card's point that kernels are
+ * auto-tuned per GPU) take the measured plan; every other shape the rules.
+ * A negative `cus` plans for -cus CUs with the rules alone (the tuned table
+ * ignored), for tests of the rules.
  * The K split (S1, S2) depends on the sizes and `cus` only, never on the
  * policy, so all policies compute the same output bits; the tile
  * configuration may differ per policy.  The planner fills the last wave of
  * the GPU (the CuSync README, opening paragraph) by splitting K where a GEMM
  * has fewer tiles than CUs, and for the fused policies splits GEMM1 in two
  * where its tiles make between half a wave and one wave.  Returns MLP_EINVAL
- * for sizes, act or policy that mlp_chain_create would reject, cus < 8, a
+ * for sizes, act or policy that mlp_chain_create would reject, |cus| < 8, a
  * NULL array or n < 3. */
 int mlp_chain_plan(int64_t M, int64_t H, int64_t I, int act, int policy, int cus, int64_t* plan, int n);
 

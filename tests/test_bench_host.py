@@ -43,12 +43,14 @@ def test_traffic_summary_is_used_only_for_its_sources_and_plan(tmp_path, monkeyp
     assert bench.measured_traffic("k", "wl", 8, "config 7 split 2,1") is None     # other sources
 
 
-def test_stream_ordered_search_includes_the_planned_configurations():
+def test_stream_ordered_search_includes_the_rules_configurations():
+    """The fastest-pair search covers the configurations the rules would
+    plan (a tuned plan's configuration is added to the search at run time)."""
     from consumer_gemm_chain_amd import mlp_chain as mc
     for wl in (1, 2, 3, 4):
         w = gen.WORKLOADS[wl]
         for M in w.Ms:
-            p = mc.mlp_chain_plan(M, w.H, w.I, mc.ACTS[w.act], mc.MLP_POLICY_STREAM_ORDERED, 256)
+            p = mc.mlp_chain_plan(M, w.H, w.I, mc.ACTS[w.act], mc.MLP_POLICY_STREAM_ORDERED, -256)
             assert p["config"] in bench.so_search_configs(M), (w.name, M, p)
     assert (1, 1) in bench.SO_SPLITS and (2, 1) in bench.SO_SPLITS
 

@@ -15,7 +15,21 @@ MS = (1, 2, 15, 16, 17, 64, 100, 128, 256, 257, 512, 768, 1024, 1536, 2048, 4096
 
 
 def plan(M, H, I, act, policy, cus=CUS):
+    """The rules' plan (the tuned table left out)."""
+    return mc.mlp_chain_plan(M, H, I, mc.ACTS[act], policy, -cus)
+
+
+def planned(M, H, I, act, policy, cus=CUS):
+    """The plan create makes: a tuned plan where the table has one."""
     return mc.mlp_chain_plan(M, H, I, mc.ACTS[act], policy, cus)
+
+
+def tuned_entries():
+    import os
+    import re
+    path = os.path.join(os.path.dirname(mc.PKG), "consumer_gemm_chain_amd", "csrc", "tuned_plans.inc")
+    text = re.sub(r"//[^\n]*", "", open(path).read())
+    return [tuple(int(v) for v in m.split(",")) for m in re.findall(r"MLPC_TUNED\(([^)]*)\)", text)]
 
 
 def cdiv(a, b):
@@ -25,8 +39,8 @@ def cdiv(a, b):
 @pytest.mark.parametrize("wl", range(len(gen.WORKLOADS)))
 def test_split_shared_by_policies_and_parts_cover_k(wl):
     w = gen.WORKLOADS[wl]
-    for M, cus in itertools.product(MS, (CUS, 80, 304)):
-        plans = [plan(M, w.H, w.I, w.act, pol, cus) for pol in POLS]
+    for M, cus, fn in itertools.product(MS, (CUS, 80, 304), (plan, planned)):
+        plans = [fn(M, w.H, w.I, w.act, pol, cus) for pol in POLS]
         assert len({(p["S1"], p["S2"]) for p in plans}) == 1, (w.name, M, cus, plans)
         for p in plans:
             nks1, nks2 = cdiv(w.H, 64), cdiv(w.I, 64)
@@ -99,7 +113,23 @@ def test_large_m_has_no_split_and_large_tiles():
 def test_plan_rejects_bad_arguments(args):
     import ctypes
     lib = mc.load_library()
-    arr = (ctypes.c_int64 * 13)()
-    assert lib.mlp_chain_plan(*args, arr, 13) == mc.MLP_EINVAL
+    arr = (ctypes.c_int64 * 14)()
+    assert lib.mlp_chain_plan(*args, arr, 14) == mc.MLP_EINVAL
     assert lib.mlp_chain_plan(64, 512, 512, 1, 2, 256, None, 13) == mc.MLP_EINVAL
     assert lib.mlp_chain_plan(64, 512, 512, 1, 2, 256, arr, 2) == mc.MLP_EINVAL
+
+
+def test_tuned_table_entries_are_used_and_valid():
+    """Every measured plan in the tuned table is what create would use for
+    its exact shape and CU count (one split for every policy, each policy its
+    measured configuration); other CU counts fall back to the rules."""
+    from consumer_gemm_chain_amd import build as b
+    ncfg = b.num_configs()
+    acts = {v: k for k, v in mc.ACTS.items()}
+    for (M, H, I, act, cus, s1, s2, c0, c1, c2) in tuned_entries():
+        for pol, cfg in zip(POLS, (c0, c1, c2)):
+            assert 0 <= cfg < ncfg
+            p = planned(M, H, I, acts[act], pol, cus)
+            assert p["tuned"] == 1 and (p["config"], p["S1"], p["S2"]) == (cfg, s1, s2), (M, H, I, pol, p)
+            assert plan(M, H, I, acts[act], pol, cus)["tuned"] == 0
+        assert planned(M, H, I, acts[act], POLS[0], cus + 8)["tuned"] == 0
