@@ -118,3 +118,18 @@ def mlp_chain(x: np.ndarray, w1: np.ndarray, w2: np.ndarray, act, dtype,
     if rc != 0:
         raise RuntimeError(f"oracle_mlp_chain failed with {rc}")
     return (y, t) if want_t else y
+
+
+def mlp_layers(x: np.ndarray, w1s, w2s, act, dtype) -> np.ndarray:
+    """A chain of MLP layers, the plain composition: layer l's input is layer
+    l-1's output Y (already rounded to the storage dtype, as every chain
+    output is), Y_l = mlp_chain(Y_{l-1}, W1_l, W2_l), Y_{-1} = x.  Chaining
+    consecutive layers in one kernel (the Hacker News thread on megakernels
+    vs CUDA graphs: overlapping work across layers) changes when tiles run,
+    not what each layer computes.  Returns the last layer's Y."""
+    if len(w1s) != len(w2s) or len(w1s) < 1:
+        raise ValueError("need the same number (>= 1) of W1 and W2 matrices")
+    y = np.ascontiguousarray(x, dtype=np.uint16)
+    for w1, w2 in zip(w1s, w2s):
+        y = mlp_chain(y, w1, w2, act, dtype)
+    return y

@@ -402,3 +402,53 @@ def test_empty_and_bad_arguments(oracle_mod):
     assert y.shape == (0, 8)
     with pytest.raises(ValueError):
         oracle_mod.mlp_chain(np.zeros((2, 8), np.uint16), w1, w2, "swiglu", "f16")
+
+
+# ---- chains of several layers (the composition) ------------------------------
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_exact_integer_layers(oracle_mod, dtype):
+    """Two layers of integer weights (act none): the oracle's chain of layers
+    equals exact int64 products with the library's rounding after every GEMM,
+    layer by layer, bit for bit.  The layers' weights differ and do not
+    commute, so a swapped layer order or a layer fed the wrong input fails."""
+    M, H, I = 6, 48, 40
+    x, xi = _int_bits((M, H), 21, -3, 3, 0.8, dtype)
+    ws = [(_int_bits((H, I), 22 + 2 * l, -2, 2, 0.6, dtype), _int_bits((I, H), 23 + 2 * l, -1, 1, 0.3, dtype))
+          for l in range(2)]
+    yi = xi
+    for (w1, w1i), (w2, w2i) in ws:
+        h = yi @ w1i
+        assert (np.abs(yi) @ np.abs(w1i)).max() < 2 ** 24
+        t_int = widen_lib(_lib_round(h, dtype), dtype).astype(np.int64)
+        yv = t_int @ w2i
+        assert (np.abs(t_int) @ np.abs(w2i)).max() < 2 ** 24
+        yi = widen_lib(_lib_round(yv, dtype), dtype).astype(np.int64)
+    y = oracle_mod.mlp_layers(x, [w[0][0] for w in ws], [w[1][0] for w in ws], "none", dtype)
+    assert np.array_equal(widen_lib(y, dtype), yi.astype(np.float64))
+    swapped = oracle_mod.mlp_layers(x, [ws[1][0][0], ws[0][0][0]], [ws[1][1][0], ws[0][1][0]], "none", dtype)
+    assert not np.array_equal(swapped, y)
+
+
+@pytest.mark.parametrize("act", ["none", "gelu_tanh"])
+def test_identity_layers(oracle_mod, act):
+    """Identity W1 and W2 in every layer: with act none the chain returns X
+    exactly after three layers; with GeLU each layer applies the separately
+    pinned activation once (checked against three explicit applications)."""
+    M, H = 9, 64
+    x = gen.normal_bits((M, H), 31, 1.0, "f16")
+    eye = gen.to_bits(np.eye(H, dtype=np.float32), "f16")
+    y = oracle_mod.mlp_layers(x, [eye] * 3, [eye] * 3, act, "f16")
+    if act == "none":
+        assert np.array_equal(y, x)
+    else:
+        v = x
+        for _ in range(3):
+            v = oracle_mod.round_to(oracle_mod.act(oracle_mod.widen(v, "f16"), "gelu_tanh"), "f16")
+        assert np.array_equal(y, v)
+
+
+def test_one_layer_is_the_chain(oracle_mod):
+    x, w1, w2 = gen.random_case(5, 64, 96, "swiglu", "bf16", seed=3)
+    assert np.array_equal(oracle_mod.mlp_layers(x, [w1], [w2], "swiglu", "bf16"),
+                          oracle_mod.mlp_chain(x, w1, w2, "swiglu", "bf16"))
