@@ -286,6 +286,42 @@ def best_stream_ordered(runner, M, stream, reps):
     return best
 
 
+LAYER_MS = (16, 256, 2048)
+
+
+def layers_sweep(w, L, Ms, reps, stream):
+    """A chain of L MLP layers of the workload's shapes (own seeded weights
+    per layer) at each M: the fused policies' single persistent kernel
+    against the 2L stream-ordered kernels, event medians (hot).  The fused
+    kernel overlaps each layer's consumers with the previous layer's tail."""
+    import torch
+    from consumer_gemm_chain_amd import gen
+    from consumer_gemm_chain_amd.mlp_chain import MlpChain
+    from consumer_gemm_chain_amd.tensors import to_dev
+    g = 2 if w.act == "swiglu" else 1
+    w1s = [to_dev(gen.normal_bits((w.H, g * w.I), 9000 + 10 * l, w.w_scale, w.dtype), w.dtype) for l in range(L)]
+    w2s = [to_dev(gen.normal_bits((w.I, w.H), 9001 + 10 * l, w.w_scale, w.dtype), w.dtype) for l in range(L)]
+    xs = to_dev(gen.x_rows(w, max(Ms)), w.dtype)
+    out = torch.empty((max(Ms), w.H), dtype=xs.dtype, device="cuda")
+    rows = []
+    for M in Ms:
+        t = {}
+        for pol in POLICIES:
+            with MlpChain(M, w.H, w.I, w.act, w.dtype, pol, layers=L) as ch:
+                for _ in range(3):
+                    ch.run_layers(xs[:M], w1s, w2s, out[:M])
+                torch.cuda.synchronize()
+                t[pol] = float(np.median(event_times(lambda: ch.run_layers(xs[:M], w1s, w2s, out[:M]),
+                                                     sweep_reps(M, reps), stream)))
+                assert ch.status() == 0
+        rows.append([M, round(t["tile_sync"], 1), round(t["row_sync"], 1), round(t["stream_ordered"], 1),
+                     round(t["stream_ordered"] / t["tile_sync"], 3),
+                     round(L * w.flops(M) / (t["tile_sync"] * 1e-6) / 1e12, 1)])
+        log(f"{L} layers of {w.name} M={M}: tile_sync {t['tile_sync']:.1f} us, row_sync {t['row_sync']:.1f} us, "
+            f"{2 * L} stream-ordered kernels {t['stream_ordered']:.1f} us")
+    return rows
+
+
 def host_cpu_model() -> str:
     """The host CPU's model name (lscpu, else /proc/cpuinfo)."""
     import subprocess
@@ -429,6 +465,8 @@ def main():
                     help="workloads swept over their M lists (the headline workload up to --M)")
     ap.add_argument("--sweep-out", default=None, help="also write the full sweep rows to this JSON file")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--layers", type=int, default=2,
+                    help="MLP layers of the multi-layer chain timed after the sweep (0: none)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work the CPU baseline aims at (bounded sample of rows)")
@@ -564,6 +602,15 @@ def main():
             runner = Runner(ws, ws.max_M)
             rows += sweep(runner, list(ws.Ms), args.sweep_reps, stream, flush_buf)
     del flush_buf
+
+    layer_Ms = [m for m in LAYER_MS if m <= M]
+    if sweep_Ms and args.layers > 1 and layer_Ms:
+        del runner
+        torch.cuda.empty_cache()
+        line["layers"] = {"workload": w.name, "layers": args.layers,
+                          "columns": ["M", "tile_sync_us", "row_sync_us", "stream_ordered_us",
+                                      "speedup_vs_stream_ordered", "tile_sync_tflops"],
+                          "rows": layers_sweep(w, args.layers, layer_Ms, args.sweep_reps, stream)}
 
     if rows:
         line["sweep_columns"] = list(SUMMARY_COLUMNS)

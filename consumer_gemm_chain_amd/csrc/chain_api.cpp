@@ -54,6 +54,8 @@ uint32_t cdiv(int64_t a, int64_t b) { return (uint32_t)((a + b - 1) / b); }
 struct mlp_chain {
     int64_t M, H, I;
     int64_t ldt;                // row stride of T: I rounded up to 64 elements
+    int64_t ldy;                // row stride of the kept layer outputs: H rounded up to 64 elements
+    uint32_t layers;            // MLP layers of the chain (2 GEMMs each)
     int act, dtype, policy;
     int device;
     int cus;
@@ -73,6 +75,7 @@ struct mlp_chain {
     size_t ws_bytes;
     size_t sync_bytes;          // the zeroed region: flags .. zero page
     uint16_t* t;
+    uint16_t* ys;               // layers > 1: the outputs of every layer but the last
     uint32_t* flags;
     uint32_t* rowcnt;
     uint32_t* cnt1;
@@ -368,7 +371,7 @@ int apply_plan(mlp_chain* h, int cfg) {
     h->grid = 0;
     if (h->policy != MLP_POLICY_STREAM_ORDERED) {
         int occ = 0;
-        hipError_t e = mlpc_persistent_occupancy(cfg, h->dtype, h->policy, &occ);
+        hipError_t e = mlpc_persistent_occupancy(cfg, h->dtype, h->policy, (int)h->layers, &occ);
         if (e != hipSuccess) return fail(MLP_EHIP, "occupancy query failed: %s", hipGetErrorString(e));
         if (occ < 1) return fail(MLP_EHIP, "persistent kernel of config %d does not fit on a CU", cfg);
         h->occ = occ;
@@ -378,7 +381,7 @@ int apply_plan(mlp_chain* h, int cfg) {
         // a consumer part, so the consumers spread over the CUs the producers
         // used instead of sharing the CUs their workgroups were placed on at
         // launch.
-        const uint64_t parts = (uint64_t)h->T1 * h->S1 + (uint64_t)h->T2 * h->S2;
+        const uint64_t parts = ((uint64_t)h->T1 * h->S1 + (uint64_t)h->T2 * h->S2) * h->layers;
         uint64_t per_cu = parts / (uint64_t)h->cus;
         if (per_cu < 1) per_cu = 1;
         if (per_cu > (uint64_t)occ) per_cu = (uint64_t)occ;
@@ -406,27 +409,33 @@ int zero_workspace(mlp_chain* h) {
     return MLP_OK;
 }
 
-// Workspace layout of the current plan at `base` (nullptr: sizes only):
-//   T [M, ldt] | flags | rowcnt | cnt1 | cnt2 | rdy1 | rdy2 | ticket | status | zero page | part1 | part2
+// Workspace layout of the current plan at `base` (nullptr: sizes only), for
+// a chain of L = layers MLP layers:
+//   T [L][M, ldt] | Y [L-1][M, ldy] | flags [L T1 + (L-1) T2] | rowcnt [(2L-1) Mt] | cnt1 [L T1] |
+//   cnt2 [L T2] | rdy1 [L T1 S1] | rdy2 [L T2 S2] | ticket | status | zero page | part1 [L] | part2 [L]
 // (flags .. zero page, sync_bytes long, is the region that starts at zero).
 // Sets ws_bytes and sync_bytes; with a base also every buffer pointer.
 void layout_workspace(mlp_chain* h, char* base) {
+    const size_t L = h->layers;
     const size_t acc_bytes = (size_t)h->ci.BM * h->ci.BN * 4;     // one tile's fp32 accumulators
-    const size_t t_b = align_up((size_t)h->M * (size_t)h->ldt * 2, 256);
-    const size_t f_b = align_up((size_t)h->T1 * 4, 256);
-    const size_t r_b = align_up((size_t)h->Mt * 4, 256);
-    const size_t c1_b = align_up((size_t)h->T1 * 4, 256);
-    const size_t c2_b = align_up((size_t)h->T2 * 4, 256);
-    const size_t p1_b = h->S1 > 1 ? align_up((size_t)h->T1 * h->S1 * acc_bytes, 256) : 0;
-    const size_t p2_b = h->S2 > 1 ? align_up((size_t)h->T2 * h->S2 * acc_bytes, 256) : 0;
-    const size_t y1_b = align_up((size_t)h->T1 * h->S1 * 4, 256);
-    const size_t y2_b = align_up((size_t)h->T2 * h->S2 * 4, 256);
+    const size_t t_b = align_up(L * (size_t)h->M * (size_t)h->ldt * 2, 256);
+    const size_t ys_b = align_up((L - 1) * (size_t)h->M * (size_t)h->ldy * 2, 256);
+    const size_t f_b = align_up((L * h->T1 + (L - 1) * h->T2) * 4, 256);
+    const size_t r_b = align_up((2 * L - 1) * h->Mt * 4, 256);
+    const size_t c1_b = align_up(L * h->T1 * 4, 256);
+    const size_t c2_b = align_up(L * h->T2 * 4, 256);
+    const size_t p1_b = h->S1 > 1 ? align_up(L * h->T1 * h->S1 * acc_bytes, 256) : 0;
+    const size_t p2_b = h->S2 > 1 ? align_up(L * h->T2 * h->S2 * acc_bytes, 256) : 0;
+    const size_t y1_b = align_up(L * h->T1 * h->S1 * 4, 256);
+    const size_t y2_b = align_up(L * h->T2 * h->S2 * 4, 256);
     h->sync_bytes = f_b + r_b + c1_b + c2_b + y1_b + y2_b + TICKET_BYTES + 2 * 256;
-    h->ws_bytes = t_b + h->sync_bytes + p1_b + p2_b;
+    h->ws_bytes = t_b + ys_b + h->sync_bytes + p1_b + p2_b;
     if (!base) return;
     char* p = base;
     h->t = reinterpret_cast<uint16_t*>(p);
     p += t_b;
+    h->ys = ys_b ? reinterpret_cast<uint16_t*>(p) : nullptr;
+    p += ys_b;
     h->flags = reinterpret_cast<uint32_t*>(p);
     p += f_b;
     h->rowcnt = reinterpret_cast<uint32_t*>(p);
@@ -509,16 +518,27 @@ mlpc::ChainArgs make_args(const mlp_chain* h, const void* x, const void* w1, con
     a.spin_limit = h->spin_limit;
     a.skip_producer = h->skip_producer;
     a.trace = h->trace;
+    a.ldx = (int)h->H;
+    a.ldo = (int)h->H;
+    a.layers = h->layers;
+    a.ldy = (int)h->ldy;
+    a.ys = h->ys;
+    a.w1s[0] = a.w1;
+    a.w2s[0] = a.w2;
     a.policy = h->policy;
     return a;
 }
 
 // The handle's sizes and defaults (no plan, no workspace yet).
-void init_handle(mlp_chain* h, int64_t M, int64_t H, int64_t I, int act, int dtype, int policy, int dev, int cus) {
+void init_handle(mlp_chain* h, int64_t M, int64_t H, int64_t I, int act, int dtype, int policy, int dev, int cus,
+                 int layers = 1) {
     h->M = M;
     h->H = H;
     h->I = I;
     h->ldt = (I + 63) / 64 * 64;
+    h->ldy = (H + 63) / 64 * 64;
+    h->layers = (uint32_t)layers;
+    h->ys = nullptr;
     h->act = act;
     h->dtype = dtype;
     h->policy = policy;
@@ -563,8 +583,16 @@ extern "C" {
 const char* mlp_chain_last_error(void) { return g_err.c_str(); }
 
 mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype, int policy) {
+    return mlp_chain_create_layers(M, H, I, act, dtype, policy, 1);
+}
+
+mlp_chain_t mlp_chain_create_layers(int64_t M, int64_t H, int64_t I, int act, int dtype, int policy, int layers) {
     g_err.clear();
     if (check_chain_args(M, H, I, act, policy) != MLP_OK) return nullptr;
+    if (layers < 1 || layers > (int)mlpc::MAX_LAYERS) {
+        fail(MLP_EINVAL, "layers must be in 1..%u, got %d", mlpc::MAX_LAYERS, layers);
+        return nullptr;
+    }
     if (dtype != MLP_DTYPE_F16 && dtype != MLP_DTYPE_BF16) {
         fail(MLP_EINVAL, "unknown dtype %d", dtype);
         return nullptr;
@@ -586,7 +614,7 @@ mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype
         fail(MLP_ENOMEM, "out of host memory");
         return nullptr;
     }
-    init_handle(h, M, H, I, act, dtype, policy, dev, prop.multiProcessorCount);
+    init_handle(h, M, H, I, act, dtype, policy, dev, prop.multiProcessorCount, layers);
     if (apply_plan(h, plan_config(M, H, I, act, policy, h->cus)) != MLP_OK || build_workspace(h) != MLP_OK) {
         if (h->ws) (void)hipFree(h->ws);
         delete h;
@@ -613,8 +641,46 @@ static int launch_phase(mlp_chain_t h, int what, const mlpc::ChainArgs& a, hipSt
     return MLP_OK;
 }
 
+int mlp_chain_run_layers(mlp_chain_t h, const void* x, const void* const* w1, const void* const* w2, void* out,
+                         void* hip_stream) {
+    if (!h) return fail(MLP_EINVAL, "NULL handle");
+    if (!w1 || !w2) return fail(MLP_EINVAL, "w1 and w2 must be host arrays of the layers' weight pointers");
+    for (uint32_t l = 0; l < h->layers; ++l)
+        if (bad_ptr(w1[l]) || bad_ptr(w2[l]))
+            return fail(MLP_EINVAL, "layer %u: w1 and w2 must be non-NULL 16-byte aligned device pointers", l);
+    if (bad_ptr(x) || bad_ptr(out))
+        return fail(MLP_EINVAL, "x and out must be non-NULL 16-byte aligned device pointers");
+    if (h->layers == 1) return mlp_chain_run(h, x, w1[0], w2[0], out, hip_stream);
+    DeviceGuard g(h->device);
+    if (!g.ok) return fail(MLP_EHIP, "cannot select the handle's device %d", h->device);
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    h->last_stream = s;
+    const bool fused = h->policy != MLP_POLICY_STREAM_ORDERED;
+    if (fused) h->epoch += 1u;
+    mlpc::ChainArgs a = make_args(h, x, w1[0], w2[0], out);
+    for (uint32_t l = 0; l < h->layers; ++l) {
+        a.w1s[l] = static_cast<const uint16_t*>(w1[l]);
+        a.w2s[l] = static_cast<const uint16_t*>(w2[l]);
+    }
+    if (!fused) {
+        // 2 x layers kernels on the stream, layer by layer
+        for (uint32_t l = 0; l < h->layers; ++l) {
+            const mlpc::ChainArgs b = mlpc::layer_args(a, l, (size_t)h->ci.BM * h->ci.BN);
+            int rc = launch_phase(h, LAUNCH_GEMM1, b, s);
+            if (rc == MLP_OK) rc = launch_phase(h, LAUNCH_GEMM2, b, s);
+            if (rc != MLP_OK) return rc;
+        }
+        return MLP_OK;
+    }
+    int rc = launch_phase(h, h->policy == MLP_POLICY_ROW_SYNC ? LAUNCH_LAYERS_ROW : LAUNCH_LAYERS_TILE, a, s);
+    if (rc != MLP_OK) h->epoch -= 1u;
+    return rc;
+}
+
 int mlp_chain_run(mlp_chain_t h, const void* x, const void* w1, const void* w2, void* out, void* hip_stream) {
     if (!h) return fail(MLP_EINVAL, "NULL handle");
+    if (h->layers != 1)
+        return fail(MLP_EINVAL, "the handle chains %u layers: run it with mlp_chain_run_layers", h->layers);
     if (bad_ptr(x) || bad_ptr(w1) || bad_ptr(w2) || bad_ptr(out))
         return fail(MLP_EINVAL, "x, w1, w2 and out must be non-NULL 16-byte aligned device pointers");
     DeviceGuard g(h->device);
@@ -716,10 +782,10 @@ int mlp_chain_status(mlp_chain_t h) {
 int mlp_chain_info(mlp_chain_t h, int64_t* info, int n) {
     if (!h || !info || n < 16) return fail(MLP_EINVAL, "mlp_chain_info needs a handle and 16 slots");
     const int64_t bn1 = h->act == MLP_ACT_SWIGLU ? h->ci.BN / 2 : h->ci.BN;
-    const int64_t v[20] = {h->ci.BM, bn1, h->ci.BN, h->ci.BK, h->Mt, h->N1t, h->N2t, h->T1, h->T2,
+    const int64_t v[21] = {h->ci.BM, bn1, h->ci.BN, h->ci.BK, h->Mt, h->N1t, h->N2t, h->T1, h->T2,
                            h->grid, h->occ, h->ci.NT, h->cus, h->epoch, h->cfg, (int64_t)h->ws_bytes,
-                           h->S1, h->S2, h->ksp1, h->ksp2};
-    for (int i = 0; i < n && i < 20; ++i) info[i] = v[i];
+                           h->S1, h->S2, h->ksp1, h->ksp2, h->layers};
+    for (int i = 0; i < n && i < 21; ++i) info[i] = v[i];
     return MLP_OK;
 }
 

@@ -60,6 +60,7 @@ enum { POL_STREAM = 0, POL_ROW = 1, POL_TILE = 2 };
 
 constexpr int BK = 64;          // K slab per main-loop step (8 chunks of 8 elements)
 constexpr uint32_t NO_SKIP = 0xffffffffu;
+constexpr uint32_t MAX_LAYERS = 8;   // MLP layers of one chain (2 GEMMs each)
 
 // Kernel arguments shared by all kernels (passed by value).
 struct ChainArgs {
@@ -100,7 +101,50 @@ struct ChainArgs {
     uint32_t spin_limit;    // back-off iterations before a consumer gives up
     uint32_t skip_producer; // test hook: producer ticket that does nothing (NO_SKIP = none)
     int policy;
+    int ldx;                // row stride of x (GEMM1's A operand): H, or ldy for a later layer's input
+    int ldo;                // row stride of y (GEMM2's output): H, or ldy for a layer's output kept for the next
+    // Chains of several MLP layers (layers > 1): layer l computes
+    // Y_l = act(Y_{l-1} W1_l) W2_l with Y_{-1} = x; the fields above then
+    // describe layer 0, and layer_args() derives any layer's view.
+    uint32_t layers;
+    int ldy;                // row stride of the layer outputs kept in the workspace (H rounded up to 64)
+    uint16_t* ys;           // [layers - 1][M, ldy]: Y_0 .. Y_{layers-2} (workspace)
+    const uint16_t* w1s[MAX_LAYERS];
+    const uint16_t* w2s[MAX_LAYERS];
 };
+
+// The arguments as layer l of a multi-layer chain sees them, for the
+// stand-alone kernels of the stream-ordered policy (tile_elems: the fp32
+// accumulators of one tile of the configuration): its weights, its input
+// (x or the previous layer's output) and output (a kept layer output or y),
+// its intermediate T_l, and its own split-K counters, ready words and
+// partials -- the same buffers the multi-layer persistent kernel gives layer
+// l (run_tile with l).  Layer 0 of a one-layer chain is the arguments
+// themselves.
+inline ChainArgs layer_args(const ChainArgs& a, uint32_t l, size_t tile_elems) {
+    ChainArgs b = a;
+    const size_t M = (size_t)a.M;
+    if (l > 0) {
+        b.x = a.ys + (l - 1) * M * (size_t)a.ldy;
+        b.ldx = a.ldy;
+    }
+    if (l + 1 < a.layers) {
+        b.y = a.ys + l * M * (size_t)a.ldy;
+        b.ldo = a.ldy;
+    }
+    b.w1 = a.w1s[l];
+    b.w2 = a.w2s[l];
+    b.t = a.t + l * M * (size_t)a.ldt;
+    b.cnt1 = a.cnt1 + l * a.T1;
+    b.cnt2 = a.cnt2 + l * a.T2;
+    b.rdy1 = a.rdy1 + l * a.T1 * a.S1;
+    b.rdy2 = a.rdy2 + l * a.T2 * a.S2;
+    if (a.part1) b.part1 = a.part1 + l * (size_t)a.T1 * a.S1 * tile_elems;
+    if (a.part2) b.part2 = a.part2 + l * (size_t)a.T2 * a.S2 * tile_elems;
+    // the stand-alone kernels see one layer whose buffers are the ones above
+    b.layers = 1;
+    return b;
+}
 
 // Tile configuration: BM x BN tile, WM x WN waves of (BM/WM) x (BN/WN), NS
 // LDS stages.  BN is the number of B (weight) columns of a tile: its output
@@ -1053,22 +1097,38 @@ __device__ __forceinline__ void part_range(int nks, uint32_t s, uint32_t ksp, in
     if (ks1 > nks) ks1 = nks;
 }
 
+// Layer l's buffers (l = 0 in a one-layer chain, where they are x, t and
+// y): its input, intermediate T_l and output, computed where they are used
+// from the kernel arguments (a copy of every layer's pointers held through
+// the item would take scalar registers the main loop needs).
+__device__ __forceinline__ const uint16_t* layer_input(const ChainArgs& a, uint32_t l) {
+    return l == 0 ? a.x : a.ys + (size_t)(l - 1) * a.M * a.ldy;
+}
+__device__ __forceinline__ uint16_t* layer_t(const ChainArgs& a, uint32_t l) {
+    return l == 0 ? a.t : a.t + (size_t)l * a.M * a.ldt;
+}
+__device__ __forceinline__ uint16_t* layer_output(const ChainArgs& a, uint32_t l) {
+    return l + 1 < a.layers ? a.ys + (size_t)l * a.M * a.ldy : a.y;
+}
+
 template <class C>
-__device__ __forceinline__ TileJob producer_job(const ChainArgs& a, uint32_t mb, uint32_t nb, uint32_t s) {
+__device__ __forceinline__ TileJob producer_job(const ChainArgs& a, uint32_t mb, uint32_t nb, uint32_t s,
+                                                uint32_t l) {
     const bool inter = a.act == ACT_SWIGLU;
     int ks0, ks1;
     part_range((a.H + BK - 1) / BK, s, a.ksp1, ks0, ks1);
-    return TileJob{a.x, a.w1, a.zero, a.H, a.M, (int)mb * C::BM,
-                   (inter ? 2 : 1) * a.I, a.I, (int)nb * producer_width<C>(a), inter ? a.I : 0,
+    return TileJob{layer_input(a, l), l == 0 ? a.w1 : a.w1s[l], a.zero, l == 0 ? a.ldx : a.ldy, a.M,
+                   (int)mb * C::BM, (inter ? 2 : 1) * a.I, a.I, (int)nb * producer_width<C>(a), inter ? a.I : 0,
                    a.H, ks0, ks1, inter};
 }
 
 template <class C>
-__device__ __forceinline__ TileJob consumer_job(const ChainArgs& a, uint32_t mb, uint32_t nb, uint32_t s) {
+__device__ __forceinline__ TileJob consumer_job(const ChainArgs& a, uint32_t mb, uint32_t nb, uint32_t s,
+                                                uint32_t l) {
     int ks0, ks1;
     part_range((a.I + BK - 1) / BK, s, a.ksp2, ks0, ks1);
-    return TileJob{a.t, a.w2, a.zero, a.ldt, a.M, (int)mb * C::BM, a.H, a.H, (int)nb * C::BN, 0,
-                   a.I, ks0, ks1, false};
+    return TileJob{layer_t(a, l), l == 0 ? a.w2 : a.w2s[l], a.zero, a.ldt, a.M, (int)mb * C::BM, a.H, a.H,
+                   (int)nb * C::BN, 0, a.I, ks0, ks1, false};
 }
 
 // Split-K for tiles of more than 16 fragments per thread, whose
@@ -1256,10 +1316,12 @@ __device__ __forceinline__ bool split_reduce(f32x4 (&acc)[C::FM][C::FN], float* 
 // unless the tile is split and another part arrives last).
 template <class C, int DT, int ROLE, class Wait>
 __device__ __forceinline__ bool run_tile(const ChainArgs& a, uint32_t mb, uint32_t nb, uint32_t s, uint32_t* s_flag,
-                                         Wait& wait) {
+                                         Wait& wait, uint32_t l = 0) {
     f32x4 acc[C::FM][C::FN];
-    const uint32_t tile = mb * (ROLE == 1 ? a.N1t : a.N2t) + nb;
-    const TileJob j = ROLE == 1 ? producer_job<C>(a, mb, nb, s) : consumer_job<C>(a, mb, nb, s);
+    // layer l's split-K counters, ready words and partials follow layer
+    // l-1's: its tiles are numbered from l * T1 (GEMM1) or l * T2 (GEMM2)
+    const uint32_t tile = (ROLE == 1 ? l * a.T1 + mb * a.N1t : l * a.T2 + mb * a.N2t) + nb;
+    const TileJob j = ROLE == 1 ? producer_job<C>(a, mb, nb, s, l) : consumer_job<C>(a, mb, nb, s, l);
     tile_mainloop<C, DT>(j, acc, wait);
     const uint32_t S = ROLE == 1 ? a.S1 : a.S2;
     if (S > 1) {
@@ -1268,9 +1330,10 @@ __device__ __forceinline__ bool run_tile(const ChainArgs& a, uint32_t mb, uint32
         if (!last) return false;
     }
     if constexpr (ROLE == 1)
-        tile_epilogue<C, DT>(acc, a.act, j.inter, a.t, a.ldt, a.M, a.I, j.m0, j.n0);
+        tile_epilogue<C, DT>(acc, a.act, j.inter, layer_t(a, l), a.ldt, a.M, a.I, j.m0, j.n0);
     else
-        tile_epilogue<C, DT>(acc, ACT_NONE, false, a.y, a.H, a.M, a.H, j.m0, j.n0);
+        tile_epilogue<C, DT>(acc, ACT_NONE, false, layer_output(a, l), l + 1 < a.layers ? a.ldy : a.ldo, a.M, a.H,
+                             j.m0, j.n0);
     return true;
 }
 

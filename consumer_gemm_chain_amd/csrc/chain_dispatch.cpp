@@ -6,7 +6,7 @@
 
 #define MLPC_DECL(id, ...)                                                                         \
     hipError_t mlpc_launch_cfg##id(const mlpc::ChainArgs&, int, int, int, hipStream_t);            \
-    hipError_t mlpc_occupancy_cfg##id(int, int, int*);                                              \
+    hipError_t mlpc_occupancy_cfg##id(int, int, int, int*);                                         \
     CfgInfo mlpc_info_cfg##id();
 MLPC_CONFIGS(MLPC_DECL)
 #undef MLPC_DECL
@@ -27,9 +27,9 @@ hipError_t mlpc_launch(const mlpc::ChainArgs& a, int cfg, int dtype, int what, i
 #undef MLPC_CASE
 }
 
-hipError_t mlpc_persistent_occupancy(int cfg, int dtype, int policy, int* per_cu) {
+hipError_t mlpc_persistent_occupancy(int cfg, int dtype, int policy, int layers, int* per_cu) {
 #define MLPC_CASE(n, ...) \
-    case n: return mlpc_occupancy_cfg##n(dtype, policy, per_cu);
+    case n: return mlpc_occupancy_cfg##n(dtype, policy, layers, per_cu);
     switch (cfg) { MLPC_CONFIGS(MLPC_CASE) default: return hipErrorInvalidValue; }
 #undef MLPC_CASE
 }

@@ -162,8 +162,19 @@ __device__ __forceinline__ uint32_t queue_owners(uint32_t grid, uint32_t x) {
     return grid > x ? (grid - x + 7) / 8 : 0;
 }
 
+// Item c of queue (bp, bc) of a chain of a.layers MLP layers: queue order
+// is layer by layer (each layer's GEMM1 parts, then its GEMM2 parts), and
+// layer l's items are numbered from l * (P1 + P2).
+__device__ __forceinline__ uint32_t queue_item_layers(const ChainArgs& a, const XcdBlock& bp, const XcdBlock& bc,
+                                                      uint32_t P1, uint32_t c) {
+    const uint32_t per = bp.len + bc.len;
+    const uint32_t l = c / per;
+    return l * (P1 + a.T2 * a.S2) + queue_item(a, bp, bc, P1, c - l * per);
+}
+
 // Wave 0 only: the next item for this workgroup, or NO_ITEM.
 constexpr uint32_t NO_ITEM = 0xffffffffu;
+template <bool LAYERS = false>
 __device__ __forceinline__ uint32_t draw_item(const ChainArgs& a, Queues& q) {
     const uint32_t lane = threadIdx.x & 63;
     const uint32_t x = (q.own + lane) & 7;
@@ -172,7 +183,7 @@ __device__ __forceinline__ uint32_t draw_item(const ChainArgs& a, Queues& q) {
     if (lane < 8) {
         bp = xcd_block(a.Mt, a.N1t, a.S1, a.rx, x);
         bc = xcd_block(a.Mt, a.N2t, a.S2, a.rx, x);
-        len = bp.len + bc.len;
+        len = (LAYERS ? a.layers : 1u) * (bp.len + bc.len);
         first = min(len, queue_owners(a.grid, x));   // items handed out at launch
     }
     for (;;) {
@@ -186,7 +197,7 @@ __device__ __forceinline__ uint32_t draw_item(const ChainArgs& a, Queues& q) {
         if (lane == k) {
             const uint32_t c = __hip_atomic_fetch_add(a.ticket + 64 * x, 1u, __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT) + first;
-            if (c < len) item = queue_item(a, bp, bc, q.P1, c);
+            if (c < len) item = LAYERS ? queue_item_layers(a, bp, bc, q.P1, c) : queue_item(a, bp, bc, q.P1, c);
         }
         item = __builtin_amdgcn_readlane(item, k);
         if (item != NO_ITEM) return item;
@@ -276,6 +287,108 @@ void chain_persistent_kernel(ChainArgs a) {
     }
 }
 
+// Persistent kernel of a chain of a.layers MLP layers, 2 * layers dependent
+// GEMMs in one launch: layer l's GEMM2 tiles wait for the GEMM1 tiles of T_l
+// they read (as in the one-layer kernel), and layer l+1's GEMM1 tiles wait,
+// K chunk by K chunk, for the GEMM2 tiles of Y_l they read -- so the
+// consumers of one layer overlap the tail of the previous one, which a
+// sequence of kernels (or a captured graph of them) cannot do (the Hacker
+// News thread on megakernels vs CUDA graphs: one task starts as soon as the
+// slice it needs is done, across layers).  Every GEMM output but the last
+// publishes per-tile flags (tile_sync) or per-row-block counts (row_sync):
+// T_l's at flags + l T1 / rowcnt + l Mt, Y_l's at flags + layers T1 + l T2 /
+// rowcnt + (layers + l) Mt.  The queues hand out each XCD's items layer by
+// layer, producers before consumers within a layer, so every item an item
+// waits for was handed out before it; with every queue owned by a resident
+// workgroup that drains its own queue first, every wait ends (the item of
+// lowest layer and stage among the waiting ones waits on an item that is
+// running and does not wait, or on one its queue's owners will draw).
+template <class C, int DT, int POL>
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
+void chain_layers_kernel(ChainArgs a) {
+    __shared__ uint32_t s_ticket;
+    __shared__ uint32_t s_ready;
+    __shared__ uint32_t s_flag;
+    const uint32_t P1 = a.T1 * a.S1;
+    const uint32_t P = P1 + a.T2 * a.S2;      // items per layer
+    const int bn1 = a.act == ACT_SWIGLU ? C::BN / 2 : C::BN;
+    Queues q{blockIdx.x & 7u, 0u, P1};
+    uint32_t item = NO_ITEM;
+    if (blockIdx.x == 0 && threadIdx.x < 8)
+        __hip_atomic_store(a.ticket_next + 64 * threadIdx.x, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    {
+        const XcdBlock bp = xcd_block(a.Mt, a.N1t, a.S1, a.rx, q.own);
+        const XcdBlock bc = xcd_block(a.Mt, a.N2t, a.S2, a.rx, q.own);
+        const uint32_t pos = blockIdx.x >> 3;
+        if (pos < a.layers * (bp.len + bc.len)) item = queue_item_layers(a, bp, bc, P1, pos);
+    }
+    for (;;) {
+        if (item == NO_ITEM) {
+            if ((threadIdx.x >> 6) == 0) {
+                const uint32_t it = draw_item<true>(a, q);
+                if (threadIdx.x == 0) s_ticket = it;
+            }
+            __syncthreads();
+            item = __builtin_amdgcn_readfirstlane(s_ticket);
+            __syncthreads();
+            if (item == NO_ITEM) break;
+        }
+        const uint32_t t = item;
+        item = NO_ITEM;
+        const uint32_t l = t / P, u = t - l * P;
+        const bool prod = u < P1;
+        if (t != a.skip_producer) {
+            const uint32_t S = prod ? a.S1 : a.S2;
+            const uint32_t v = prod ? u : u - P1;
+            const uint32_t tile = v / S, part = v % S;
+            const uint32_t nt = prod ? a.N1t : a.N2t;
+            const uint32_t mb = tile / nt, nb = tile % nt;
+            const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+            uint64_t t_waited = t_start;
+            bool wrote;
+            if (prod) {
+                // GEMM1 of layer l > 0 reads Y_{l-1}: its K chunks are Y's
+                // column blocks of BN (whole 128-byte lines per tile); layer
+                // 0's GEMM1 reads x and waits for nothing (an inactive wait,
+                // so that both share one copy of the tile code)
+                const uint32_t lp = l > 0 ? l - 1 : 0;
+                const uint32_t* fy = a.flags + a.layers * a.T1 + lp * a.T2;
+                const uint32_t* cy = a.rowcnt + (a.layers + lp) * a.Mt;
+                ChainWait<POL> w{l > 0, fy + mb * a.N2t, cy + mb, a.N2t,
+                                 POL == POL_ROW ? a.epoch * a.N2t : a.epoch, C::BN, a.status, a.spin_limit,
+                                 0u, &s_ready, (part * a.ksp1 * BK) / (uint32_t)C::BN, false, t_start};
+                wrote = run_tile<C, DT, 1>(a, mb, nb, part, &s_flag, w, l);
+                t_waited = w.t_waited;
+            } else {
+                ChainWait<POL> w{true, a.flags + l * a.T1 + mb * a.N1t, a.rowcnt + l * a.Mt + mb, a.N1t,
+                                 POL == POL_ROW ? a.epoch * a.N1t : a.epoch, bn1, a.status, a.spin_limit,
+                                 a.acq_agent, &s_ready, (part * a.ksp2 * BK) / (uint32_t)bn1, false, t_start};
+                wrote = run_tile<C, DT, 2>(a, mb, nb, part, &s_flag, w, l);
+                t_waited = w.t_waited;
+            }
+            if (a.trace && threadIdx.x == 0) trace_item(a, t, t_start, t_waited, wrote);
+            if (wrote && (prod || l + 1 < a.layers)) {
+                // publish the tile of T_l (GEMM1) or Y_l (GEMM2 of a layer that is not the last)
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+                __syncthreads();
+                if (threadIdx.x == 0) {
+                    if constexpr (POL == POL_TILE) {
+                        uint32_t* f = prod ? a.flags + l * a.T1 + mb * a.N1t + nb
+                                           : a.flags + a.layers * a.T1 + l * a.T2 + mb * a.N2t + nb;
+                        __hip_atomic_store(f, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                    } else {
+                        uint32_t* c = prod ? a.rowcnt + l * a.Mt + mb : a.rowcnt + (a.layers + l) * a.Mt + mb;
+                        __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                }
+            }
+        }
+        // (as in the one-layer kernel: keeps the thread-0 release apart from
+        // the thread-0 ticket draw at the top of the loop)
+        __syncthreads();
+    }
+}
+
 // ------------------------------------------------------------------ host side
 
 template <class C, int DT>
@@ -292,6 +405,14 @@ static hipError_t launch_t(const ChainArgs& a, int what, int grid, hipStream_t s
     case LAUNCH_TILE: {
         auto k = (what == LAUNCH_ROW) ? chain_persistent_kernel<C, DT, POL_ROW>
                                       : chain_persistent_kernel<C, DT, POL_TILE>;
+        if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, k, C::NT, 0);
+        hipLaunchKernelGGL(k, dim3(grid), dim3(C::NT), 0, s, a);
+        return hipGetLastError();
+    }
+    case LAUNCH_LAYERS_ROW:
+    case LAUNCH_LAYERS_TILE: {
+        auto k = (what == LAUNCH_LAYERS_ROW) ? chain_layers_kernel<C, DT, POL_ROW>
+                                             : chain_layers_kernel<C, DT, POL_TILE>;
         if (occ) return hipOccupancyMaxActiveBlocksPerMultiprocessor(occ, k, C::NT, 0);
         hipLaunchKernelGGL(k, dim3(grid), dim3(C::NT), 0, s, a);
         return hipGetLastError();
@@ -324,9 +445,11 @@ hipError_t MLPC_CAT(mlpc_launch_cfg, MLPC_CFG)(const ChainArgs& a, int dtype, in
     return launch_c<Cfg>(a, dtype, what, grid, s, nullptr);
 }
 
-hipError_t MLPC_CAT(mlpc_occupancy_cfg, MLPC_CFG)(int dtype, int policy, int* per_cu) {
+hipError_t MLPC_CAT(mlpc_occupancy_cfg, MLPC_CFG)(int dtype, int policy, int layers, int* per_cu) {
     ChainArgs dummy{};
-    return launch_c<Cfg>(dummy, dtype, policy == POL_ROW ? LAUNCH_ROW : LAUNCH_TILE, 0, nullptr, per_cu);
+    const int what = layers > 1 ? (policy == POL_ROW ? LAUNCH_LAYERS_ROW : LAUNCH_LAYERS_TILE)
+                                : (policy == POL_ROW ? LAUNCH_ROW : LAUNCH_TILE);
+    return launch_c<Cfg>(dummy, dtype, what, 0, nullptr, per_cu);
 }
 
 CfgInfo MLPC_CAT(mlpc_info_cfg, MLPC_CFG)() {

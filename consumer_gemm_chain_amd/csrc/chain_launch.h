@@ -6,7 +6,8 @@
 
 #include "chain_device.hpp"
 
-enum { LAUNCH_GEMM1 = 1, LAUNCH_GEMM2 = 2, LAUNCH_ROW = 3, LAUNCH_TILE = 4 };
+enum { LAUNCH_GEMM1 = 1, LAUNCH_GEMM2 = 2, LAUNCH_ROW = 3, LAUNCH_TILE = 4, LAUNCH_LAYERS_ROW = 5,
+       LAUNCH_LAYERS_TILE = 6 };
 
 struct CfgInfo {
     int id;
@@ -21,8 +22,9 @@ CfgInfo mlpc_config_info(int id);
 // LAUNCH_GEMM2 (grid a.T2) or a persistent kernel (grid `grid`).
 hipError_t mlpc_launch(const mlpc::ChainArgs& a, int cfg, int dtype, int what, int grid, hipStream_t s);
 
-// Resident workgroups per CU of the persistent kernel for a configuration.
-hipError_t mlpc_persistent_occupancy(int cfg, int dtype, int policy, int* per_cu);
+// Resident workgroups per CU of the persistent kernel for a configuration
+// (the multi-layer kernel when layers > 1).
+hipError_t mlpc_persistent_occupancy(int cfg, int dtype, int policy, int layers, int* per_cu);
 
 // The static device scratch of the entry point that allocates nothing
 // (chain_scratch.hip): 128 MiB per device.

@@ -29,10 +29,10 @@ EXPORTS = ("mlp_chain_create", "mlp_chain_run", "mlp_chain_destroy", "mlp_chain_
            "mlp_chain_debug_set_spin_limit", "mlp_chain_debug_skip_producer",
            "mlp_chain_debug_set_config", "mlp_chain_debug_set_split", "mlp_chain_debug_set_grid",
            "mlp_chain_debug_set_order", "mlp_chain_debug_set_trace", "mlp_chain_debug_read_intermediate",
-           "mlp_chain_run_noalloc")
+           "mlp_chain_run_noalloc", "mlp_chain_create_layers", "mlp_chain_run_layers")
 
 INFO_FIELDS = ("BM", "BN1", "BN2", "BK", "Mt", "N1t", "N2t", "T1", "T2", "grid", "wg_per_cu",
-               "threads", "cus", "epoch", "config", "workspace_bytes", "S1", "S2", "ksp1", "ksp2")
+               "threads", "cus", "epoch", "config", "workspace_bytes", "S1", "S2", "ksp1", "ksp2", "layers")
 
 _lib = None
 
@@ -88,6 +88,10 @@ def load_library(path: str | None = None):
     lib.mlp_chain_debug_read_intermediate.restype = ci
     lib.mlp_chain_run_noalloc.argtypes = [i64, i64, i64, ci, ci, ci, vp, vp, vp, vp, vp, vp]
     lib.mlp_chain_run_noalloc.restype = ci
+    lib.mlp_chain_create_layers.argtypes = [i64, i64, i64, ci, ci, ci, ci]
+    lib.mlp_chain_create_layers.restype = vp
+    lib.mlp_chain_run_layers.argtypes = [vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp]
+    lib.mlp_chain_run_layers.restype = ci
     _lib = lib
     return lib
 
@@ -110,6 +114,22 @@ def mlp_chain_create(M: int, H: int, I: int, act: int, dtype: int, policy: int) 
     if not h:
         raise MlpChainError(MLP_EINVAL, mlp_chain_last_error())
     return h
+
+
+def mlp_chain_create_layers(M: int, H: int, I: int, act: int, dtype: int, policy: int, layers: int) -> int:
+    """A chain of `layers` MLP layers; returns the opaque handle, raises on failure."""
+    h = load_library().mlp_chain_create_layers(int(M), int(H), int(I), int(act), int(dtype), int(policy),
+                                               int(layers))
+    if not h:
+        raise MlpChainError(MLP_EINVAL, mlp_chain_last_error())
+    return h
+
+
+def mlp_chain_run_layers(h: int, x: int, w1s, w2s, out: int, hip_stream: int | None) -> int:
+    """`w1s` / `w2s`: sequences of the layers' device pointers."""
+    arr1 = (ctypes.c_void_p * len(w1s))(*w1s)
+    arr2 = (ctypes.c_void_p * len(w2s))(*w2s)
+    return _check(load_library().mlp_chain_run_layers(h, x, arr1, arr2, out, hip_stream or None))
 
 
 def mlp_chain_run(h: int, x: int, w1: int, w2: int, out: int, hip_stream: int | None) -> int:
@@ -200,10 +220,13 @@ class MlpChain:
     torch's current stream (or `stream`)."""
 
     def __init__(self, M: int, H: int, I: int, act: str = "gelu_tanh", dtype: str = "f16",
-                 policy: str = "tile_sync"):
+                 policy: str = "tile_sync", layers: int = 1):
         self.M, self.H, self.I = int(M), int(H), int(I)
-        self.act, self.dtype, self.policy = act, dtype, policy
-        self.h = mlp_chain_create(M, H, I, ACTS[act], DTYPES[dtype], POLICIES[policy])
+        self.act, self.dtype, self.policy, self.layers = act, dtype, policy, int(layers)
+        if self.layers == 1:
+            self.h = mlp_chain_create(M, H, I, ACTS[act], DTYPES[dtype], POLICIES[policy])
+        else:
+            self.h = mlp_chain_create_layers(M, H, I, ACTS[act], DTYPES[dtype], POLICIES[policy], self.layers)
 
     def close(self):
         if self.h:
@@ -247,6 +270,17 @@ class MlpChain:
                       self._stream(stream))
         return out
 
+    def run_layers(self, x, w1s, w2s, out, stream=None):
+        """One pass of a multi-layer chain: `w1s` / `w2s` are sequences of the
+        layers' weight tensors."""
+        if len(w1s) != self.layers or len(w2s) != self.layers:
+            raise ValueError(f"expected {self.layers} weights per GEMM, got {len(w1s)} and {len(w2s)}")
+        for w1, w2 in zip(w1s, w2s):
+            self._shapes(x, w1, w2, out)
+        mlp_chain_run_layers(self.h, x.data_ptr(), [w.data_ptr() for w in w1s], [w.data_ptr() for w in w2s],
+                             out.data_ptr(), self._stream(stream))
+        return out
+
     def run_phase(self, phase, x=None, w1=None, w2=None, out=None, stream=None):
         self._shapes(x, w1, w2, out)
         p = lambda t: t.data_ptr() if t is not None else None  # noqa: E731
@@ -285,7 +319,7 @@ class MlpChain:
             self._trace = None
             return None
         info = self.info()
-        n = info["T1"] * info["S1"] + info["T2"] * info["S2"]
+        n = (info["T1"] * info["S1"] + info["T2"] * info["S2"]) * info["layers"]
         self._trace = torch.zeros((n, 4), dtype=torch.int64, device="cuda")
         mlp_chain_debug_set_trace(self.h, self._trace.data_ptr())
         return self._trace

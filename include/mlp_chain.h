@@ -99,6 +99,34 @@ mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype
 int mlp_chain_run(mlp_chain_t h, const void* x, const void* w1, const void* w2, void* out,
                   void* hip_stream);
 
+/* A chain of `layers` MLP layers (1..8), 2 x layers dependent GEMMs:
+ * layer l computes Y_l = act(Y_{l-1} W1_l) W2_l, with Y_{-1} = x and the last
+ * layer's Y written to out; every layer has the sizes of mlp_chain_create
+ * (H wide in and out, I inner), the same activation and dtype, and its own
+ * weights.  With the fused policies all 2 x layers GEMMs run in ONE
+ * persistent kernel: a layer's GEMM2 tiles wait for the GEMM1 tiles of its
+ * intermediate they read, and the next layer's GEMM1 tiles wait, K chunk by
+ * K chunk, for the GEMM2 tiles of Y_l they read, so one layer's consumers
+ * overlap the previous layer's tail -- the cross-layer overlap of the
+ * megakernel discussion (Hacker News thread on megakernels vs CUDA graphs:
+ * CUDA graphs do not overlap work across layers; fine-grained tasks spread
+ * over the SMs).  stream_ordered launches the 2 x layers kernels in order on
+ * the stream.  Every policy computes every layer with the plan
+ * mlp_chain_create makes for these sizes, so outputs are bit-identical to
+ * `layers` one-layer runs in sequence.  The workspace keeps every layer's
+ * intermediate and every layer output but the last (rows padded to 64
+ * elements).  Returns NULL on error as mlp_chain_create. */
+mlp_chain_t mlp_chain_create_layers(int64_t M, int64_t H, int64_t I, int act, int dtype, int policy, int layers);
+
+/* Enqueue one pass of a multi-layer chain: `w1` and `w2` are HOST arrays of
+ * `layers` device pointers (layer l's [H, g I] and [I, H] weights, layouts
+ * as for mlp_chain_run); x and out as for mlp_chain_run.  A one-layer handle
+ * runs as mlp_chain_run(w1[0], w2[0]); mlp_chain_run refuses a handle of
+ * more than one layer.  Errors, asynchrony and the watchdog as
+ * mlp_chain_run. */
+int mlp_chain_run_layers(mlp_chain_t h, const void* x, const void* const* w1, const void* const* w2, void* out,
+                         void* hip_stream);
+
 /* Release the handle and its workspace.  Waits first for the stream of the
  * handle's last run (that stream must still exist; other streams are not
  * waited for).  NULL-safe; returns MLP_OK, or MLP_EHIP if the wait or the
@@ -159,11 +187,11 @@ int mlp_chain_status(mlp_chain_t h);
 const char* mlp_chain_last_error(void);
 
 /* Plan and launch facts of a handle, for tests and measurement; fills the
- * first min(n, 20) of
+ * first min(n, 21) of
  *   { BM, BN1, BN2, BK, Mt, N1t, N2t, T1, T2, persistent grid,
  *     workgroups per CU, threads per workgroup, CUs, epoch,
  *     config id, workspace bytes, S1, S2, K slabs per GEMM1 part,
- *     K slabs per GEMM2 part }.
+ *     K slabs per GEMM2 part, layers }.
  * (S1, S2: the deterministic K split of GEMM1 / GEMM2 tiles, 1 = none.)
  * Returns MLP_EINVAL for a NULL handle or array, or n < 16. */
 int mlp_chain_info(mlp_chain_t h, int64_t* info, int n);
@@ -238,9 +266,9 @@ int mlp_chain_debug_set_order(mlp_chain_t h, int order);
 
 /* Timeline trace of every policy (measurement of the non-overlapped share,
  * as the FLUX summary card advises in Interesting ideas, I3):
- * `buffer` is a DEVICE buffer of 4 * (T1*S1 + T2*S2) uint64 (see
+ * `buffer` is a DEVICE buffer of 4 * layers * (T1*S1 + T2*S2) uint64 (see
  * mlp_chain_info), NULL turns tracing off.  Each run then writes, per ticket
- * t (producer parts first), words 4t..4t+3 = { start, end of the part's
+ * t (layer by layer, producer parts first), words 4t..4t+3 = { start, end of the part's
  * last wait (= start where nothing waits), end } on the 100 MHz realtime
  * clock, and { t | XCD << 32 |
  * HW_ID << 36 | (part wrote the tile's output) << 63 }.  The buffer stays

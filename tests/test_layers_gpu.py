@@ -1,0 +1,192 @@
+"""Chains of several MLP layers in one persistent kernel (2 x layers
+dependent GEMMs), through the C ABI: every policy bit-identical to the
+stream-ordered kernels and to one-layer runs in sequence, within tolerance of
+the oracle's composition, exact on integer inputs, and free of stale reads
+across runs."""
+import numpy as np
+import pytest
+
+from consumer_gemm_chain_amd import gen
+from consumer_gemm_chain_amd import mlp_chain as mc
+from tests._helpers import POLICIES, check_against_oracle, empty_dev, from_dev, run_chain, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer_weights(L, H, I, act, dtype, seed):
+    g = 2 if act == "swiglu" else 1
+    w1s = [gen.normal_bits((H, g * I), seed + 10 * l, 1.0 / np.sqrt(H), dtype) for l in range(L)]
+    w2s = [gen.normal_bits((I, H), seed + 10 * l + 1, 1.0 / np.sqrt(I), dtype) for l in range(L)]
+    return w1s, w2s
+
+
+def _run_layers(x, w1s, w2s, act, dtype, policy, cfg=None, split=None, decoy=True, reps=1):
+    import torch
+    M, H = x.shape
+    I = w2s[0].shape[0]
+    L = len(w1s)
+    dx = to_dev(x, dtype)
+    dw1 = [to_dev(w, dtype) for w in w1s]
+    dw2 = [to_dev(w, dtype) for w in w2s]
+    with mc.MlpChain(M, H, I, act, dtype, policy, layers=L) as ch:
+        if cfg is not None:
+            ch.set_config(cfg)
+        if split is not None:
+            ch.set_split(*split)
+        assert ch.info()["layers"] == L
+        out = empty_dev((M, H), dtype)
+        if decoy:
+            # a first run on X with its rows reversed: a stale read of any
+            # layer's intermediate or output would see the decoy's values
+            ch.run_layers(torch.flip(dx, dims=[0]).contiguous(), dw1, dw2, out)
+        for _ in range(reps):
+            out.fill_(float("nan"))
+            ch.run_layers(dx, dw1, dw2, out)
+        torch.cuda.synchronize()
+        assert ch.status() == mc.MLP_OK
+        return from_dev(out)
+
+
+@pytest.mark.parametrize("L", [2, 3])
+@pytest.mark.parametrize("act,dtype,cfg", [("gelu_tanh", "f16", 0), ("swiglu", "bf16", 3), ("none", "bf16", 2),
+                                           ("gelu_tanh", "f16", 7), ("swiglu", "f16", 4)])
+def test_layers_match_oracle_and_sequential_runs(oracle_mod, L, act, dtype, cfg):
+    M, H, I = 200, 328, 456
+    print(f"layers L={L} M={M} H={H} I={I} act={act} dtype={dtype} cfg={cfg}", flush=True)
+    x = gen.normal_bits((M, H), 7 + L, 1.0, dtype)
+    w1s, w2s = _layer_weights(L, H, I, act, dtype, seed=100 * L + cfg)
+    y_ref = oracle_mod.mlp_layers(x, w1s, w2s, act, dtype)
+    # one-layer runs in sequence (the planned configuration)
+    y_seq = x
+    for w1, w2 in zip(w1s, w2s):
+        y_seq = run_chain(y_seq, w1, w2, act, dtype, "stream_ordered")
+    check_against_oracle(y_seq, y_ref, dtype, f"{L} sequential one-layer runs")
+    outs = {pol: _run_layers(x, w1s, w2s, act, dtype, pol, cfg=cfg) for pol in POLICIES}
+    for pol, y in outs.items():
+        assert np.array_equal(y, outs["stream_ordered"]), pol
+    # the configuration changes no output element; the split is the planner's
+    assert np.array_equal(outs["stream_ordered"], y_seq)
+
+
+@pytest.mark.parametrize("split", [(3, 2), (1, 4)])
+def test_layers_with_split_k(oracle_mod, split):
+    """K split in the layers' GEMMs: each layer has its own counters, ready
+    words and partials; alternating two inputs over several runs."""
+    import torch
+    M, H, I, L, act, dtype = 40, 1000, 1088, 2, "gelu_tanh", "f16"
+    xa = gen.normal_bits((M, H), 41, 1.0, dtype)
+    xb = gen.normal_bits((M, H), 42, 1.0, dtype)
+    w1s, w2s = _layer_weights(L, H, I, act, dtype, seed=43)
+    refs = [_run_layers(x, w1s, w2s, act, dtype, "stream_ordered", cfg=0, split=split, decoy=False)
+            for x in (xa, xb)]
+    for x, r in zip((xa, xb), refs):
+        check_against_oracle(r, oracle_mod.mlp_layers(x, w1s, w2s, act, dtype), dtype, f"split {split}")
+    dxs = [to_dev(x, dtype) for x in (xa, xb)]
+    dw1 = [to_dev(w, dtype) for w in w1s]
+    dw2 = [to_dev(w, dtype) for w in w2s]
+    for pol in ("row_sync", "tile_sync"):
+        with mc.MlpChain(M, H, I, act, dtype, pol, layers=L) as ch:
+            ch.set_config(0)
+            ch.set_split(*split)
+            out = empty_dev((M, H), dtype)
+            for i in range(12):
+                out.fill_(float("nan"))
+                ch.run_layers(dxs[i % 2], dw1, dw2, out)
+                torch.cuda.synchronize()
+                assert np.array_equal(from_dev(out), refs[i % 2]), (pol, i)
+            assert ch.status() == mc.MLP_OK
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_layers_exact_integer_pin(oracle_mod, dtype):
+    """Integer inputs (act none) whose partial sums are exact in fp32 in any
+    order: every policy equals exact int64 products with the library's
+    rounding after every GEMM, layer by layer."""
+    M, H, I, L = 96, 512, 384, 2
+    r = np.random.Generator(np.random.PCG64(77 + (dtype == "bf16")))
+
+    def ints(shape, lo, hi, dens):
+        v = r.integers(lo, hi + 1, size=shape).astype(np.float32)
+        v[r.random(shape) >= dens] = 0
+        return v
+    xv = ints((M, H), -2, 2, 0.5)
+    w1v = [ints((H, I), -2, 2, 0.4) for _ in range(L)]
+    w2v = [ints((I, H), -1, 1, 0.05) for _ in range(L)]
+    yi = xv.astype(np.int64)
+    for a, b in zip(w1v, w2v):
+        h = yi @ a.astype(np.int64)
+        assert (np.abs(yi) @ np.abs(a.astype(np.int64))).max() < 2 ** 24
+        t = gen.from_bits(gen.to_bits(h.astype(np.float32), dtype), dtype).astype(np.int64)
+        yv = t @ b.astype(np.int64)
+        assert (np.abs(t) @ np.abs(b.astype(np.int64))).max() < 2 ** 24
+        yi = gen.from_bits(gen.to_bits(yv.astype(np.float32), dtype), dtype).astype(np.int64)
+    y_bits = gen.to_bits(yi.astype(np.float32), dtype)
+    x = gen.to_bits(xv, dtype)
+    w1s = [gen.to_bits(v, dtype) for v in w1v]
+    w2s = [gen.to_bits(v, dtype) for v in w2v]
+    assert np.array_equal(oracle_mod.mlp_layers(x, w1s, w2s, "none", dtype), y_bits)
+    for pol in POLICIES:
+        assert np.array_equal(_run_layers(x, w1s, w2s, "none", dtype, pol), y_bits), pol
+
+
+@pytest.mark.parametrize("M", [16, 2048])
+def test_layers_full_size_gpt3_shard(oracle_mod, M):
+    """Two GPT-3 175B MLP shard layers (H=12288, I=6144, fp16, GeLU) in the
+    planner's launch configuration: the policies agree bit for bit on the
+    whole output and sampled rows agree with the oracle's composition."""
+    w = gen.WORKLOADS[1]
+    L = 2
+    x = gen.x_rows(w, M)
+    w1s, w2s = _layer_weights(L, w.H, w.I, w.act, w.dtype, seed=1500)
+    outs = {pol: _run_layers(x, w1s, w2s, w.act, w.dtype, pol) for pol in POLICIES}
+    assert np.array_equal(outs["row_sync"], outs["stream_ordered"])
+    assert np.array_equal(outs["tile_sync"], outs["stream_ordered"])
+    rows = sorted({0, M // 2, M - 1})
+    y_ref = oracle_mod.mlp_layers(x[rows], w1s, w2s, w.act, w.dtype)
+    check_against_oracle(outs["tile_sync"][rows], y_ref, w.dtype, f"2 GPT-3 layers M={M}")
+
+
+@pytest.mark.parametrize("policy", ["row_sync", "tile_sync"])
+def test_layers_watchdog_reports_timeout_and_recovers(policy):
+    """A producer of layer 0 told from the host to skip its work: its
+    consumers time out, the handle reports MLP_ETIMEOUT and the next run is
+    correct again."""
+    import torch
+    M, H, I, L, act, dtype = 96, 256, 384, 2, "gelu_tanh", "f16"
+    x = gen.normal_bits((M, H), 5, 1.0, dtype)
+    w1s, w2s = _layer_weights(L, H, I, act, dtype, seed=55)
+    ref = _run_layers(x, w1s, w2s, act, dtype, "stream_ordered", decoy=False)
+    dx = to_dev(x, dtype)
+    dw1 = [to_dev(w, dtype) for w in w1s]
+    dw2 = [to_dev(w, dtype) for w in w2s]
+    with mc.MlpChain(M, H, I, act, dtype, policy, layers=L) as ch:
+        out = empty_dev((M, H), dtype)
+        ch.set_spin_limit(2000)
+        ch.skip_producer(0)
+        ch.run_layers(dx, dw1, dw2, out)
+        torch.cuda.synchronize()
+        assert ch.status() == mc.MLP_ETIMEOUT
+        ch.skip_producer(-1)
+        ch.set_spin_limit(0)
+        ch.run_layers(dx, dw1, dw2, out)
+        torch.cuda.synchronize()
+        assert ch.status() == mc.MLP_OK
+        assert np.array_equal(from_dev(out), ref)
+
+
+def test_layers_entry_points_check_arguments():
+    import ctypes
+    import torch
+    lib = mc.load_library()
+    assert not lib.mlp_chain_create_layers(64, 256, 256, 1, 0, 2, 0)
+    assert "layers" in mc.mlp_chain_last_error()
+    assert not lib.mlp_chain_create_layers(64, 256, 256, 1, 0, 2, 9)
+    with mc.MlpChain(64, 256, 256, "gelu_tanh", "f16", "tile_sync", layers=2) as ch:
+        t = torch.zeros((256, 256), dtype=torch.float16, device="cuda")
+        p = t.data_ptr()
+        s = torch.cuda.current_stream().cuda_stream
+        assert lib.mlp_chain_run(ch.h, p, p, p, p, s) == mc.MLP_EINVAL      # a 2-layer handle needs run_layers
+        assert "run_layers" in mc.mlp_chain_last_error()
+        arr = (ctypes.c_void_p * 2)(p, None)
+        assert lib.mlp_chain_run_layers(ch.h, p, arr, arr, p, s) == mc.MLP_EINVAL
+        assert ch.info()["epoch"] == 0
