@@ -19,10 +19,13 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmlp_chain.so")
+# the same library with pseudo-random pauses before every publication
+# (-DMLPC_CHAOS=1), loaded only by the tests
+CHAOS_LIB = os.path.join(LIBDIR, "libmlp_chain_chaos.so")
 BUILD = os.path.join(ROOT, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["chain_api.cpp", "chain_dispatch.cpp", "chain_scratch.hip"]
+SOURCES = ["chain_api.cpp", "chain_dispatch.cpp", "chain_scratch.hip", "chain_litmus.hip"]
 KERNELS = "chain_kernels.hip"     # compiled once per tile configuration
 
 
@@ -48,10 +51,10 @@ def hipcc() -> str:
 
 
 def _compile(job, verbose: bool) -> str:
-    src, cfg = job
-    tag = os.path.basename(src) + ("" if cfg is None else f".cfg{cfg}")
+    src, cfg, chaos = job
+    tag = os.path.basename(src) + ("" if cfg is None else f".cfg{cfg}") + (".chaos" if chaos else "")
     obj = os.path.join(BUILD, tag + ".o")
-    defs = [] if cfg is None else [f"-DMLPC_CFG={cfg}"]
+    defs = ([] if cfg is None else [f"-DMLPC_CFG={cfg}"]) + (["-DMLPC_CHAOS=1"] if chaos else [])
     cmd = [hipcc(), "-x", "hip", *FLAGS, *defs, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -59,19 +62,28 @@ def _compile(job, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    os.makedirs(LIBDIR, exist_ok=True)
-    jobs = [(KERNELS, c) for c in range(num_configs())] + [(src, None) for src in SOURCES]
-    workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
-    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
-        objs = list(ex.map(lambda j: _compile(j, verbose), jobs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Build the library and its test variant with chaos pauses."""
+    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(LIBDIR, exist_ok=True)
+    kern = [(KERNELS, c, False) for c in range(num_configs())]
+    chaos = [(KERNELS, c, True) for c in range(num_configs())]
+    api = [(src, None, False) for src in SOURCES]
+    jobs = kern + chaos + api
+    workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = dict(zip(jobs, ex.map(lambda j: _compile(j, verbose), jobs)))
+    _link([objs[j] for j in kern + api], LIB, verbose)
+    _link([objs[j] for j in chaos + api], CHAOS_LIB, verbose)
     return LIB
 
 

@@ -858,6 +858,21 @@ int mlp_chain_debug_set_split(mlp_chain_t h, int s1, int s2) {
     return replan(h);
 }
 
+int mlp_chain_debug_litmus(void* data, size_t data_bytes, void* flags, size_t flag_bytes, void* result, int rounds,
+                           int half_lines, int agent, uint32_t spin_limit, void* hip_stream) {
+    if (!data || !flags || !result || ((uintptr_t)data & 255u) != 0 || ((uintptr_t)flags & 3u) != 0 ||
+        ((uintptr_t)result & 3u) != 0)
+        return fail(MLP_EINVAL, "litmus: data (256-byte aligned), flags and result must be device pointers");
+    if (rounds < 1 || rounds > 4096 || data_bytes < (size_t)rounds * (1u << 20) || flag_bytes < (size_t)rounds * 1024)
+        return fail(MLP_EINVAL, "litmus: %d rounds need %zu data bytes and %zu flag bytes", rounds,
+                    (size_t)rounds << 20, (size_t)rounds * 1024);
+    const hipError_t e = mlpc_litmus(data, data_bytes, flags, flag_bytes, result, rounds, half_lines, agent,
+                                     spin_limit ? spin_limit : DEFAULT_SPIN_LIMIT,
+                                     static_cast<hipStream_t>(hip_stream));
+    if (e != hipSuccess) return fail(MLP_EHIP, "litmus launch failed: %s", hipGetErrorString(e));
+    return MLP_OK;
+}
+
 int mlp_chain_debug_set_trace(mlp_chain_t h, void* buffer) {
     if (!h) return fail(MLP_EINVAL, "NULL handle");
     h->trace = static_cast<uint64_t*>(buffer);

@@ -187,6 +187,26 @@ struct TileCfg {
 
 // ------------------------------------------------------------------ helpers
 
+// Test builds only (compiled with -DMLPC_CHAOS=1, a separate library that
+// the tests load): a pseudo-random pause of up to about 16 us before a tile
+// or a split part publishes, so that consumers and reducing parts meet
+// their producers at shifted times.  Nothing in the normal build.
+#ifndef MLPC_CHAOS
+#define MLPC_CHAOS 0
+#endif
+__device__ __forceinline__ void chaos_delay(uint32_t key) {
+#if MLPC_CHAOS
+    uint32_t h = key * 0x9E3779B1u;
+    h ^= h >> 16;
+    h *= 0x85EBCA6Bu;
+    h ^= h >> 13;
+    const uint32_t n = h & 63u;
+    for (uint32_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(8);
+#else
+    (void)key;
+#endif
+}
+
 // The thread's index in the workgroup, read afresh at each use: the empty
 // volatile asm hands the compiler a new value each time, so nothing computed
 // from it can be hoisted out of the persistent kernel's item loop.  (Hoisted,
@@ -1152,6 +1172,7 @@ __device__ __forceinline__ bool split_reduce_release(f32x4 (&acc)[C::FM][C::FN],
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn)
             base[((size_t)s * NF + fm * C::FN + fn) * C::NT + tid] = acc[fm][fn];
+    chaos_delay(tile * 64u + s);
     // every thread's partial happens before thread 0's agent-scope release
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __syncthreads();
@@ -1243,6 +1264,7 @@ __device__ __forceinline__ bool split_reduce(f32x4 (&acc)[C::FM][C::FN], float* 
 #pragma unroll
             for (int fn = 0; fn < C::FN; ++fn)
                 base[((size_t)s * NF + fm * C::FN + fn) * C::NT + tid] = acc[fm][fn];
+        chaos_delay(tile * 64u + s);
         // every thread's partial happens before thread 0's agent-scope release
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         __syncthreads();

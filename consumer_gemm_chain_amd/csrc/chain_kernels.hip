@@ -265,6 +265,7 @@ void chain_persistent_kernel(ChainArgs a) {
             }
             if (a.trace && threadIdx.x == 0) trace_item(a, t, t_start, w.t_waited, wrote);
             if (prod && wrote) {
+                chaos_delay(t ^ (a.epoch << 20));
                 // every thread's T stores happen before thread 0's agent-scope
                 // release (workgroup release + barrier), which publishes the tile
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -369,6 +370,7 @@ void chain_layers_kernel(ChainArgs a) {
             if (a.trace && threadIdx.x == 0) trace_item(a, t, t_start, t_waited, wrote);
             if (wrote && (prod || l + 1 < a.layers)) {
                 // publish the tile of T_l (GEMM1) or Y_l (GEMM2 of a layer that is not the last)
+                chaos_delay(t ^ (a.epoch << 20));
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
                 __syncthreads();
                 if (threadIdx.x == 0) {

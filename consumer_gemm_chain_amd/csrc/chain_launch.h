@@ -38,3 +38,9 @@ hipError_t mlpc_scratch_address(int device, void** ptr);
 // aligned device address p, and *status if non-null (no memset node, so the
 // call may be captured into a graph).
 hipError_t mlpc_zero_words(void* p, size_t bytes, uint32_t* status, hipStream_t s);
+
+// The hand-off litmus kernel (chain_litmus.hip): `rounds` rounds of 256
+// workgroups; data >= rounds x 1 MiB, flags >= rounds x 256 words and
+// result >= 8 words, all zeroed by the caller.
+hipError_t mlpc_litmus(void* data, size_t data_bytes, void* flags, size_t flag_bytes, void* result, int rounds,
+                       int half_lines, int agent, uint32_t spin_limit, hipStream_t s);

@@ -29,7 +29,7 @@ EXPORTS = ("mlp_chain_create", "mlp_chain_run", "mlp_chain_destroy", "mlp_chain_
            "mlp_chain_debug_set_spin_limit", "mlp_chain_debug_skip_producer",
            "mlp_chain_debug_set_config", "mlp_chain_debug_set_split", "mlp_chain_debug_set_grid",
            "mlp_chain_debug_set_order", "mlp_chain_debug_set_trace", "mlp_chain_debug_read_intermediate",
-           "mlp_chain_run_noalloc", "mlp_chain_create_layers", "mlp_chain_run_layers")
+           "mlp_chain_run_noalloc", "mlp_chain_create_layers", "mlp_chain_run_layers", "mlp_chain_debug_litmus")
 
 INFO_FIELDS = ("BM", "BN1", "BN2", "BK", "Mt", "N1t", "N2t", "T1", "T2", "grid", "wg_per_cu",
                "threads", "cus", "epoch", "config", "workspace_bytes", "S1", "S2", "ksp1", "ksp2", "layers")
@@ -48,7 +48,17 @@ def load_library(path: str | None = None):
     global _lib
     if _lib is not None:
         return _lib
-    path = path or LIB_PATH
+    _lib = _bind(path or LIB_PATH)
+    return _lib
+
+
+def load_chaos_library():
+    """The test build of the library (pauses before every publication), as a
+    separate ctypes handle with the same signatures."""
+    return _bind(os.path.join(PKG, "lib", "libmlp_chain_chaos.so"))
+
+
+def _bind(path: str):
     if not os.path.exists(path):
         raise RuntimeError(f"HIP library not found at {path}; build it with "
                            "`python -m consumer_gemm_chain_amd.build` (needs hipcc)")
@@ -88,11 +98,13 @@ def load_library(path: str | None = None):
     lib.mlp_chain_debug_read_intermediate.restype = ci
     lib.mlp_chain_run_noalloc.argtypes = [i64, i64, i64, ci, ci, ci, vp, vp, vp, vp, vp, vp]
     lib.mlp_chain_run_noalloc.restype = ci
+    sz = ctypes.c_size_t
+    lib.mlp_chain_debug_litmus.argtypes = [vp, sz, vp, sz, vp, ci, ci, ci, u32, vp]
+    lib.mlp_chain_debug_litmus.restype = ci
     lib.mlp_chain_create_layers.argtypes = [i64, i64, i64, ci, ci, ci, ci]
     lib.mlp_chain_create_layers.restype = vp
     lib.mlp_chain_run_layers.argtypes = [vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp]
     lib.mlp_chain_run_layers.restype = ci
-    _lib = lib
     return lib
 
 
@@ -198,6 +210,13 @@ def mlp_chain_debug_set_order(h: int, order: int) -> int:
 
 def mlp_chain_debug_set_trace(h: int, buffer: int | None) -> int:
     return _check(load_library().mlp_chain_debug_set_trace(h, buffer))
+
+
+def mlp_chain_debug_litmus(data: int, data_bytes: int, flags: int, flag_bytes: int, result: int, rounds: int,
+                           half_lines: bool, agent: bool, spin_limit: int, hip_stream: int | None) -> int:
+    return _check(load_library().mlp_chain_debug_litmus(data, int(data_bytes), flags, int(flag_bytes), result,
+                                                        int(rounds), int(bool(half_lines)), int(bool(agent)),
+                                                        int(spin_limit), hip_stream or None))
 
 
 def mlp_chain_debug_read_intermediate(h: int, dst: int, hip_stream: int | None) -> int:

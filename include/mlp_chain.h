@@ -276,6 +276,26 @@ int mlp_chain_debug_set_order(mlp_chain_t h, int order);
  * MLP_EINVAL for a NULL handle. */
 int mlp_chain_debug_set_trace(mlp_chain_t h, void* buffer);
 
+/* Test hook: a message-passing litmus test of the hand-off between tiles
+ * (the pages give no memory-ordering protocol; the CuSync README's opening
+ * paragraph only says dependent tiles are synchronized).  256 workgroups run
+ * `rounds` rounds in one launch; in each, every workgroup writes its share
+ * of a fresh 8 KB region and publishes it exactly as a producer tile does,
+ * then consumes a region one of whose two writers sits on its own XCD,
+ * exactly as a consumer tile does (relaxed polls, hand-off acquire of
+ * workgroup scope, or agent scope if `agent`, operand DMA into LDS), and
+ * checks every word.  With `half_lines` the two writers of a region write
+ * the two 64-byte halves of each of its 128-byte lines, from two XCDs.
+ * DEVICE buffers, zeroed by the caller: data >= rounds MiB (256-byte
+ * aligned), flags >= rounds x 1 KiB, result >= 8 uint32:
+ *   result[0] = words read wrong, result[1..5] = the first one's round + 1,
+ *   consumer workgroup, 16-byte chunk, word read, word expected,
+ *   result[6] != 0 if a wait exceeded `spin_limit` polls (0 = default).
+ * Enqueued on hip_stream.  Returns MLP_EINVAL for bad pointers or sizes
+ * (rounds 1..4096), MLP_EHIP if the launch fails. */
+int mlp_chain_debug_litmus(void* data, size_t data_bytes, void* flags, size_t flag_bytes, void* result, int rounds,
+                           int half_lines, int agent, uint32_t spin_limit, void* hip_stream);
+
 /* Copy the handle's intermediate T [M, I] (as left by the last run on the
  * handle) into the caller's device buffer `dst` (M * I elements of the
  * storage dtype, rows contiguous: the workspace's row padding is dropped),

@@ -173,3 +173,22 @@ def test_no_scratch_traffic_inside_k_loops(asm):
                 assert "scratch_" not in body, name
             for seg in _inner_mfma_loops(body):
                 assert "scratch_" not in "\n".join(seg), name
+
+
+def test_chaos_pauses_only_in_the_test_build():
+    """The chaos build (-DMLPC_CHAOS=1) pauses before publications; the
+    normal build carries no such pause."""
+    if not os.path.exists(b.hipcc()):
+        pytest.skip("hipcc not available")
+    import tempfile
+    src = os.path.join(b.CSRC, "chain_kernels.hip")
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "chaos.s")
+        subprocess.run([b.hipcc(), "-x", "hip", *b.FLAGS, "-DMLPC_CFG=0", "-DMLPC_CHAOS=1", "--cuda-device-only", "-S",
+                        src, "-o", out], check=True, stderr=subprocess.DEVNULL)
+        chaos = open(out).read()
+    assert "s_sleep 8" in chaos
+
+
+def test_normal_build_has_no_chaos_pause(asm):
+    assert "s_sleep 8" not in asm
