@@ -192,3 +192,25 @@ def test_chaos_pauses_only_in_the_test_build():
 
 def test_normal_build_has_no_chaos_pause(asm):
     assert "s_sleep 8" not in asm
+
+
+def test_packed_fp32_switch_reaches_the_device_pass(tmp_path):
+    """The build's `-target-feature -packed-fp32-ops` acts on the gfx950
+    device pass (the host pass does not know the feature and warns, which is
+    harmless): a float2 multiply that compiles to v_pk_mul_f32 without the
+    switch compiles to scalar multiplies with it."""
+    if not os.path.exists(b.hipcc()):
+        pytest.skip("hipcc not available")
+    src = tmp_path / "pk.hip"
+    src.write_text("#include <hip/hip_runtime.h>\n"
+                   "__global__ void k(float2* a) { int i = threadIdx.x;\n"
+                   "  a[i] = make_float2(a[i].x * a[i + 64].x, a[i].y * a[i + 64].y); }\n")
+    outs = {}
+    for tag, extra in (("with", ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]), ("without", [])):
+        out = tmp_path / f"{tag}.s"
+        subprocess.run([b.hipcc(), "-x", "hip", f"--offload-arch={b.ARCH}", "-O3", *extra, "--cuda-device-only",
+                        "-S", str(src), "-o", str(out)], check=True, stderr=subprocess.DEVNULL)
+        outs[tag] = out.read_text()
+    assert "v_pk_mul_f32" in outs["without"]
+    assert "v_pk_mul_f32" not in outs["with"] and "v_mul_f32" in outs["with"]
+    assert all(f in b.FLAGS for f in ("-target-feature", "-packed-fp32-ops"))
