@@ -873,6 +873,22 @@ int mlp_chain_debug_litmus(void* data, size_t data_bytes, void* flags, size_t fl
     return MLP_OK;
 }
 
+int mlp_chain_debug_set_epoch(mlp_chain_t h, uint32_t epoch) {
+    if (!h) return fail(MLP_EINVAL, "NULL handle");
+    DeviceGuard g(h->device);
+    // flags and row counters as the run of epoch `epoch` leaves them: every
+    // flag published with it, every row counter at epoch x tiles per row
+    const uint32_t L = h->layers;
+    hipError_t e = hipDeviceSynchronize();
+    if (e == hipSuccess) e = hipMemsetD32(h->flags, (int)epoch, L * h->T1 + (L - 1) * h->T2);
+    if (e == hipSuccess) e = hipMemsetD32(h->rowcnt, (int)(epoch * h->N1t), L * h->Mt);
+    if (e == hipSuccess && L > 1) e = hipMemsetD32(h->rowcnt + L * h->Mt, (int)(epoch * h->N2t), (L - 1) * h->Mt);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) return fail(MLP_EHIP, "setting the epoch failed: %s", hipGetErrorString(e));
+    h->epoch = epoch;
+    return MLP_OK;
+}
+
 int mlp_chain_debug_set_trace(mlp_chain_t h, void* buffer) {
     if (!h) return fail(MLP_EINVAL, "NULL handle");
     h->trace = static_cast<uint64_t*>(buffer);

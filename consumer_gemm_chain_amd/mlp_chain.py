@@ -29,7 +29,8 @@ EXPORTS = ("mlp_chain_create", "mlp_chain_run", "mlp_chain_destroy", "mlp_chain_
            "mlp_chain_debug_set_spin_limit", "mlp_chain_debug_skip_producer",
            "mlp_chain_debug_set_config", "mlp_chain_debug_set_split", "mlp_chain_debug_set_grid",
            "mlp_chain_debug_set_order", "mlp_chain_debug_set_trace", "mlp_chain_debug_read_intermediate",
-           "mlp_chain_run_noalloc", "mlp_chain_create_layers", "mlp_chain_run_layers", "mlp_chain_debug_litmus")
+           "mlp_chain_run_noalloc", "mlp_chain_create_layers", "mlp_chain_run_layers", "mlp_chain_debug_litmus",
+           "mlp_chain_debug_set_epoch")
 
 INFO_FIELDS = ("BM", "BN1", "BN2", "BK", "Mt", "N1t", "N2t", "T1", "T2", "grid", "wg_per_cu",
                "threads", "cus", "epoch", "config", "workspace_bytes", "S1", "S2", "ksp1", "ksp2", "layers")
@@ -101,6 +102,8 @@ def _bind(path: str):
     sz = ctypes.c_size_t
     lib.mlp_chain_debug_litmus.argtypes = [vp, sz, vp, sz, vp, ci, ci, ci, u32, vp]
     lib.mlp_chain_debug_litmus.restype = ci
+    lib.mlp_chain_debug_set_epoch.argtypes = [vp, u32]
+    lib.mlp_chain_debug_set_epoch.restype = ci
     lib.mlp_chain_create_layers.argtypes = [i64, i64, i64, ci, ci, ci, ci]
     lib.mlp_chain_create_layers.restype = vp
     lib.mlp_chain_run_layers.argtypes = [vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp]
@@ -206,6 +209,10 @@ def mlp_chain_debug_set_grid(h: int, grid: int) -> int:
 
 def mlp_chain_debug_set_order(h: int, order: int) -> int:
     return _check(load_library().mlp_chain_debug_set_order(h, int(order)))
+
+
+def mlp_chain_debug_set_epoch(h: int, epoch: int) -> int:
+    return _check(load_library().mlp_chain_debug_set_epoch(h, int(epoch) & 0xFFFFFFFF))
 
 
 def mlp_chain_debug_set_trace(h: int, buffer: int | None) -> int:
@@ -322,6 +329,9 @@ class MlpChain:
 
     def set_order(self, order: int):
         mlp_chain_debug_set_order(self.h, order)
+
+    def set_epoch(self, epoch: int):
+        mlp_chain_debug_set_epoch(self.h, epoch)
 
     def set_spin_limit(self, limit: int):
         mlp_chain_debug_set_spin_limit(self.h, limit)

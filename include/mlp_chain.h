@@ -264,6 +264,14 @@ int mlp_chain_debug_set_grid(mlp_chain_t h, int grid);
  * run.  Returns MLP_EINVAL for a NULL handle or a value outside -1..3. */
 int mlp_chain_debug_set_order(mlp_chain_t h, int order);
 
+/* Test hook: put the handle's synchronization state where the fused run of
+ * epoch `epoch` leaves it (every ready flag holding `epoch`, every row
+ * counter at epoch x tiles per row block, modulo 2^32), so that the next
+ * runs use epochs epoch+1, epoch+2, ... -- e.g. across the 32-bit wrap.
+ * Synchronizes the device.  Returns MLP_EINVAL for a NULL handle, MLP_EHIP
+ * if the device reports an error. */
+int mlp_chain_debug_set_epoch(mlp_chain_t h, uint32_t epoch);
+
 /* Timeline trace of every policy (measurement of the non-overlapped share,
  * as the FLUX summary card advises in Interesting ideas, I3):
  * `buffer` is a DEVICE buffer of 4 * layers * (T1*S1 + T2*S2) uint64 (see

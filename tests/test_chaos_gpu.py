@@ -64,7 +64,7 @@ def test_chaos_repeated_runs(chaos, M, H, I, act, dtype, cfg, split, policy):
             assert chaos.mlp_chain_debug_set_split(h, *split) == mc.MLP_OK
         out = empty_dev((M, H), dtype)
         s = torch.cuda.current_stream().cuda_stream
-        for i in range(24):
+        for i in range(64):
             out.fill_(float("nan"))
             assert chaos.mlp_chain_run(h, dxs[i % 2].data_ptr(), dw1.data_ptr(), dw2.data_ptr(), out.data_ptr(),
                                        s) == mc.MLP_OK

@@ -412,3 +412,47 @@ def test_tile_orders_agree_bitwise(oracle_mod, policy):
                 ref = y
                 check_against_oracle(y, y_ref, dtype, f"{policy} order {order} split {split}")
             assert np.array_equal(y, ref), (policy, order, split)
+
+
+@pytest.mark.parametrize("policy", ["row_sync", "tile_sync"])
+@pytest.mark.parametrize("layers", [1, 2])
+def test_epoch_wrap_and_a_thousand_runs(policy, layers):
+    """The epoch is modular 32-bit: runs across the wrap (flags and row
+    counters set where epoch 2^32 - 4 leaves them) stay bit-exact; then 1000
+    back-to-back runs alternating two inputs, every output kept and compared
+    with the stream-ordered outputs at the end."""
+    import torch
+    from consumer_gemm_chain_amd.mlp_chain import MlpChain
+    from tests._helpers import empty_dev, from_dev
+    M, H, I, act, dtype = 64, 512, 640, "gelu_tanh", "f16"
+    xs = [gen.normal_bits((M, H), 600 + i, 1.0, dtype) for i in range(2)]
+    w1s = [gen.normal_bits((H, I), 610 + l, 1.0 / np.sqrt(H), dtype) for l in range(layers)]
+    w2s = [gen.normal_bits((I, H), 620 + l, 1.0 / np.sqrt(I), dtype) for l in range(layers)]
+    refs = []
+    for x in xs:
+        y = x
+        for w1, w2 in zip(w1s, w2s):
+            y = run_chain(y, w1, w2, act, dtype, "stream_ordered")
+        refs.append(torch.from_numpy(y.view(np.int16)).cuda())
+    dxs = [to_dev(x, dtype) for x in xs]
+    dw1 = [to_dev(w, dtype) for w in w1s]
+    dw2 = [to_dev(w, dtype) for w in w2s]
+    n = 1000
+    outs = torch.empty((n, M, H), dtype=dxs[0].dtype, device="cuda")
+    with MlpChain(M, H, I, act, dtype, policy, layers=layers) as ch:
+        run = (lambda x, o: ch.run(x, dw1[0], dw2[0], o)) if layers == 1 else \
+              (lambda x, o: ch.run_layers(x, dw1, dw2, o))
+        ch.set_epoch(2 ** 32 - 4)
+        for i in range(8):                          # epochs 2^32-3 .. 4
+            out = empty_dev((M, H), dtype)
+            run(dxs[i % 2], out)
+            torch.cuda.synchronize()
+            assert np.array_equal(from_dev(out), refs[i % 2].cpu().numpy().view(np.uint16)), ("wrap", i)
+        assert ch.info()["epoch"] == 4
+        for i in range(n):
+            run(dxs[i % 2], outs[i])
+        torch.cuda.synchronize()
+        assert ch.status() == 0
+    o = outs.view(torch.int16)
+    assert torch.equal(o[0::2], refs[0].expand(n // 2, M, H))
+    assert torch.equal(o[1::2], refs[1].expand(n // 2, M, H))
