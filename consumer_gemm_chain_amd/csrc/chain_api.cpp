@@ -64,6 +64,7 @@ struct mlp_chain {
     int forced_s1, forced_s2;   // 0 = planner's split
     int forced_grid;            // 0 = planner's persistent grid
     int forced_order;           // -1 = planner's tile order
+    int forced_rx;              // 0 = planner's XCD grid rows
     uint32_t order;             // bit 0 / 1: GEMM1 / GEMM2 tiles column-major in each XCD block
     CfgInfo ci;
     uint32_t Mt, N1t, N2t, T1, T2;
@@ -169,8 +170,9 @@ uint32_t plan_split(uint32_t tiles, uint32_t nks, int cus, int64_t M, uint32_t M
 //     tiles with four stages and one workgroup per CU (three slabs of
 //     weights in flight per CU);
 //   * otherwise 256 x 128 tiles (eight waves of 64 x 64, three stages) or
-//     256 x 256 tiles (eight waves of 128 x 64, two stages: a third fewer
-//     operand bytes per MFMA) once there are enough of those: for the
+//     256 x 256 tiles (eight waves of 128 x 64, a third fewer operand bytes
+//     per MFMA; four stages of half a slab, which ran 2-6% faster than two
+//     of a whole slab on the 256 x 256 shapes) once there are enough of those: for the
 //     stream-ordered pair when GEMM2 has a wave of them, for the fused
 //     policies when GEMM1 fills 7/8 of a wave (with fewer producer tiles the
 //     consumers start early and wait);
@@ -178,7 +180,7 @@ uint32_t plan_split(uint32_t tiles, uint32_t nks, int cus, int64_t M, uint32_t M
 constexpr int CFG_SMALL = 0;    // 16 x 64, four stages
 constexpr int CFG_DEEP = 4;     // 64 x 128, four stages, one workgroup per CU
 constexpr int CFG_WIDE = 3;     // 256 x 128, eight waves, three stages
-constexpr int CFG_BIG = 7;      // 256 x 256, eight waves of 128 x 64, two stages
+constexpr int CFG_BIG = 8;      // 256 x 256, eight waves of 128 x 64, four stages of half a slab
 
 // Fused split of GEMM1.  When GEMM1's unsplit tiles make more than half a
 // wave and at most one, every producer tile runs at once, all of them finish
@@ -495,7 +497,7 @@ mlpc::ChainArgs make_args(const mlp_chain* h, const void* x, const void* w1, con
     a.N2t = h->N2t;
     a.T1 = h->T1;
     a.T2 = h->T2;
-    a.rx = h->Mt >= 2 ? 2u : 1u;
+    a.rx = h->forced_rx > 0 ? (uint32_t)h->forced_rx : h->Mt >= 2 ? 2u : 1u;
     a.order = h->order;
     a.ticket = h->ticket + 512 * (h->epoch & 1u);
     a.ticket_next = h->ticket + 512 * ((h->epoch & 1u) ^ 1u);
@@ -548,6 +550,7 @@ void init_handle(mlp_chain* h, int64_t M, int64_t H, int64_t I, int act, int dty
     h->forced_s1 = 0;
     h->forced_grid = 0;
     h->forced_order = -1;
+    h->forced_rx = 0;
     h->forced_s2 = 0;
     h->spin_limit = DEFAULT_SPIN_LIMIT;
     h->skip_producer = mlpc::NO_SKIP;
@@ -845,8 +848,12 @@ int mlp_chain_debug_set_grid(mlp_chain_t h, int grid) {
 
 int mlp_chain_debug_set_order(mlp_chain_t h, int order) {
     if (!h) return fail(MLP_EINVAL, "NULL handle");
-    if (order < -1 || order > 3) return fail(MLP_EINVAL, "order must be -1 (planned) or 0..3, got %d", order);
-    h->forced_order = order;
+    const int rx = order < 0 ? 0 : order >> 4;
+    if (order < -1 || (order >= 0 && ((order & ~0xf3) != 0 || (rx != 0 && rx != 1 && rx != 2 && rx != 4 && rx != 8))))
+        return fail(MLP_EINVAL, "order must be -1 (planned) or (0..3) | rx << 4 with rx in {0, 1, 2, 4, 8}, got %d",
+                    order);
+    h->forced_order = order < 0 ? -1 : order & 3;
+    h->forced_rx = rx;
     return apply_plan(h, h->cfg);
 }
 

@@ -147,42 +147,50 @@ inline ChainArgs layer_args(const ChainArgs& a, uint32_t l, size_t tile_elems) {
 }
 
 // Tile configuration: BM x BN tile, WM x WN waves of (BM/WM) x (BN/WN), NS
-// LDS stages.  BN is the number of B (weight) columns of a tile: its output
-// width, except for SwiGLU producer tiles, whose BN columns are gate/up
-// pairs of BN/2 output columns.
-template <int BM_, int BN_, int WM_, int WN_, int NS_, int OCC_>
+// LDS stages of KS K-elements each (KS = 64: one slab per stage, read in two
+// halves; KS = 32: half a slab per stage).  BN is the number of B (weight)
+// columns of a tile: its output width, except for SwiGLU producer tiles,
+// whose BN columns are gate/up pairs of BN/2 output columns.
+template <int BM_, int BN_, int WM_, int WN_, int NS_, int OCC_, int KS_ = 64>
 struct TileCfg {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NS = NS_;
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NS = NS_, KS = KS_;
     // waves per SIMD the persistent kernel is register-limited to
     static constexpr int OCC = OCC_;
     static constexpr int NW = WM * WN;
     static constexpr int NT = 64 * NW;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int FM = WTM / 16, FN = WTN / 16;
+    static_assert(KS == 64 || KS == 32, "K per stage: a slab or half a slab");
     static_assert(WTM % 16 == 0 && WTN % 16 == 0, "wave tile must be a multiple of 16x16");
     static_assert(FN % 2 == 0, "SwiGLU tiles pair gate/up fragments within a wave");
     static_assert(NS >= 2 && NS <= 14, "2 to 14 LDS stages");
-    static constexpr int A_BYTES = BM * BK * 2;          // A slab: BM rows x 128 bytes
-    static constexpr int B_BYTES = BK * BN * 2;          // B slab: 64 k-rows x BN columns
+    static_assert(KS == 64 || NS >= 3, "a ring of half slabs needs three stages");
+    static_assert(KS == 64 || (BM * (KS / 8) / 64 / NW + KS * (BN / 8) / 64 / NW) * (NS - 1) <= 63,
+                  "vmcnt range of a ring of half slabs");
+    static constexpr int A_ROW = KS * 2;                 // bytes of one A row in a stage
+    static constexpr int A_BYTES = BM * A_ROW;           // A stage: BM rows x KS elements
+    static constexpr int B_BYTES = KS * BN * 2;          // B stage: KS k-rows x BN columns
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    // epilogue staging (padded rows) in EPI_PASSES row passes that each fit a stage
-    static constexpr int EPI_PASSES = BM * (BN + 8) * 2 <= STAGE ? 1 : BM * (BN + 8) * 2 <= 2 * STAGE ? 2 : 4;
+    static constexpr int RING = NS * STAGE;
+    // epilogue staging (padded rows) in EPI_PASSES row passes that each fit the ring
+    static constexpr int EPI_PASSES = BM * (BN + 8) * 2 <= RING ? 1 : BM * (BN + 8) * 2 <= 2 * RING ? 2 : 4;
     static constexpr int EPI_ROWS = BM / EPI_PASSES;
-    static_assert(EPI_ROWS * (BN + 8) * 2 <= STAGE, "epilogue pass must fit one stage");
+    static_assert(EPI_ROWS * (BN + 8) * 2 <= RING, "epilogue pass must fit the ring");
     static constexpr int CPR = BN / 8;                   // 16-byte chunks per B row
-    static constexpr int A_PER_WAVE = BM / 8 / NW;       // 1 KB DMA instructions per wave per slab
-    static constexpr int B_PER_WAVE = CPR / NW;
-    static_assert(A_PER_WAVE * NW * 8 == BM && B_PER_WAVE * NW == CPR, "DMA split across waves");
-    static constexpr int LPS = A_PER_WAVE + B_PER_WAVE;  // DMA instructions per wave per slab
+    static constexpr int A_PER_WAVE = BM * (KS / 8) / 64 / NW;   // 1 KB DMA instructions per wave per stage
+    static constexpr int B_PER_WAVE = KS * CPR / 64 / NW;
+    static_assert(A_PER_WAVE * NW * 64 == BM * (KS / 8) && B_PER_WAVE * NW * 64 == KS * CPR,
+                  "DMA split across waves");
+    static constexpr int LPS = A_PER_WAVE + B_PER_WAVE;  // DMA instructions per wave per stage
     static_assert(LPS * (NS - 2) <= 63, "vmcnt range");
     static constexpr int NREAD = FM + 2 * FN;            // LDS reads per fragment set
     // DMA of the next slab spread over the second half slab's MFMAs (eight
-    // waves, at least three stages); otherwise issued in one group after the
-    // first half slab's reads.  The spread form needs a branch-free step,
-    // which made the compiler copy AGPR-resident accumulators around the
-    // loop in the smaller configurations.
-    static constexpr bool SPREAD = NW == 8 && NS >= 3;
-    static constexpr int lds_bytes() { return NS * STAGE; }
+    // waves, at least three stages of a whole slab); otherwise issued in one
+    // group after the first half slab's reads.  The spread form needs a
+    // branch-free step, which made the compiler copy AGPR-resident
+    // accumulators around the loop in the smaller configurations.
+    static constexpr bool SPREAD = NW == 8 && NS >= 3 && KS == 64;
+    static constexpr int lds_bytes() { return RING; }
 };
 
 // ------------------------------------------------------------------ helpers
@@ -522,6 +530,31 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // apart are a fixed offset apart.
 __device__ __forceinline__ int a_chunk(int r, int c) { return c ^ (r & 7); }
 
+// The same for stages of half a slab (4 chunks of 16 bytes per A row): row r
+// chunk c sits at physical chunk c ^ s(r), s(r) = r2 | (r1 ^ r3) << 1 (bit i
+// of r is ri).  Any 16 consecutive rows then fill 16 distinct 16-byte slots
+// of a 256-byte bank row, and any 8 of them starting at a multiple of 8 fill
+// 8 distinct slots of a 128-byte one, so a ds_read_b128 fragment read (16
+// rows, one chunk each) is free of bank conflicts whether the LDS serves
+// 8 or 16 lanes per pass.  s depends on bits 1..3 of r only, so fragments
+// 16 rows apart are a fixed offset apart.
+__device__ __forceinline__ int a_chunk32(int r, int c) {
+    return c ^ (((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1));
+}
+
+// Row and logical chunk of A-stage chunk position L (16-byte units) of
+// configuration C: the global chunk a lane fetches into position L.
+template <class C>
+__device__ __forceinline__ void a_position(int L, int& r, int& c) {
+    if constexpr (C::KS == 64) {
+        r = L >> 3;
+        c = a_chunk(r, L & 7);
+    } else {
+        r = L >> 2;
+        c = a_chunk32(r, L & 3);
+    }
+}
+
 // Physical chunk of logical chunk c in B row k.  A transpose read covers,
 // per 32 lanes, rows 8g + (0..3) for g in {0,1} (or {2,3}) and two adjacent
 // chunks per row; the XOR term 2*((k & 3) | ((k >> 3) & 1) << 2) gives those
@@ -576,7 +609,8 @@ __device__ __forceinline__ TileDma<C> tile_dma(const TileJob& j) {
 #pragma unroll
     for (int q = 0; q < C::A_PER_WAVE; ++q) {
         const int L = (wave * C::A_PER_WAVE + q) * 64 + lane;
-        const int r = L >> 3, c = a_chunk(r, L & 7);
+        int r, c;
+        a_position<C>(L, r, c);
         const int rr = min(j.m0 + r, j.a_rows - 1) - j.m0;
         d.va[q] = (uint32_t)rr * (uint32_t)j.lda * 2u + (uint32_t)c * 16u;
     }
@@ -590,16 +624,17 @@ __device__ __forceinline__ TileDma<C> tile_dma(const TileJob& j) {
     return d;
 }
 
-// Issue the DMA of slab ks (B part and/or A part) into stage `stage`.  Every
+// Issue the DMA of K stage hs (K elements hs*KS .. hs*KS+KS-1; the slab
+// itself when KS = 64) into ring stage `stage`, B part or A part.  Every
 // wave issues B_PER_WAVE B instructions and A_PER_WAVE A instructions; lane
 // i of an instruction fills LDS chunk L0 + i with the global chunk that
 // belongs there under the swizzle.  TAIL: per-lane addresses, with the zero
 // page for rows, columns and K indices outside the matrices.
 template <class C, bool TAIL>
-__device__ __forceinline__ void issue_b(const TileJob& j, const TileDma<C>& d, int ks, int stage) {
+__device__ __forceinline__ void issue_b(const TileJob& j, const TileDma<C>& d, int hs, int stage) {
     char* st = lds_ring<C>() + stage * C::STAGE + C::A_BYTES;
     const int wave = uniform_wave();
-    const int k0 = ks * BK;
+    const int k0 = hs * C::KS;
     if constexpr (!TAIL) {
         const char* base = d.b_base + (size_t)k0 * j.ldb * 2;
 #pragma unroll
@@ -623,10 +658,10 @@ __device__ __forceinline__ void issue_b(const TileJob& j, const TileDma<C>& d, i
 }
 
 template <class C, bool TAIL>
-__device__ __forceinline__ void issue_a(const TileJob& j, const TileDma<C>& d, int ks, int stage) {
+__device__ __forceinline__ void issue_a(const TileJob& j, const TileDma<C>& d, int hs, int stage) {
     char* st = lds_ring<C>() + stage * C::STAGE;
     const int wave = uniform_wave();
-    const int k0 = ks * BK;
+    const int k0 = hs * C::KS;
     if constexpr (!TAIL) {
         const char* base = d.a_base + (size_t)k0 * 2;
 #pragma unroll
@@ -638,7 +673,8 @@ __device__ __forceinline__ void issue_a(const TileJob& j, const TileDma<C>& d, i
         for (int q = 0; q < C::A_PER_WAVE; ++q) {
             const int L0 = (wave * C::A_PER_WAVE + q) * 64;
             const int L = L0 + lane;
-            const int r = L >> 3, c = a_chunk(r, L & 7);
+            int r, c;
+            a_position<C>(L, r, c);
             const int gm = j.m0 + r, gk = k0 + c * 8;
             const uint16_t* src = (gm < j.a_rows && gk < j.K) ? j.A + (size_t)gm * j.lda + gk : j.zero;
             dma16(src, st + L0 * 16);
@@ -700,10 +736,15 @@ __device__ __forceinline__ FragBase<C> frag_base() {
     const int wm = wave / C::WN, wn = wave % C::WN;
     const int g = lane >> 4, jj = lane & 15;
     const int r = wm * C::WTM + jj;
+    if constexpr (C::KS == 64) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) f.a[kk] = ring + (r * 8 + a_chunk(r, kk * 4 + g)) * 16;
+        for (int kk = 0; kk < 2; ++kk) f.a[kk] = ring + (r * 8 + a_chunk(r, kk * 4 + g)) * 16;
+    } else {
+        f.a[0] = f.a[1] = ring + (r * 4 + a_chunk32(r, g)) * 16;
+    }
     // lane (g, jj) of a transpose read: row k = 8g + jj/4 (+4 for the upper
-    // rows, +32 for half slab 1), columns (jj%4)*4..+3 of the fragment.
+    // rows, +32 for half slab 1 of a whole-slab stage), columns (jj%4)*4..+3
+    // of the fragment.
     // b_chunk depends on k & 3 and (k >> 3) & 1 only, which neither +4 nor
     // +32 changes.
     const int k = g * 8 + (jj >> 2);
@@ -716,14 +757,16 @@ __device__ __forceinline__ FragBase<C> frag_base() {
     return f;
 }
 
-// Issue the LDS reads of half slab KK of the stage at byte offset `so` into f.
+// Issue the LDS reads of half slab KK of the stage at byte offset `so` into f
+// (KK = 0 for a stage of half a slab).
 template <class C, int KK>
 __device__ __forceinline__ void frag_load(const FragBase<C>& fb, uint32_t so, Frags<C>& f) {
-    constexpr uint32_t A_MAX = (C::FM - 1) * 16 * 128;
+    static_assert(KK == 0 || C::KS == 64, "a stage of half a slab has one half");
+    constexpr uint32_t A_MAX = (C::FM - 1) * 16 * C::A_ROW;
     constexpr uint32_t B_MAX = (KK * 32 + 4) * C::CPR * 16;
     static_assert(A_MAX < 65536 && C::A_BYTES + B_MAX < 65536, "stage too large for ds offsets");
     const uint32_t a = fb.a[KK] + so;
-    static_for<0, C::FM>([&](auto fm) { f.a[fm] = ds_read_b128<decltype(fm)::value * 16 * 128>(a); });
+    static_for<0, C::FM>([&](auto fm) { f.a[fm] = ds_read_b128<decltype(fm)::value * 16 * C::A_ROW>(a); });
     static_for<0, C::FN>([&](auto fn) {
         const uint32_t b = fb.b[fn] + so;
         const u32x2 lo = ds_read_tr16_b64<KK * 32 * C::CPR * 16>(b);
@@ -754,7 +797,7 @@ __device__ __forceinline__ void mfma_block(f32x4 (&acc)[C::FM][C::FN], const Fra
 template <class C, int KK, int R>
 __device__ __forceinline__ void frag_read_one(const FragBase<C>& fb, uint32_t so, Frags<C>& f) {
     if constexpr (R < C::FM) {
-        f.a[R] = ds_read_b128<R * 16 * 128>(fb.a[KK] + so);
+        f.a[R] = ds_read_b128<R * 16 * C::A_ROW>(fb.a[KK] + so);
     } else {
         constexpr int fn = (R - C::FM) / 2, hi = (R - C::FM) % 2;
         const u32x2 v = ds_read_tr16_b64<(KK * 32 + 4 * hi) * C::CPR * 16>(fb.b[fn] + so);
@@ -873,9 +916,9 @@ __device__ __forceinline__ void lds_barrier() { ring_barrier<63>(); }
 // DMA instruction Q (of LPS) of slab ks into stage `stage`: Q < B_PER_WAVE
 // is B instruction Q, the rest are the A instructions.
 template <class C, bool TAIL, int Q>
-__device__ __forceinline__ void issue_one(const TileJob& j, const TileDma<C>& d, int ks, int stage) {
+__device__ __forceinline__ void issue_one(const TileJob& j, const TileDma<C>& d, int hs, int stage) {
     const int wave = uniform_wave();
-    const int k0 = ks * BK;
+    const int k0 = hs * C::KS;
     if constexpr (Q < C::B_PER_WAVE) {
         char* st = lds_ring<C>() + stage * C::STAGE + C::A_BYTES;
         if constexpr (!TAIL) {
@@ -899,7 +942,8 @@ __device__ __forceinline__ void issue_one(const TileJob& j, const TileDma<C>& d,
         } else {
             const int L0 = (wave * C::A_PER_WAVE + QA) * 64;
             const int L = L0 + (thread_index() & 63);
-            const int r = L >> 3, c = a_chunk(r, L & 7);
+            int r, c;
+            a_position<C>(L, r, c);
             const int gm = j.m0 + r, gk = k0 + c * 8;
             dma16((gm < j.a_rows && gk < j.K) ? j.A + (size_t)gm * j.lda + gk : j.zero, st + L0 * 16);
         }
@@ -1007,6 +1051,104 @@ __device__ __forceinline__ void tile_kloop(const TileJob& j, f32x4 (&acc)[C::FM]
     }
 }
 
+// The MFMAs of fragments f (a ring of half slabs), with the reads of the
+// next stage's fragments into g issued among them in read_plan order and
+// the LPS DMA instructions of K stage hr (into ring stage `stage`) issued
+// after every other MFMA: weights first, then the consumer's wait for the
+// slab (where the stage starts one), then the activations.
+template <class C, int DT, bool TAIL, class Wait>
+__device__ __forceinline__ void mfma_block_fine(f32x4 (&acc)[C::FM][C::FN], const Frags<C>& f, const FragBase<C>& fb,
+                                                uint32_t so, Frags<C>& g, const TileJob& j, const TileDma<C>& d,
+                                                int hr, int stage, Wait& wait) {
+    constexpr ReadPlan<C> plan = read_plan<C>();
+    constexpr int GAP = (C::FM * C::FN) / C::LPS >= 2 ? 2 : 1;
+    constexpr int HPS = BK / C::KS;
+    static_for<0, C::FM * C::FN>([&](auto i) {
+        constexpr int I = decltype(i)::value;
+        acc[I / C::FN][I % C::FN] = mfma16x16x32<DT>(f.a[I / C::FN], f.b[I % C::FN], acc[I / C::FN][I % C::FN]);
+        if constexpr (plan.after[I] >= 0) frag_read_one<C, 0, plan.after[I]>(fb, so, g);
+        if constexpr (I % GAP == 0 && I / GAP < C::LPS) {
+            constexpr int Q = I / GAP;
+            if constexpr (Q == C::B_PER_WAVE) {
+                if (hr % HPS == 0) wait(hr / HPS);
+            }
+            issue_one<C, TAIL, Q>(j, d, hr, stage);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    });
+    static_for<0, plan.ntail>([&](auto t) { frag_read_one<C, 0, plan.tail[decltype(t)::value]>(fb, so, g); });
+    if constexpr ((C::FM * C::FN + GAP - 1) / GAP < C::LPS) {
+        static_for<(C::FM * C::FN + GAP - 1) / GAP, C::LPS>([&](auto q) {
+            constexpr int Q = decltype(q)::value;
+            if constexpr (Q == C::B_PER_WAVE) {
+                if (hr % HPS == 0) wait(hr / HPS);
+            }
+            issue_one<C, TAIL, Q>(j, d, hr, stage);
+        });
+    }
+}
+
+// The K loop over a ring of NS stages of half a slab (KS = 32).  K stage h
+// (of 32 elements; a part's slabs ks0 .. ks1-1 are stages 2 ks0 .. 2 ks1 - 1)
+// lives in ring stage (h - 2 ks0) % NS.  Stages h0 .. h0+NS-1 fill the ring
+// before the first step and the fragments of stage h0 are read.  One step per
+// stage h, its fragments in registers (f):
+//   wait for this wave's reads of stage h, then for the DMA of stage h+1 in
+//   every wave (barrier): the ring stage of h is free again;
+//   the MFMAs of f, with the reads of stage h+1's fragments (g) and the DMA
+//   of stage h+NS into the ring stage of h (weights first, then the
+//   consumer's wait for the slab, then the activations) issued among them.
+// So NS-1 stages are in flight while one is multiplied and the next one is
+// read (three for NS = 4: 96 KB for 256 x 256 tiles, where a ring of two
+// whole slabs has one slab, 64 KB), and no MFMA waits for its fragments
+// after a barrier.  The number of steps is even, so the loop takes two per
+// iteration and f and g swap roles without copies.
+template <class C, int DT, bool TAIL, class Wait>
+__device__ __forceinline__ void tile_kloop_fine(const TileJob& j, f32x4 (&acc)[C::FM][C::FN], Wait& wait) {
+    static_assert(C::KS == 32 && C::NS >= 3, "ring of half slabs");
+    constexpr int HPS = BK / C::KS;       // stages per slab
+    const FragBase<C> fb = frag_base<C>();
+    const TileDma<C> d = tile_dma<C>(j);
+    const int h0 = j.ks0 * HPS, h1 = j.ks1 * HPS;
+    auto request = [&](int h, int stage) {
+        issue_b<C, TAIL>(j, d, h, stage);
+        if (h % HPS == 0) wait(h / HPS);
+        issue_a<C, TAIL>(j, d, h, stage);
+    };
+    // (a part shorter than the ring requests its last stage again into the
+    // ring stages it does not use, so that every wave has issued the same
+    // number of DMA instructions at every barrier)
+#pragma unroll
+    for (int i = 0; i < C::NS; ++i) request(h0 + i < h1 ? h0 + i : h1 - 1, i);
+    Frags<C> f, g;
+    // stage h0 landed in every wave
+    ring_barrier<C::LPS * (C::NS - 1)>();
+    frag_load<C, 0>(fb, 0u, f);
+    __builtin_amdgcn_sched_barrier(0);
+    int st = 0;
+    auto step = [&](int h, Frags<C>& cur, Frags<C>& nxt) {
+        const int sn = st + 1 == C::NS ? 0 : st + 1;
+        lgkm_wait<0>();
+        frag_pin(cur);
+        // Every step requests one stage into the ring stage of h, so the
+        // DMA count per step and the waits stay fixed: past the part's end
+        // that is the part's last stage again (never read from there).
+        ring_barrier<C::LPS * (C::NS - 2)>();
+        const int hr = h + C::NS < h1 ? h + C::NS : h1 - 1;
+        mfma_block_fine<C, DT, TAIL>(acc, cur, fb, (uint32_t)sn * C::STAGE, nxt, j, d, hr, st, wait);
+        __builtin_amdgcn_sched_barrier(0);
+        st = sn;
+    };
+    for (int h = h0; h < h1; h += 2) {
+        step(h, f, g);
+        step(h + 1, g, f);
+    }
+    // the last step's reads (never used) land before their registers can be
+    // given to anything else
+    lgkm_wait<0>();
+    frag_pin(f);
+}
+
 template <class C, int DT, class Wait>
 __device__ __forceinline__ void tile_mainloop(const TileJob& j, f32x4 (&acc)[C::FM][C::FN], Wait& wait) {
 #pragma unroll
@@ -1014,8 +1156,13 @@ __device__ __forceinline__ void tile_mainloop(const TileJob& j, f32x4 (&acc)[C::
 #pragma unroll
         for (int fn = 0; fn < C::FN; ++fn) acc[fm][fn] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (j.ks1 > j.ks0) {
-        if (j.ks1 * BK <= j.K) tile_kloop<C, DT, false>(j, acc, wait);
-        else tile_kloop<C, DT, true>(j, acc, wait);
+        if constexpr (C::KS == 32) {
+            if (j.ks1 * BK <= j.K) tile_kloop_fine<C, DT, false>(j, acc, wait);
+            else tile_kloop_fine<C, DT, true>(j, acc, wait);
+        } else {
+            if (j.ks1 * BK <= j.K) tile_kloop<C, DT, false>(j, acc, wait);
+            else tile_kloop<C, DT, true>(j, acc, wait);
+        }
     }
     // every wave is done reading the ring (and all DMA has landed) before
     // the epilogue reuses stage 0

@@ -430,8 +430,8 @@ static hipError_t launch_c(const ChainArgs& a, int dtype, int what, int grid, hi
                            : launch_t<C, DT_BF16>(a, what, grid, s, occ);
 }
 
-#define MLPC_PICK(id, bm, bn, wm, wn, ns, occ) \
-    if constexpr (id == MLPC_CFG) return TileCfg<bm, bn, wm, wn, ns, occ>{};
+#define MLPC_PICK(id, bm, bn, wm, wn, ns, occ, ks) \
+    if constexpr (id == MLPC_CFG) return TileCfg<bm, bn, wm, wn, ns, occ, ks>{};
 static constexpr auto this_cfg() { MLPC_CONFIGS(MLPC_PICK) }
 #undef MLPC_PICK
 using Cfg = decltype(this_cfg());

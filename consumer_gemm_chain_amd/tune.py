@@ -51,8 +51,8 @@ def candidate_configs(M):
     if M <= 128:
         return (0, 4, 3)
     if M <= 512:
-        return (4, 3, 7)
-    return (3, 7)
+        return (4, 3, 8)
+    return (3, 7, 8)
 
 
 def candidate_splits(H, I):
@@ -97,7 +97,7 @@ def time_plan(dev, w, M, policy, cfg, split, reps, stream, flush=None):
 def tune_shape(dev, w, M, stream, flush_buf, cus):
     cfgs = candidate_configs(M)
     splits = candidate_splits(w.H, w.I)
-    reps = 8 if M <= 1024 else 4
+    reps = 12 if M <= 1024 else 6
     times = {}
     for split in splits:
         for pol in POLICIES:

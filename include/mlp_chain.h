@@ -258,10 +258,14 @@ int mlp_chain_debug_set_grid(mlp_chain_t h, int grid);
 /* Override the order in which each XCD walks its block of the tile grid:
  * bit 0 for GEMM1, bit 1 for GEMM2, set = column-major (the tiles an XCD
  * runs together form a patch of rows x columns rather than a run along one
- * row); -1 restores the planner's choice.  The order changes which tiles
- * share an XCD's L2 at a time and, for the fused policies, when each row
- * block of T completes -- never any output value.  Takes effect on the next
- * run.  Returns MLP_EINVAL for a NULL handle or a value outside -1..3. */
+ * row); bits 4..7 (rx = order >> 4, one of 1, 2, 4, 8; 0 = planned) the
+ * number of XCD rows of the partition of each GEMM's tile grid over the 8
+ * XCDs (rx rows of 8/rx XCDs: with rx = 1 every XCD holds all row blocks,
+ * so the whole GPU completes the row blocks of T one after another).  -1
+ * restores the planner's choices.  The order changes which tiles share an
+ * XCD's L2 at a time and, for the fused policies, when each row block of T
+ * completes -- never any output value.  Takes effect on the next run.
+ * Returns MLP_EINVAL for a NULL handle or a value outside those. */
 int mlp_chain_debug_set_order(mlp_chain_t h, int order);
 
 /* Test hook: put the handle's synchronization state where the fused run of
