@@ -411,9 +411,20 @@ int zero_workspace(mlp_chain* h) {
     return MLP_OK;
 }
 
+// Words between the 8 copies of the ready flags, one per XCD: the flags of
+// all layers, rounded up to 1 KB, plus 128 bytes, so that each copy starts
+// on the next class of 128-byte lines (another memory channel).  Producers
+// publish into every copy; the consumers of an XCD poll their own copy, so
+// the hundreds of consumers that may wait at small M spread their polls over
+// eight sets of lines instead of one.
+uint32_t flag_stride(const mlp_chain* h) {
+    const size_t n = (size_t)h->layers * h->T1 + (size_t)(h->layers - 1) * h->T2;
+    return (uint32_t)(align_up(n, 256) + 32);
+}
+
 // Workspace layout of the current plan at `base` (nullptr: sizes only), for
 // a chain of L = layers MLP layers:
-//   T [L][M, ldt] | Y [L-1][M, ldy] | flags [L T1 + (L-1) T2] | rowcnt [(2L-1) Mt] | cnt1 [L T1] |
+//   T [L][M, ldt] | Y [L-1][M, ldy] | flags [8][fstride >= L T1 + (L-1) T2] | rowcnt [(2L-1) Mt] | cnt1 [L T1] |
 //   cnt2 [L T2] | rdy1 [L T1 S1] | rdy2 [L T2 S2] | ticket | status | zero page | part1 [L] | part2 [L]
 // (flags .. zero page, sync_bytes long, is the region that starts at zero).
 // Sets ws_bytes and sync_bytes; with a base also every buffer pointer.
@@ -422,7 +433,7 @@ void layout_workspace(mlp_chain* h, char* base) {
     const size_t acc_bytes = (size_t)h->ci.BM * h->ci.BN * 4;     // one tile's fp32 accumulators
     const size_t t_b = align_up(L * (size_t)h->M * (size_t)h->ldt * 2, 256);
     const size_t ys_b = align_up((L - 1) * (size_t)h->M * (size_t)h->ldy * 2, 256);
-    const size_t f_b = align_up((L * h->T1 + (L - 1) * h->T2) * 4, 256);
+    const size_t f_b = align_up(8 * (size_t)flag_stride(h) * 4, 256);
     const size_t r_b = align_up((2 * L - 1) * h->Mt * 4, 256);
     const size_t c1_b = align_up(L * h->T1 * 4, 256);
     const size_t c2_b = align_up(L * h->T2 * 4, 256);
@@ -502,6 +513,7 @@ mlpc::ChainArgs make_args(const mlp_chain* h, const void* x, const void* w1, con
     a.ticket = h->ticket + 512 * (h->epoch & 1u);
     a.ticket_next = h->ticket + 512 * ((h->epoch & 1u) ^ 1u);
     a.flags = h->flags;
+    a.fstride = flag_stride(h);
     a.rowcnt = h->rowcnt;
     a.status = h->status;
     a.zero = h->zero;
@@ -887,7 +899,7 @@ int mlp_chain_debug_set_epoch(mlp_chain_t h, uint32_t epoch) {
     // flag published with it, every row counter at epoch x tiles per row
     const uint32_t L = h->layers;
     hipError_t e = hipDeviceSynchronize();
-    if (e == hipSuccess) e = hipMemsetD32(h->flags, (int)epoch, L * h->T1 + (L - 1) * h->T2);
+    if (e == hipSuccess) e = hipMemsetD32(h->flags, (int)epoch, 8 * (size_t)flag_stride(h));
     if (e == hipSuccess) e = hipMemsetD32(h->rowcnt, (int)(epoch * h->N1t), L * h->Mt);
     if (e == hipSuccess && L > 1) e = hipMemsetD32(h->rowcnt + L * h->Mt, (int)(epoch * h->N2t), (L - 1) * h->Mt);
     if (e == hipSuccess) e = hipDeviceSynchronize();

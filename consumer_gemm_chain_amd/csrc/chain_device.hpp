@@ -79,7 +79,8 @@ struct ChainArgs {
     uint32_t* ticket;       // this run's 8 tile-queue counters (one per XCD), 64 words apart; zero when
                             // the run starts
     uint32_t* ticket_next;  // the other set of 8 (used by the next run): workgroup 0 zeroes it
-    uint32_t* flags;        // [Mt * N1t] ready epochs (tile_sync)
+    uint32_t* flags;        // [8][fstride] ready epochs (tile_sync): one copy per XCD, each [Mt * N1t]
+    uint32_t fstride;       // words between the XCDs' copies of the flags
     uint32_t* rowcnt;       // [Mt] producer completions (row_sync)
     uint32_t* status;       // sticky watchdog status (nonzero = a consumer gave up)
     const uint16_t* zero;   // >= 16 zero bytes: the source of every out-of-range chunk
@@ -1483,9 +1484,16 @@ __device__ __forceinline__ bool split_reduce(f32x4 (&acc)[C::FM][C::FN], float* 
 // time, the tiles ran 2-20% slower than the same tiles in the stand-alone
 // kernels.  Returns true if this part wrote the tile's output (always,
 // unless the tile is split and another part arrives last).
-template <class C, int DT, int ROLE, class Wait>
+struct NoPrefetch {
+    __device__ __forceinline__ void operator()() const {}
+};
+
+// `done()` is called once the part has no wait left (after its K loop and
+// any split-K reduction), before the epilogue: the persistent kernels start
+// drawing their next item there, so that the draw overlaps the stores.
+template <class C, int DT, int ROLE, class Wait, class Done = NoPrefetch>
 __device__ __forceinline__ bool run_tile(const ChainArgs& a, uint32_t mb, uint32_t nb, uint32_t s, uint32_t* s_flag,
-                                         Wait& wait, uint32_t l = 0) {
+                                         Wait& wait, uint32_t l = 0, Done done = Done{}) {
     f32x4 acc[C::FM][C::FN];
     // layer l's split-K counters, ready words and partials follow layer
     // l-1's: its tiles are numbered from l * T1 (GEMM1) or l * T2 (GEMM2)
@@ -1496,7 +1504,10 @@ __device__ __forceinline__ bool run_tile(const ChainArgs& a, uint32_t mb, uint32
     if (S > 1) {
         const bool last = ROLE == 1 ? split_reduce<C>(acc, a.part1, a.cnt1, a.rdy1, tile, s, S, s_flag, a.status, a.spin_limit)
                                     : split_reduce<C>(acc, a.part2, a.cnt2, a.rdy2, tile, s, S, s_flag, a.status, a.spin_limit);
+        done();
         if (!last) return false;
+    } else {
+        done();
     }
     if constexpr (ROLE == 1)
         tile_epilogue<C, DT>(acc, a.act, j.inter, layer_t(a, l), a.ldt, a.M, a.I, j.m0, j.n0);

@@ -205,12 +205,68 @@ __device__ __forceinline__ uint32_t draw_item(const ChainArgs& a, Queues& q) {
     }
 }
 
+// Publication of a ready flag by wave 0 (called by all its lanes, after the
+// workgroup barrier that follows the tile's stores): one agent-scope release,
+// then lane x < 8 stores the epoch into XCD x's copy of the flags.
+__device__ __forceinline__ void publish_flag(const ChainArgs& a, uint32_t idx) {
+    const uint32_t lane = threadIdx.x & 63;
+    if (lane < 8) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_store(a.flags + lane * a.fstride + idx, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Early draw.  Once an item has no wait left (its K loop and split-K
+// reduction are done), the first thread of wave 1 takes the next position of
+// the own queue with one atomic, and the epilogue's stores and the
+// publication run while it is in flight; after the publication it leaves the
+// position in LDS, and wave 0 resolves it at the top of the loop
+// (resolve_early), falling back to draw_item, which scans the other queues,
+// only when that position is past the queue's end.  The draw of the next
+// item then costs the workgroup about one memory round trip less (two
+// before: the counters' loads, then the atomic).  The atomic is wave 1's so
+// that the release that publishes the item (thread 0's) does not wait for it:
+// at the end of a wave of producers the queue counters are contended and the
+// atomic can take microseconds.  An item never waits for one its own
+// workgroup holds: the early draw comes after the current item's last wait.
+constexpr uint32_t EARLY_THREAD = 64;
+
+struct EarlyDraw {
+    const ChainArgs& a;
+    uint32_t own;
+    bool& issued;       // uniform: an early draw was started for the current item
+    uint32_t& pos;      // thread EARLY_THREAD: the position the atomic returned
+    __device__ __forceinline__ void operator()() const {
+        issued = true;
+        // (a wrapping increment with an all-ones bound is +1 here; unlike an
+        // atomic add the compiler does not rewrite it into a wave-wide add
+        // whose result it waits for at once)
+        if (threadIdx.x == EARLY_THREAD)
+            pos = __builtin_amdgcn_atomic_inc32(a.ticket + 64 * own, 0xffffffffu, __ATOMIC_RELAXED, "agent");
+    }
+};
+
+// Wave 0 only: the item at the position the early draw took, or NO_ITEM
+// with the own queue marked dry.
+template <bool LAYERS>
+__device__ __forceinline__ uint32_t resolve_early(const ChainArgs& a, Queues& q, uint32_t c) {
+    if (q.dry & 1u) return NO_ITEM;
+    const XcdBlock bp = xcd_block(a.Mt, a.N1t, a.S1, a.rx, q.own);
+    const XcdBlock bc = xcd_block(a.Mt, a.N2t, a.S2, a.rx, q.own);
+    const uint32_t len = (LAYERS ? a.layers : 1u) * (bp.len + bc.len);
+    const uint32_t p = c + min(len, queue_owners(a.grid, q.own));
+    if (p < len) return LAYERS ? queue_item_layers(a, bp, bc, q.P1, p) : queue_item(a, bp, bc, q.P1, p);
+    q.dry |= 1u;
+    return NO_ITEM;
+}
+
 template <class C, int DT, int POL>
 __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(C::OCC)))
 void chain_persistent_kernel(ChainArgs a) {
     __shared__ uint32_t s_ticket;
     __shared__ uint32_t s_ready;
     __shared__ uint32_t s_flag;
+    __shared__ uint32_t s_pos;
     const uint32_t P1 = a.T1 * a.S1;
     const int bn1 = a.act == ACT_SWIGLU ? C::BN / 2 : C::BN;
     Queues q{blockIdx.x & 7u, 0u, P1};
@@ -224,13 +280,20 @@ void chain_persistent_kernel(ChainArgs a) {
         const uint32_t pos = blockIdx.x >> 3;
         if (pos < bp.len + bc.len) item = queue_item(a, bp, bc, P1, pos);
     }
+    bool issued = false;
+    uint32_t pos = 0;
+    static_assert(C::NT > EARLY_THREAD, "the early draw is wave 1's");
+    const EarlyDraw early{a, q.own, issued, pos};
     for (;;) {
         if (item == NO_ITEM) {
-            // draw the next item (wave 0), from the own queue or the next ones
+            // the next item (wave 0): the early draw's, else from the own
+            // queue or the next ones
             if ((threadIdx.x >> 6) == 0) {
-                const uint32_t it = draw_item(a, q);
+                uint32_t it = issued ? resolve_early<false>(a, q, s_pos) : NO_ITEM;
+                if (it == NO_ITEM) it = draw_item(a, q);
                 if (threadIdx.x == 0) s_ticket = it;
             }
+            issued = false;
             __syncthreads();
             // The item is the same for every thread of the workgroup; reading
             // it through readfirstlane makes that visible to the compiler, so
@@ -253,15 +316,15 @@ void chain_persistent_kernel(ChainArgs a) {
             // first producer block the part's K range reads
             const uint32_t first = prod ? 0u : (part * a.ksp2 * BK) / (uint32_t)bn1;
             const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
-            ChainWait<POL> w{!prod, a.flags + mb * a.N1t, a.rowcnt + mb, a.N1t,
+            ChainWait<POL> w{!prod, a.flags + q.own * a.fstride + mb * a.N1t, a.rowcnt + mb, a.N1t,
                              POL == POL_ROW ? a.epoch * a.N1t : a.epoch, bn1, a.status, a.spin_limit,
                              a.acq_agent, &s_ready, first, false, t_start};
             bool wrote;
             if (prod) {
                 NoWait nw;
-                wrote = run_tile<C, DT, 1>(a, mb, nb, part, &s_flag, nw);
+                wrote = run_tile<C, DT, 1>(a, mb, nb, part, &s_flag, nw, 0, early);
             } else {
-                wrote = run_tile<C, DT, 2>(a, mb, nb, part, &s_flag, w);
+                wrote = run_tile<C, DT, 2>(a, mb, nb, part, &s_flag, w, 0, early);
             }
             if (a.trace && threadIdx.x == 0) trace_item(a, t, t_start, w.t_waited, wrote);
             if (prod && wrote) {
@@ -270,15 +333,14 @@ void chain_persistent_kernel(ChainArgs a) {
                 // release (workgroup release + barrier), which publishes the tile
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
                 __syncthreads();
-                if (threadIdx.x == 0) {
-                    if constexpr (POL == POL_TILE)
-                        __hip_atomic_store(a.flags + mb * a.N1t + nb, a.epoch, __ATOMIC_RELEASE,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-                    else
-                        __hip_atomic_fetch_add(a.rowcnt + mb, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                if constexpr (POL == POL_TILE) {
+                    if ((threadIdx.x >> 6) == 0) publish_flag(a, mb * a.N1t + nb);
+                } else if (threadIdx.x == 0) {
+                    __hip_atomic_fetch_add(a.rowcnt + mb, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
         }
+        if (issued && threadIdx.x == EARLY_THREAD) s_pos = pos;
         // Keep this barrier: it separates the thread-0-only release above from
         // the thread-0-only ticket draw at the top of the loop.  Without it the
         // compiler may merge the two across the back edge into a loop in which
@@ -310,6 +372,7 @@ void chain_layers_kernel(ChainArgs a) {
     __shared__ uint32_t s_ticket;
     __shared__ uint32_t s_ready;
     __shared__ uint32_t s_flag;
+    __shared__ uint32_t s_pos;
     const uint32_t P1 = a.T1 * a.S1;
     const uint32_t P = P1 + a.T2 * a.S2;      // items per layer
     const int bn1 = a.act == ACT_SWIGLU ? C::BN / 2 : C::BN;
@@ -323,12 +386,18 @@ void chain_layers_kernel(ChainArgs a) {
         const uint32_t pos = blockIdx.x >> 3;
         if (pos < a.layers * (bp.len + bc.len)) item = queue_item_layers(a, bp, bc, P1, pos);
     }
+    bool issued = false;
+    uint32_t pos = 0;
+    static_assert(C::NT > EARLY_THREAD, "the early draw is wave 1's");
+    const EarlyDraw early{a, q.own, issued, pos};
     for (;;) {
         if (item == NO_ITEM) {
             if ((threadIdx.x >> 6) == 0) {
-                const uint32_t it = draw_item<true>(a, q);
+                uint32_t it = issued ? resolve_early<true>(a, q, s_pos) : NO_ITEM;
+                if (it == NO_ITEM) it = draw_item<true>(a, q);
                 if (threadIdx.x == 0) s_ticket = it;
             }
+            issued = false;
             __syncthreads();
             item = __builtin_amdgcn_readfirstlane(s_ticket);
             __syncthreads();
@@ -353,18 +422,18 @@ void chain_layers_kernel(ChainArgs a) {
                 // 0's GEMM1 reads x and waits for nothing (an inactive wait,
                 // so that both share one copy of the tile code)
                 const uint32_t lp = l > 0 ? l - 1 : 0;
-                const uint32_t* fy = a.flags + a.layers * a.T1 + lp * a.T2;
+                const uint32_t* fy = a.flags + q.own * a.fstride + a.layers * a.T1 + lp * a.T2;
                 const uint32_t* cy = a.rowcnt + (a.layers + lp) * a.Mt;
                 ChainWait<POL> w{l > 0, fy + mb * a.N2t, cy + mb, a.N2t,
                                  POL == POL_ROW ? a.epoch * a.N2t : a.epoch, C::BN, a.status, a.spin_limit,
                                  0u, &s_ready, (part * a.ksp1 * BK) / (uint32_t)C::BN, false, t_start};
-                wrote = run_tile<C, DT, 1>(a, mb, nb, part, &s_flag, w, l);
+                wrote = run_tile<C, DT, 1>(a, mb, nb, part, &s_flag, w, l, early);
                 t_waited = w.t_waited;
             } else {
-                ChainWait<POL> w{true, a.flags + l * a.T1 + mb * a.N1t, a.rowcnt + l * a.Mt + mb, a.N1t,
+                ChainWait<POL> w{true, a.flags + q.own * a.fstride + l * a.T1 + mb * a.N1t, a.rowcnt + l * a.Mt + mb, a.N1t,
                                  POL == POL_ROW ? a.epoch * a.N1t : a.epoch, bn1, a.status, a.spin_limit,
                                  a.acq_agent, &s_ready, (part * a.ksp2 * BK) / (uint32_t)bn1, false, t_start};
-                wrote = run_tile<C, DT, 2>(a, mb, nb, part, &s_flag, w, l);
+                wrote = run_tile<C, DT, 2>(a, mb, nb, part, &s_flag, w, l, early);
                 t_waited = w.t_waited;
             }
             if (a.trace && threadIdx.x == 0) trace_item(a, t, t_start, t_waited, wrote);
@@ -373,18 +442,16 @@ void chain_layers_kernel(ChainArgs a) {
                 chaos_delay(t ^ (a.epoch << 20));
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
                 __syncthreads();
-                if (threadIdx.x == 0) {
-                    if constexpr (POL == POL_TILE) {
-                        uint32_t* f = prod ? a.flags + l * a.T1 + mb * a.N1t + nb
-                                           : a.flags + a.layers * a.T1 + l * a.T2 + mb * a.N2t + nb;
-                        __hip_atomic_store(f, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-                    } else {
-                        uint32_t* c = prod ? a.rowcnt + l * a.Mt + mb : a.rowcnt + (a.layers + l) * a.Mt + mb;
-                        __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-                    }
+                if constexpr (POL == POL_TILE) {
+                    if ((threadIdx.x >> 6) == 0)
+                        publish_flag(a, prod ? l * a.T1 + mb * a.N1t + nb : a.layers * a.T1 + l * a.T2 + mb * a.N2t + nb);
+                } else if (threadIdx.x == 0) {
+                    uint32_t* c = prod ? a.rowcnt + l * a.Mt + mb : a.rowcnt + (a.layers + l) * a.Mt + mb;
+                    __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
         }
+        if (issued && threadIdx.x == EARLY_THREAD) s_pos = pos;
         // (as in the one-layer kernel: keeps the thread-0 release apart from
         // the thread-0 ticket draw at the top of the loop)
         __syncthreads();

@@ -139,8 +139,8 @@ def test_k_loops_keep_accumulators_in_place_and_use_scalar_base_dma(asm):
 # of the 256 x 256 configuration keeps a few values per item in scratch
 # (stored once, reloaded once per item, never inside a K loop).  SGPR spills
 # go to VGPR lanes and are bounded too.
-SGPR_SPILL_CAP = 112
-LAYERS_256x256_SPILL_CAP = 16
+SGPR_SPILL_CAP = 128
+LAYERS_256x256_SPILL_CAP = 24
 
 
 def _spills(text):
