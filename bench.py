@@ -84,7 +84,7 @@ def measured_traffic(kernel: str, workload: str, M: int, plan: str):
     profiles/<kernel>_<workload>_M<M>_traffic.md (FETCH_SIZE + WRITE_SIZE
     scaled by the copy calibration), or None when there is no summary or it
     was taken on other kernel sources or another plan (tile configuration and
-    K split, e.g. "config 7 split 2,1")."""
+    K split, e.g. "config 8 split 2,1")."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_M{M}_traffic.md")
     if not os.path.exists(path):
         return None
