@@ -35,6 +35,11 @@ def test_misaligned_and_null_pointers_rejected():
         assert mc.mlp_chain_status(h) == mc.MLP_OK
         info = mc.mlp_chain_info(h)
         assert info["epoch"] == 0          # rejected runs do not advance the epoch
+        # tile-order hook: order bits 0..1 and XCD rows 1, 2, 4 or 8 in bits 4..7
+        for bad in (-2, 4, 3 << 4, 5 << 4, 16 << 4):
+            assert lib.mlp_chain_debug_set_order(h, bad) == mc.MLP_EINVAL, bad
+        for good in (-1, 0, 3, 1 << 4, 2 | (8 << 4)):
+            assert lib.mlp_chain_debug_set_order(h, good) == mc.MLP_OK, good
     finally:
         mc.mlp_chain_destroy(h)
 

@@ -386,8 +386,9 @@ def test_tile_configs_agree_bitwise(act, dtype):
 @pytest.mark.parametrize("policy", ["stream_ordered", "row_sync", "tile_sync"])
 def test_tile_orders_agree_bitwise(oracle_mod, policy):
     """The order in which each XCD walks its tiles (row- or column-major, per
-    GEMM) moves no output bit, with and without a K split; checked on a
-    shape with several row blocks per XCD block and ragged edges."""
+    GEMM) and the number of XCD rows the tile grids are split into (1, 2, 4
+    or 8) move no output bit, with and without a K split; checked on a shape
+    with several row blocks per XCD block and ragged edges."""
     import torch
     from consumer_gemm_chain_amd.mlp_chain import MlpChain
     from tests._helpers import empty_dev, from_dev
@@ -398,7 +399,7 @@ def test_tile_orders_agree_bitwise(oracle_mod, policy):
     dev = (to_dev(x, dtype), to_dev(w1, dtype), to_dev(w2, dtype))
     for split in ((1, 1), (2, 3)):
         ref = None
-        for order in (0, 1, 2, 3, -1):
+        for order in (0, 1, 2, 3, -1, 1 << 4, 3 | (4 << 4), 2 | (8 << 4)):
             with MlpChain(M, H, I, act, dtype, policy) as ch:
                 ch.set_config(2)
                 ch.set_split(*split)
