@@ -15,7 +15,8 @@ So, per shape:
   2. the split is the one whose best tile_sync time is lowest, decided
      among the three best by a longer re-timing, hot and with the Infinity
      Cache flushed (the mean of the two medians);
-  3. each policy then takes its fastest configuration under that split.
+  3. each policy then takes its fastest configuration under that split,
+     its candidates re-timed in alternating rounds.
 The output is one MLPC_TUNED(M, H, I, act, cus, S1, S2, config_stream,
 config_row, config_tile) line per shape, with the measured times as a
 comment.  The planner uses a line only for the exact (M, H, I, act) and CU
@@ -56,9 +57,11 @@ def candidate_configs(M):
 
 
 def candidate_splits(H, I):
+    # (5 and 7 matter where a tile count such as LLaMA-65's 43 column tiles
+    # makes 4 or 6 parts per tile leave CUs idle or spill into a second wave)
     n1, n2 = (H + 63) // 64, (I + 63) // 64
-    s1s = [s for s in (1, 2, 3, 4, 6) if s == 1 or n1 // s >= MIN_SLABS]
-    s2s = [s for s in (1, 2, 3, 4) if s == 1 or n2 // s >= MIN_SLABS]
+    s1s = [s for s in (1, 2, 3, 4, 5, 6, 7, 8) if s == 1 or n1 // s >= MIN_SLABS]
+    s2s = [s for s in (1, 2, 3, 4, 5) if s == 1 or n2 // s >= MIN_SLABS]
     return [(a, b) for a in s1s for b in s2s]
 
 
@@ -113,7 +116,18 @@ def tune_shape(dev, w, M, stream, flush_buf, cus):
         cold = time_plan(dev, w, M, "tile_sync", c, s, max(4, reps), stream, flush)
         score[s] = (hot + cold) / 2
     split = min(top, key=lambda s: score[s])
-    pick = {pol: min(cfgs, key=lambda c: times[(split, pol, c)]) for pol in POLICIES}
+    # each policy's configuration under that split: the candidates re-timed in
+    # alternating rounds (the clock drifts with power and temperature, so
+    # timings taken one after another favour whichever ran first)
+    pick = {}
+    for pol in POLICIES:
+        rounds = {c: [] for c in cfgs}
+        for _ in range(3):
+            for c in cfgs:
+                rounds[c].append(time_plan(dev, w, M, pol, c, split, reps, stream))
+        for c in cfgs:
+            times[(split, pol, c)] = float(np.median(rounds[c]))
+        pick[pol] = min(cfgs, key=lambda c: times[(split, pol, c)])
     best_so = min((times[(s, "stream_ordered", c)], s, c) for s in splits for c in cfgs)
     entry = (M, w.H, w.I, {"none": 0, "gelu_tanh": 1, "swiglu": 2}[w.act], cus, split[0], split[1],
              pick["stream_ordered"], pick["row_sync"], pick["tile_sync"])

@@ -129,7 +129,9 @@ def test_fused_split_plan_is_shared_by_every_policy():
             assert (info["S1"], info["S2"]) == (2, 1), (M, pol, info)
         fused = plans["tile_sync"]
         assert fused["BM"] == 256 and 128 < fused["T1"] <= 256, fused
-        assert plans["row_sync"]["config"] == fused["config"]
+        # the fused policies use the same tile shape (configurations 7 and 8
+        # differ only in their LDS ring)
+        assert (plans["row_sync"]["BM"], plans["row_sync"]["BN1"]) == (fused["BM"], fused["BN1"])
     # the LLaMA-65 shard (64-slab halves) keeps the unsplit plan at M = 2048
     with mc.MlpChain(2048, 8192, 2752, "swiglu", "f16", "tile_sync") as ch:
         assert ch.info()["S1"] == 1
