@@ -74,7 +74,8 @@ def test_sweep_summary_of_every_workload_stays_small():
                 rows.append({"workload": w.name, "M": M, "policy": pol, "us": 1234.5678, "us_cold": 1234.5678,
                              "stream_ordered_best": {"us": 1234.5678, "us_cold": 1234.5678},
                              "speedup_vs_stream_ordered_best": 1.02345, "speedup_vs_stream_ordered_best_cold": 1.02345,
-                             "speedup_vs_stream_ordered": 1.02345, "roofline_frac_cold": 0.43219, "bound": "mfma"})
+                             "speedup_vs_stream_ordered": 1.02345, "roofline_frac_cold": 0.43219,
+                             "roofline_frac_cold_written": 0.43219, "bound": "mfma"})
     s = bench.sweep_summary(rows)
     assert len(s) == sum(len(gen.WORKLOADS[wl].Ms) for wl in (1, 2, 3, 4))
     assert all(len(r) == len(bench.SUMMARY_COLUMNS) for r in s)
