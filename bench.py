@@ -442,16 +442,17 @@ def roofline_entry(w, M, policy, info, kern_us):
     return roof
 
 
-def graph_replay_time(runner, M, plan, steps, warmup, stream):
-    """Wall time of `steps` replays of the stream-ordered pair of `plan`
-    (config, S1, S2) captured as a HIP graph: the same two kernels without
-    host launch gaps (the stream-ordered launches depend on nothing the host
-    changes per run)."""
+def graph_replay_time(runner, M, plan, steps, warmup, stream, policy="stream_ordered"):
+    """Wall time of `steps` replays of one run of `policy` (the stream-ordered
+    pair, or a fused run), with the plan (config, S1, S2) or the planned one
+    (plan None), captured as a HIP graph: the same kernels without host
+    launch gaps (no launch depends on anything the host changes per run)."""
     import torch
     x, w1, w2, out = runner.args(M)
-    with runner.chain(M, "stream_ordered") as sg:
-        sg.set_config(plan[0])
-        sg.set_split(plan[1], plan[2])
+    with runner.chain(M, policy) as sg:
+        if plan is not None:
+            sg.set_config(plan[0])
+            sg.set_split(plan[1], plan[2])
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
@@ -608,6 +609,10 @@ def main():
                                         "plan": [bcfg, bs1, bs2],
                                         "note": "fastest pair captured as a HIP graph and replayed"}
         line["speedup_vs_stream_ordered_graph"] = round(value / sgraph_tflops, 4)
+        wall_pgraph = graph_replay_time(runner, M, None, args.steps, args.warmup, stream, args.policy)
+        line["policy_graph"] = {"value": round(F / (wall_pgraph / args.steps) / 1e12, 2),
+                                "ms_per_step": round(wall_pgraph / args.steps * 1e3, 4),
+                                "note": f"{args.policy} captured as a HIP graph and replayed"}
 
     rows = []
     flush_buf = torch.zeros(512 << 20, dtype=torch.uint8, device="cuda") if sweep_Ms else None
@@ -639,10 +644,8 @@ def main():
     if rows:
         line["sweep_columns"] = list(SUMMARY_COLUMNS)
         line["sweep"] = sweep_summary(rows)
-        line["sweep_note"] = ("tile_sync per workload and M: event medians hot / cold (512 MB read between "
-                              "runs); roofline_frac_cold_written: cold after 512 MB written between runs; best "
-                              "pair = fastest stream-ordered plan over configs x splits; full rows of all "
-                              "policies on stderr")
+        line["sweep_note"] = ("tile_sync event medians hot / cold (512 MB read between runs; _written: 512 MB "
+                              "written); best pair: fastest stream-ordered plan; all rows on stderr")
     if args.sweep_out:
         with open(args.sweep_out, "w") as fh:
             json.dump(rows, fh, indent=1)

@@ -4,6 +4,10 @@
 // Per-run synchronization state lives in the workspace and is never cleared
 // from the host between runs (no memset on the run path, so a run is a
 // single kernel for the fused policies):
+//   * a fused run's epoch is kept on the device: a 64-bit word counts
+//     finished runs in its high half (each run's workgroups add 2^32 in
+//     total as they finish), and a run's epoch is one more than the count
+//     it reads at launch, so no launch argument changes between runs;
 //   * two sets of 8 tile-queue counters alternate by epoch parity: a run
 //     uses one (zero when it starts) and its workgroup 0 zeroes the other,
 //     which the next run takes;
@@ -12,9 +16,10 @@
 //   * row counters grow by N1t per run; a consumer of run e waits for
 //     (int32)(count - e * N1t) >= 0;
 //   * split-K arrival counters are set back to zero by the last part of
-//     each tile, so the stream-ordered launches depend on nothing the host
-//     changes between runs (they can be captured in a HIP graph).
-// The epoch arithmetic is modular 32-bit, so wrap-around is harmless.
+//     each tile.
+// So every policy's launches depend on nothing the host changes between
+// runs, and may be captured in a HIP graph and replayed.  The epoch
+// arithmetic is modular 32-bit, so wrap-around is harmless.
 #include <hip/hip_runtime.h>
 
 #include <stdarg.h>
@@ -86,10 +91,10 @@ struct mlp_chain {
     uint32_t* ticket;
     uint32_t* status;
     uint16_t* zero;
+    uint64_t* run_epoch;        // high half: the last finished fused run's epoch
     float* part1;
     float* part2;
     // run state
-    uint32_t epoch;             // fused runs
     uint32_t spin_limit;
     uint32_t skip_producer;
     uint64_t* trace;            // caller's timeline buffer (debug), or nullptr
@@ -407,7 +412,6 @@ int zero_workspace(mlp_chain* h) {
     if (e != hipSuccess) return fail(MLP_EHIP, "hipMemset failed: %s", hipGetErrorString(e));
     e = hipDeviceSynchronize();
     if (e != hipSuccess) return fail(MLP_EHIP, "hipDeviceSynchronize failed: %s", hipGetErrorString(e));
-    h->epoch = 0;
     return MLP_OK;
 }
 
@@ -441,7 +445,7 @@ void layout_workspace(mlp_chain* h, char* base) {
     const size_t p2_b = h->S2 > 1 ? align_up(L * h->T2 * h->S2 * acc_bytes, 256) : 0;
     const size_t y1_b = align_up(L * h->T1 * h->S1 * 4, 256);
     const size_t y2_b = align_up(L * h->T2 * h->S2 * 4, 256);
-    h->sync_bytes = f_b + r_b + c1_b + c2_b + y1_b + y2_b + TICKET_BYTES + 2 * 256;
+    h->sync_bytes = f_b + r_b + c1_b + c2_b + y1_b + y2_b + TICKET_BYTES + 3 * 256;
     h->ws_bytes = t_b + ys_b + h->sync_bytes + p1_b + p2_b;
     if (!base) return;
     char* p = base;
@@ -464,7 +468,8 @@ void layout_workspace(mlp_chain* h, char* base) {
     h->ticket = reinterpret_cast<uint32_t*>(p);            // 2 sets of 8 queue counters, 256 B apart
     h->status = reinterpret_cast<uint32_t*>(p + TICKET_BYTES);
     h->zero = reinterpret_cast<uint16_t*>(p + TICKET_BYTES + 256);
-    p += TICKET_BYTES + 2 * 256;
+    h->run_epoch = reinterpret_cast<uint64_t*>(p + TICKET_BYTES + 2 * 256);
+    p += TICKET_BYTES + 3 * 256;
     h->part1 = p1_b ? reinterpret_cast<float*>(p) : nullptr;
     p += p1_b;
     h->part2 = p2_b ? reinterpret_cast<float*>(p) : nullptr;
@@ -510,8 +515,8 @@ mlpc::ChainArgs make_args(const mlp_chain* h, const void* x, const void* w1, con
     a.T2 = h->T2;
     a.rx = h->forced_rx > 0 ? (uint32_t)h->forced_rx : h->Mt >= 2 ? 2u : 1u;
     a.order = h->order;
-    a.ticket = h->ticket + 512 * (h->epoch & 1u);
-    a.ticket_next = h->ticket + 512 * ((h->epoch & 1u) ^ 1u);
+    a.ticket = h->ticket;
+    a.run_epoch = h->run_epoch;
     a.flags = h->flags;
     a.fstride = flag_stride(h);
     a.rowcnt = h->rowcnt;
@@ -527,7 +532,6 @@ mlpc::ChainArgs make_args(const mlp_chain* h, const void* x, const void* w1, con
     a.cnt2 = h->cnt2;
     a.rdy1 = h->rdy1;
     a.rdy2 = h->rdy2;
-    a.epoch = h->epoch;
     a.grid = h->grid;
     a.spin_limit = h->spin_limit;
     a.skip_producer = h->skip_producer;
@@ -671,7 +675,6 @@ int mlp_chain_run_layers(mlp_chain_t h, const void* x, const void* const* w1, co
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     h->last_stream = s;
     const bool fused = h->policy != MLP_POLICY_STREAM_ORDERED;
-    if (fused) h->epoch += 1u;
     mlpc::ChainArgs a = make_args(h, x, w1[0], w2[0], out);
     for (uint32_t l = 0; l < h->layers; ++l) {
         a.w1s[l] = static_cast<const uint16_t*>(w1[l]);
@@ -687,9 +690,7 @@ int mlp_chain_run_layers(mlp_chain_t h, const void* x, const void* const* w1, co
         }
         return MLP_OK;
     }
-    int rc = launch_phase(h, h->policy == MLP_POLICY_ROW_SYNC ? LAUNCH_LAYERS_ROW : LAUNCH_LAYERS_TILE, a, s);
-    if (rc != MLP_OK) h->epoch -= 1u;
-    return rc;
+    return launch_phase(h, h->policy == MLP_POLICY_ROW_SYNC ? LAUNCH_LAYERS_ROW : LAUNCH_LAYERS_TILE, a, s);
 }
 
 int mlp_chain_run(mlp_chain_t h, const void* x, const void* w1, const void* w2, void* out, void* hip_stream) {
@@ -708,14 +709,11 @@ int mlp_chain_run(mlp_chain_t h, const void* x, const void* w1, const void* w2, 
         if (rc == MLP_OK) rc = launch_phase(h, LAUNCH_GEMM2, a, s);
         return rc;   // (a failed launch leaves the device unusable; counters need not roll back)
     }
-    h->epoch += 1u;
+    // the run's epoch is the device's (one more than the last finished
+    // run's), so nothing here changes between runs and the launch may be
+    // captured into a graph
     const mlpc::ChainArgs a = make_args(h, x, w1, w2, out);
-    int rc = launch_phase(h, h->policy == MLP_POLICY_ROW_SYNC ? LAUNCH_ROW : LAUNCH_TILE, a, s);
-    if (rc != MLP_OK) {
-        h->epoch -= 1u;
-        return rc;
-    }
-    return MLP_OK;
+    return launch_phase(h, h->policy == MLP_POLICY_ROW_SYNC ? LAUNCH_ROW : LAUNCH_TILE, a, s);
 }
 
 int mlp_chain_run_noalloc(int64_t M, int64_t H, int64_t I, int act, int dtype, int policy, const void* x,
@@ -747,11 +745,10 @@ int mlp_chain_run_noalloc(int64_t M, int64_t H, int64_t I, int act, int dtype, i
     if (status) h.status = static_cast<uint32_t*>(status);
     hipStream_t s = static_cast<hipStream_t>(hip_stream);
     // Every call starts from zeroed synchronization words (flags, counters,
-    // ready words, queue counters, status, zero page) and epoch 1, whatever
-    // an earlier call on this device left there.
+    // ready words, queue counters, status, zero page, epoch words: the run
+    // is epoch 1), whatever an earlier call on this device left there.
     e = mlpc_zero_words(h.flags, h.sync_bytes, h.status, s);
     if (e != hipSuccess) return fail(MLP_EHIP, "clearing the scratch failed: %s", hipGetErrorString(e));
-    h.epoch = 1u;
     const mlpc::ChainArgs a = make_args(&h, x, w1, w2, out);
     if (policy == MLP_POLICY_STREAM_ORDERED) {
         int r = launch_phase(&h, LAUNCH_GEMM1, a, s);
@@ -796,9 +793,17 @@ int mlp_chain_status(mlp_chain_t h) {
 
 int mlp_chain_info(mlp_chain_t h, int64_t* info, int n) {
     if (!h || !info || n < 16) return fail(MLP_EINVAL, "mlp_chain_info needs a handle and 16 slots");
+    // the epoch of the last finished fused run, read on the stream of the
+    // handle's last run, after it
+    DeviceGuard g(h->device);
+    uint64_t word = 0;
+    hipError_t e = hipMemcpyAsync(&word, h->run_epoch, sizeof word, hipMemcpyDeviceToHost, h->last_stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(h->last_stream);
+    if (e != hipSuccess) return fail(MLP_EHIP, "reading the epoch failed: %s", hipGetErrorString(e));
+    const uint32_t epoch = (uint32_t)(word >> 32);
     const int64_t bn1 = h->act == MLP_ACT_SWIGLU ? h->ci.BN / 2 : h->ci.BN;
     const int64_t v[21] = {h->ci.BM, bn1, h->ci.BN, h->ci.BK, h->Mt, h->N1t, h->N2t, h->T1, h->T2,
-                           h->grid, h->occ, h->ci.NT, h->cus, h->epoch, h->cfg, (int64_t)h->ws_bytes,
+                           h->grid, h->occ, h->ci.NT, h->cus, epoch, h->cfg, (int64_t)h->ws_bytes,
                            h->S1, h->S2, h->ksp1, h->ksp2, h->layers};
     for (int i = 0; i < n && i < 21; ++i) info[i] = v[i];
     return MLP_OK;
@@ -902,9 +907,12 @@ int mlp_chain_debug_set_epoch(mlp_chain_t h, uint32_t epoch) {
     if (e == hipSuccess) e = hipMemsetD32(h->flags, (int)epoch, 8 * (size_t)flag_stride(h));
     if (e == hipSuccess) e = hipMemsetD32(h->rowcnt, (int)(epoch * h->N1t), L * h->Mt);
     if (e == hipSuccess && L > 1) e = hipMemsetD32(h->rowcnt + L * h->Mt, (int)(epoch * h->N2t), (L - 1) * h->Mt);
+    // both sets of queue counters zero, the run count `epoch`
+    const uint64_t word = (uint64_t)epoch << 32;
+    if (e == hipSuccess) e = hipMemset(h->ticket, 0, TICKET_BYTES);
+    if (e == hipSuccess) e = hipMemcpy(h->run_epoch, &word, sizeof word, hipMemcpyHostToDevice);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) return fail(MLP_EHIP, "setting the epoch failed: %s", hipGetErrorString(e));
-    h->epoch = epoch;
     return MLP_OK;
 }
 

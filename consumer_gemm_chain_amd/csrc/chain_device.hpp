@@ -76,9 +76,11 @@ struct ChainArgs {
     uint32_t Mt, N1t, N2t, T1, T2;
     uint32_t rx;            // XCD grid rows (1, 2, 4 or 8; the grid is rx x 8/rx)
     uint32_t order;         // bit 0 / bit 1: GEMM1 / GEMM2 tiles walked column-major in each XCD block
-    uint32_t* ticket;       // this run's 8 tile-queue counters (one per XCD), 64 words apart; zero when
-                            // the run starts
-    uint32_t* ticket_next;  // the other set of 8 (used by the next run): workgroup 0 zeroes it
+    uint32_t* ticket;       // two sets of 8 tile-queue counters (one per XCD, 64 words apart), 512
+                            // words apart: a fused run of epoch e uses set e & 1 (zero when it
+                            // starts) and its workgroup 0 zeroes the other set
+    uint64_t* run_epoch;    // fused runs: finished runs in the high 32 bits (the last finished run's
+                            // epoch); the low half returns to its value at the end of each run
     uint32_t* flags;        // [8][fstride] ready epochs (tile_sync): one copy per XCD, each [Mt * N1t]
     uint32_t fstride;       // words between the XCDs' copies of the flags
     uint32_t* rowcnt;       // [Mt] producer completions (row_sync)
@@ -97,7 +99,6 @@ struct ChainArgs {
     uint32_t* rdy1;         // [T1 * S1] part published (S1 > 1), zero between executions
     uint32_t* rdy2;         // [T2 * S2] part published (S2 > 1), zero between executions
     uint64_t* trace;        // optional timeline: 4 words per ticket (nullptr = off)
-    uint32_t epoch;         // this run's epoch (mod 2^32)
     uint32_t grid;          // persistent workgroups
     uint32_t spin_limit;    // back-off iterations before a consumer gives up
     uint32_t skip_producer; // test hook: producer ticket that does nothing (NO_SKIP = none)
@@ -1500,6 +1501,9 @@ __device__ __forceinline__ bool run_tile(const ChainArgs& a, uint32_t mb, uint32
     const uint32_t tile = (ROLE == 1 ? l * a.T1 + mb * a.N1t : l * a.T2 + mb * a.N2t) + nb;
     const TileJob j = ROLE == 1 ? producer_job<C>(a, mb, nb, s, l) : consumer_job<C>(a, mb, nb, s, l);
     tile_mainloop<C, DT>(j, acc, wait);
+    // timeline: a GEMM1 part's second word is the end of its K loop
+    if (ROLE == 1 && l == 0 && a.trace && thread_index() == 0)
+        a.trace[4 * (size_t)((mb * a.N1t + nb) * a.S1 + s) + 1] = __builtin_amdgcn_s_memrealtime();
     const uint32_t S = ROLE == 1 ? a.S1 : a.S2;
     if (S > 1) {
         const bool last = ROLE == 1 ? split_reduce<C>(acc, a.part1, a.cnt1, a.rdy1, tile, s, S, s_flag, a.status, a.spin_limit)

@@ -91,10 +91,11 @@ mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype
  * fails.  A consumer tile that waits longer than the spin limit for its
  * producer gives up and records MLP_ETIMEOUT in the handle's status word
  * (see mlp_chain_status); its output is then undefined.
- * A stream-ordered handle's launches depend on nothing the host changes
- * between runs, so they may be captured into a HIP graph and replayed (the
- * same pointers each replay).  The fused policies' launches carry a new
- * epoch for their ready flags each run and must not be captured.
+ * A run's launches depend on nothing the host changes between runs (the
+ * fused policies keep the epoch of their ready flags on the device), so
+ * they may be captured into a HIP graph and replayed, every policy (the
+ * same pointers each replay; replays and direct runs of one handle on one
+ * stream may be mixed).
  * (CuSync README, opening and MLP paragraphs.) */
 int mlp_chain_run(mlp_chain_t h, const void* x, const void* w1, const void* w2, void* out,
                   void* hip_stream);
@@ -192,8 +193,11 @@ const char* mlp_chain_last_error(void);
  *     workgroups per CU, threads per workgroup, CUs, epoch,
  *     config id, workspace bytes, S1, S2, K slabs per GEMM1 part,
  *     K slabs per GEMM2 part, layers }.
- * (S1, S2: the deterministic K split of GEMM1 / GEMM2 tiles, 1 = none.)
- * Returns MLP_EINVAL for a NULL handle or array, or n < 16. */
+ * (S1, S2: the deterministic K split of GEMM1 / GEMM2 tiles, 1 = none;
+ * epoch: that of the last finished fused run, read from the device after
+ * waiting for the stream of the handle's last run.)
+ * Returns MLP_EINVAL for a NULL handle or array, or n < 16, MLP_EHIP if
+ * reading the epoch fails. */
 int mlp_chain_info(mlp_chain_t h, int64_t* info, int n);
 
 /* The plan mlp_chain_create would make for these sizes on a GPU with `cus`
@@ -270,8 +274,9 @@ int mlp_chain_debug_set_order(mlp_chain_t h, int order);
 
 /* Test hook: put the handle's synchronization state where the fused run of
  * epoch `epoch` leaves it (every ready flag holding `epoch`, every row
- * counter at epoch x tiles per row block, modulo 2^32), so that the next
- * runs use epochs epoch+1, epoch+2, ... -- e.g. across the 32-bit wrap.
+ * counter at epoch x tiles per row block, modulo 2^32, both sets of queue
+ * counters zero, the device's epoch word `epoch`), so that the next runs
+ * use epochs epoch+1, epoch+2, ... -- e.g. across the 32-bit wrap.
  * Synchronizes the device.  Returns MLP_EINVAL for a NULL handle, MLP_EHIP
  * if the device reports an error. */
 int mlp_chain_debug_set_epoch(mlp_chain_t h, uint32_t epoch);

@@ -32,7 +32,8 @@ def test_bench_driver_shape_with_one_point_sweep():
     d = json.loads(lines[0])
     for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
               "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "cpu_baseline",
-              "stream_ordered", "stream_ordered_best", "stream_ordered_graph", "sweep", "sweep_columns"):
+              "stream_ordered", "stream_ordered_best", "stream_ordered_graph", "policy_graph", "sweep",
+              "sweep_columns"):
         assert k in d, k
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1 and d["unit"] == "TFLOP/s"
     assert d["value"] > 0 and d["ms_per_step"] > 0 and d["higher_is_better"] is True
@@ -45,6 +46,7 @@ def test_bench_driver_shape_with_one_point_sweep():
     assert cpu["cpu_model"] and cpu["nproc"] >= 1
     for k in ("stream_ordered", "stream_ordered_best", "stream_ordered_graph"):
         assert d[k]["value"] > 0 and d[k]["plan"][1] >= 1
+    assert d["policy_graph"]["value"] > 0 and d["policy_graph"]["ms_per_step"] > 0
     assert len(d["sweep"]) == 1 and len(d["sweep"][0]) == len(d["sweep_columns"])
     rows = [json.loads(l) for l in err.splitlines() if l.startswith("{")]
     assert sorted(r["policy"] for r in rows) == ["row_sync", "stream_ordered", "tile_sync"]
