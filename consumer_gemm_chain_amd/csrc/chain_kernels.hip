@@ -144,7 +144,7 @@ struct Queues {
     uint32_t own;
     uint32_t dry;          // bit v: queue (own + v) & 7 is known to be empty (wave-uniform)
     uint32_t P1;
-    uint32_t* ticket;      // this run's set of 8 queue counters (set before each draw)
+    uint32_t* ticket;      // this run's set of 8 queue counters
 };
 
 __device__ __forceinline__ uint32_t queue_item(const ChainArgs& a, const XcdBlock& bp, const XcdBlock& bc,
@@ -228,38 +228,14 @@ __device__ __forceinline__ void publish_flag(const ChainArgs& a, uint32_t idx, u
 // to this one word is needed (each workgroup's read comes before its own add;
 // the next run is ordered after this one by its stream).  The count wraps at
 // 2^32 runs like every other epoch comparison.
-//
-// The read is issued at launch and waited for only where an item first
-// needs the value -- a consumer's wait, a producer's publication, the next
-// draw -- so it never holds up the first item's K loop.  The empty asm at
-// each use keeps the compiler from moving the wait (and the readfirstlane)
-// up to the launch.
-// Only the high half is read (a 32-bit read of it: the 64-bit adds are
-// atomic, so it sees each of them whole or not at all), so that the load has
-// a single destination register, which stays reserved until the first use
-// instead of being waited for when the compiler reuses its other half.
-struct Epoch {
-    uint32_t raw;   // finished runs, as read at launch (in flight until first used)
-    __device__ __forceinline__ uint32_t get() const {
-        uint32_t v = raw;
-        asm volatile("" : "+v"(v));
-        return __builtin_amdgcn_readfirstlane(v) + 1u;
-    }
-};
-
-__device__ __forceinline__ Epoch run_epoch(const ChainArgs& a) {
-    const uint32_t* hi = reinterpret_cast<const uint32_t*>(a.run_epoch) + 1;   // little-endian high half
-    return Epoch{__hip_atomic_load(hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)};
+__device__ __forceinline__ uint32_t run_epoch(const ChainArgs& a) {
+    const uint64_t w = __hip_atomic_load(a.run_epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_amdgcn_readfirstlane((uint32_t)(w >> 32)) + 1u;
 }
 
-// After a workgroup's last item: workgroup 0 zeroes the set of queue
-// counters this run did not use (the next run's; nothing of this run reads
-// it), and thread 0 of every workgroup adds its share to the run counter (no
-// result is needed).
-__device__ __forceinline__ void run_finished(const ChainArgs& a, const Epoch& ep) {
-    if (blockIdx.x == 0 && threadIdx.x < 8)
-        __hip_atomic_store(a.ticket + 512 * ((ep.get() & 1u) ^ 1u) + 64 * threadIdx.x, 0u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+// Thread 0 of each workgroup, after its last item: its share of the run
+// counter (no result is needed).
+__device__ __forceinline__ void run_finished(const ChainArgs& a) {
     if (threadIdx.x == 0) {
         const uint64_t add = blockIdx.x == 0 ? (1ull << 32) - gridDim.x + 1u : 1ull;
         (void)__hip_atomic_fetch_add(a.run_epoch, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -282,8 +258,7 @@ __device__ __forceinline__ void run_finished(const ChainArgs& a, const Epoch& ep
 constexpr uint32_t EARLY_THREAD = 64;
 
 struct EarlyDraw {
-    uint32_t* tickets;  // both sets of queue counters
-    const Epoch& ep;    // the run's epoch: its parity picks the set
+    uint32_t* ticket;   // this run's set of queue counters
     uint32_t own;
     bool& issued;       // uniform: an early draw was started for the current item
     uint32_t& pos;      // thread EARLY_THREAD: the position the atomic returned
@@ -293,8 +268,7 @@ struct EarlyDraw {
         // atomic add the compiler does not rewrite it into a wave-wide add
         // whose result it waits for at once)
         if (threadIdx.x == EARLY_THREAD)
-            pos = __builtin_amdgcn_atomic_inc32(tickets + 512 * (ep.get() & 1u) + 64 * own, 0xffffffffu,
-                                                __ATOMIC_RELAXED, "agent");
+            pos = __builtin_amdgcn_atomic_inc32(ticket + 64 * own, 0xffffffffu, __ATOMIC_RELAXED, "agent");
     }
 };
 
@@ -321,9 +295,12 @@ void chain_persistent_kernel(ChainArgs a) {
     __shared__ uint32_t s_pos;
     const uint32_t P1 = a.T1 * a.S1;
     const int bn1 = a.act == ACT_SWIGLU ? C::BN / 2 : C::BN;
-    const Epoch ep = run_epoch(a);
-    Queues q{blockIdx.x & 7u, 0u, P1, nullptr};
+    const uint32_t epoch = run_epoch(a);
+    Queues q{blockIdx.x & 7u, 0u, P1, a.ticket + 512 * (epoch & 1u)};
     uint32_t item = NO_ITEM;
+    if (blockIdx.x == 0 && threadIdx.x < 8)
+        __hip_atomic_store(a.ticket + 512 * ((epoch & 1u) ^ 1u) + 64 * threadIdx.x, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     {
         // the launch-time item: position blockIdx / 8 of the own queue
         const XcdBlock bp = xcd_block(a.Mt, a.N1t, a.S1, a.rx, q.own);
@@ -334,13 +311,12 @@ void chain_persistent_kernel(ChainArgs a) {
     bool issued = false;
     uint32_t pos = 0;
     static_assert(C::NT > EARLY_THREAD, "the early draw is wave 1's");
-    const EarlyDraw early{a.ticket, ep, q.own, issued, pos};
+    const EarlyDraw early{q.ticket, q.own, issued, pos};
     for (;;) {
         if (item == NO_ITEM) {
             // the next item (wave 0): the early draw's, else from the own
             // queue or the next ones
             if ((threadIdx.x >> 6) == 0) {
-                q.ticket = a.ticket + 512 * (ep.get() & 1u);
                 uint32_t it = issued ? resolve_early<false>(a, q, s_pos) : NO_ITEM;
                 if (it == NO_ITEM) it = draw_item(a, q);
                 if (threadIdx.x == 0) s_ticket = it;
@@ -369,7 +345,7 @@ void chain_persistent_kernel(ChainArgs a) {
             const uint32_t first = prod ? 0u : (part * a.ksp2 * BK) / (uint32_t)bn1;
             const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
             ChainWait<POL> w{!prod, a.flags + q.own * a.fstride + mb * a.N1t, a.rowcnt + mb, a.N1t,
-                             prod ? 0u : POL == POL_ROW ? ep.get() * a.N1t : ep.get(), bn1, a.status, a.spin_limit,
+                             prod ? 0u : POL == POL_ROW ? epoch * a.N1t : epoch, bn1, a.status, a.spin_limit,
                              a.acq_agent, &s_ready, first, false, t_start};
             bool wrote;
             if (prod) {
@@ -380,13 +356,13 @@ void chain_persistent_kernel(ChainArgs a) {
             }
             if (a.trace && threadIdx.x == 0) trace_item(a, t, t_start, prod ? ~0ull : w.t_waited, wrote);
             if (prod && wrote) {
-                chaos_delay(t ^ (ep.get() << 20));
+                chaos_delay(t ^ (epoch << 20));
                 // every thread's T stores happen before thread 0's agent-scope
                 // release (workgroup release + barrier), which publishes the tile
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
                 __syncthreads();
                 if constexpr (POL == POL_TILE) {
-                    if ((threadIdx.x >> 6) == 0) publish_flag(a, mb * a.N1t + nb, ep.get());
+                    if ((threadIdx.x >> 6) == 0) publish_flag(a, mb * a.N1t + nb, epoch);
                 } else if (threadIdx.x == 0) {
                     __hip_atomic_fetch_add(a.rowcnt + mb, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
                 }
@@ -400,7 +376,7 @@ void chain_persistent_kernel(ChainArgs a) {
         // thread 0 waits to draw the next one, which never ends.
         __syncthreads();
     }
-    run_finished(a, ep);
+    run_finished(a);
 }
 
 // Persistent kernel of a chain of a.layers MLP layers, 2 * layers dependent
@@ -429,9 +405,12 @@ void chain_layers_kernel(ChainArgs a) {
     const uint32_t P1 = a.T1 * a.S1;
     const uint32_t P = P1 + a.T2 * a.S2;      // items per layer
     const int bn1 = a.act == ACT_SWIGLU ? C::BN / 2 : C::BN;
-    const Epoch ep = run_epoch(a);
-    Queues q{blockIdx.x & 7u, 0u, P1, nullptr};
+    const uint32_t epoch = run_epoch(a);
+    Queues q{blockIdx.x & 7u, 0u, P1, a.ticket + 512 * (epoch & 1u)};
     uint32_t item = NO_ITEM;
+    if (blockIdx.x == 0 && threadIdx.x < 8)
+        __hip_atomic_store(a.ticket + 512 * ((epoch & 1u) ^ 1u) + 64 * threadIdx.x, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     {
         const XcdBlock bp = xcd_block(a.Mt, a.N1t, a.S1, a.rx, q.own);
         const XcdBlock bc = xcd_block(a.Mt, a.N2t, a.S2, a.rx, q.own);
@@ -441,11 +420,10 @@ void chain_layers_kernel(ChainArgs a) {
     bool issued = false;
     uint32_t pos = 0;
     static_assert(C::NT > EARLY_THREAD, "the early draw is wave 1's");
-    const EarlyDraw early{a.ticket, ep, q.own, issued, pos};
+    const EarlyDraw early{q.ticket, q.own, issued, pos};
     for (;;) {
         if (item == NO_ITEM) {
             if ((threadIdx.x >> 6) == 0) {
-                q.ticket = a.ticket + 512 * (ep.get() & 1u);
                 uint32_t it = issued ? resolve_early<true>(a, q, s_pos) : NO_ITEM;
                 if (it == NO_ITEM) it = draw_item<true>(a, q);
                 if (threadIdx.x == 0) s_ticket = it;
@@ -478,14 +456,14 @@ void chain_layers_kernel(ChainArgs a) {
                 const uint32_t* fy = a.flags + q.own * a.fstride + a.layers * a.T1 + lp * a.T2;
                 const uint32_t* cy = a.rowcnt + (a.layers + lp) * a.Mt;
                 ChainWait<POL> w{l > 0, fy + mb * a.N2t, cy + mb, a.N2t,
-                                 l == 0 ? 0u : POL == POL_ROW ? ep.get() * a.N2t : ep.get(), C::BN, a.status,
+                                 l == 0 ? 0u : POL == POL_ROW ? epoch * a.N2t : epoch, C::BN, a.status,
                                  a.spin_limit,
                                  0u, &s_ready, (part * a.ksp1 * BK) / (uint32_t)C::BN, false, t_start};
                 wrote = run_tile<C, DT, 1>(a, mb, nb, part, &s_flag, w, l, early);
                 t_waited = w.t_waited;
             } else {
                 ChainWait<POL> w{true, a.flags + q.own * a.fstride + l * a.T1 + mb * a.N1t, a.rowcnt + l * a.Mt + mb, a.N1t,
-                                 POL == POL_ROW ? ep.get() * a.N1t : ep.get(), bn1, a.status, a.spin_limit,
+                                 POL == POL_ROW ? epoch * a.N1t : epoch, bn1, a.status, a.spin_limit,
                                  a.acq_agent, &s_ready, (part * a.ksp2 * BK) / (uint32_t)bn1, false, t_start};
                 wrote = run_tile<C, DT, 2>(a, mb, nb, part, &s_flag, w, l, early);
                 t_waited = w.t_waited;
@@ -493,13 +471,13 @@ void chain_layers_kernel(ChainArgs a) {
             if (a.trace && threadIdx.x == 0) trace_item(a, t, t_start, t_waited, wrote);
             if (wrote && (prod || l + 1 < a.layers)) {
                 // publish the tile of T_l (GEMM1) or Y_l (GEMM2 of a layer that is not the last)
-                chaos_delay(t ^ (ep.get() << 20));
+                chaos_delay(t ^ (epoch << 20));
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
                 __syncthreads();
                 if constexpr (POL == POL_TILE) {
                     if ((threadIdx.x >> 6) == 0)
                         publish_flag(a, prod ? l * a.T1 + mb * a.N1t + nb : a.layers * a.T1 + l * a.T2 + mb * a.N2t + nb,
-                                     ep.get());
+                                     epoch);
                 } else if (threadIdx.x == 0) {
                     uint32_t* c = prod ? a.rowcnt + l * a.Mt + mb : a.rowcnt + (a.layers + l) * a.Mt + mb;
                     __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
@@ -511,7 +489,7 @@ void chain_layers_kernel(ChainArgs a) {
         // the thread-0 ticket draw at the top of the loop)
         __syncthreads();
     }
-    run_finished(a, ep);
+    run_finished(a);
 }
 
 // ------------------------------------------------------------------ host side
