@@ -100,29 +100,43 @@ def measured_traffic(kernel: str, workload: str, M: int, plan: str):
     return int(float(fields["traffic_bytes_per_launch"]))
 
 
-class Runner:
-    """Device inputs for one workload at its largest M; runs slice X rows."""
+def weight_strides(w, dense: bool):
+    """Row strides (elements) of the workload's device weights: the
+    library's preferred padded strides (rows an odd number of 128-byte
+    lines apart), or dense rows."""
+    from consumer_gemm_chain_amd import mlp_chain as mc
+    g = 2 if w.act == "swiglu" else 1
+    return (g * w.I, w.H) if dense else mc.mlp_chain_weight_ld(w.H, w.I, mc.ACTS[w.act])
 
-    def __init__(self, w, max_M):
+
+class Runner:
+    """Device inputs for one workload at its largest M; runs slice X rows.
+    The weights live in rows `ld` apart (weight_strides), and every chain
+    made here is told so."""
+
+    def __init__(self, w, max_M, dense_weights=False):
         import torch
         from consumer_gemm_chain_amd import gen
-        from consumer_gemm_chain_amd.tensors import to_dev
+        from consumer_gemm_chain_amd.tensors import to_dev, to_dev_rows
         self.w = w
         t0 = time.time()
         w1, w2 = gen.weights(w)
         x = gen.x_rows(w, max_M, max_M=max(max_M, w.max_M))
         self.host = (x, w1, w2)
+        self.ld = weight_strides(w, dense_weights)
         self.x = to_dev(x, w.dtype)
-        self.w1 = to_dev(w1, w.dtype)
-        self.w2 = to_dev(w2, w.dtype)
+        self.w1 = to_dev_rows(w1, w.dtype, self.ld[0])
+        self.w2 = to_dev_rows(w2, w.dtype, self.ld[1])
         dt = self.x.dtype
         self.out = torch.empty((max_M, w.H), dtype=dt, device="cuda")
         torch.cuda.synchronize()
         log(f"inputs for {w.name} (M<={max_M}) ready in {time.time() - t0:.1f}s")
 
-    def chain(self, M, policy):
+    def chain(self, M, policy, layers=1):
         from consumer_gemm_chain_amd.mlp_chain import MlpChain
-        return MlpChain(M, self.w.H, self.w.I, self.w.act, self.w.dtype, policy)
+        ch = MlpChain(M, self.w.H, self.w.I, self.w.act, self.w.dtype, policy, layers=layers)
+        ch.set_weight_ld(*self.ld)
+        return ch
 
     def args(self, M):
         return self.x[:M], self.w1, self.w2, self.out[:M]
@@ -313,7 +327,7 @@ def best_stream_ordered(runner, M, stream, reps):
 LAYER_MS = (16, 256, 2048)
 
 
-def layers_sweep(w, L, Ms, reps, stream):
+def layers_sweep(w, L, Ms, reps, stream, ld):
     """A chain of L MLP layers of the workload's shapes (own seeded weights
     per layer) at each M: the fused policies' single persistent kernel
     against the 2L stream-ordered kernels, event medians (hot).  The fused
@@ -321,10 +335,12 @@ def layers_sweep(w, L, Ms, reps, stream):
     import torch
     from consumer_gemm_chain_amd import gen
     from consumer_gemm_chain_amd.mlp_chain import MlpChain
-    from consumer_gemm_chain_amd.tensors import to_dev
+    from consumer_gemm_chain_amd.tensors import to_dev, to_dev_rows
     g = 2 if w.act == "swiglu" else 1
-    w1s = [to_dev(gen.normal_bits((w.H, g * w.I), 9000 + 10 * l, w.w_scale, w.dtype), w.dtype) for l in range(L)]
-    w2s = [to_dev(gen.normal_bits((w.I, w.H), 9001 + 10 * l, w.w_scale, w.dtype), w.dtype) for l in range(L)]
+    w1s = [to_dev_rows(gen.normal_bits((w.H, g * w.I), 9000 + 10 * l, w.w_scale, w.dtype), w.dtype, ld[0])
+           for l in range(L)]
+    w2s = [to_dev_rows(gen.normal_bits((w.I, w.H), 9001 + 10 * l, w.w_scale, w.dtype), w.dtype, ld[1])
+           for l in range(L)]
     xs = to_dev(gen.x_rows(w, max(Ms)), w.dtype)
     out = torch.empty((max(Ms), w.H), dtype=xs.dtype, device="cuda")
     rows = []
@@ -332,6 +348,7 @@ def layers_sweep(w, L, Ms, reps, stream):
         t = {}
         for pol in POLICIES:
             with MlpChain(M, w.H, w.I, w.act, w.dtype, pol, layers=L) as ch:
+                ch.set_weight_ld(*ld)
                 for _ in range(3):
                     ch.run_layers(xs[:M], w1s, w2s, out[:M])
                 torch.cuda.synchronize()
@@ -497,6 +514,8 @@ def main():
                     help="seconds of oracle work the CPU baseline aims at (bounded sample of rows)")
     ap.add_argument("--kernels-only", action="store_true",
                     help="only the headline policy and the planned stream-ordered pair (profiler runs)")
+    ap.add_argument("--dense-weights", action="store_true",
+                    help="weights in dense rows instead of the library's preferred padded row strides")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only a device copy of this many MiB, three times (counter calibration)")
     args = ap.parse_args()
@@ -520,7 +539,7 @@ def main():
     M = args.M
     quick = args.kernels_only
     sweep_Ms = [m for m in w.Ms if m <= M] if not (args.no_sweep or quick) else []
-    runner = Runner(w, max(M, max(sweep_Ms) if sweep_Ms else M))
+    runner = Runner(w, max(M, max(sweep_Ms) if sweep_Ms else M), args.dense_weights)
     stream = torch.cuda.current_stream()
     hargs = runner.args(M)
     x, w1, w2, out = hargs
@@ -587,7 +606,7 @@ def main():
         "config": {"workload": w.name, "M": M, "H": w.H, "I": w.I, "act": w.act, "policy": args.policy,
                    "tile": [info["BM"], info["BN1"], info["BK"]], "tiles": [info["T1"], info["T2"]],
                    "tile_config": info["config"], "split": [info["S1"], info["S2"]],
-                   "grid": info["grid"], "parallelism": "single GPU"},
+                   "grid": info["grid"], "weight_ld": list(runner.ld), "parallelism": "single GPU"},
         "stream_ordered": {"value": round(so_tflops, 2), "ms_per_step": round(wall_so / args.steps * 1e3, 4),
                            "kernel_pair_us": round(float(np.mean(kern_so)), 2),
                            "plan": [so_info["config"], so_info["S1"], so_info["S2"]],
@@ -628,7 +647,7 @@ def main():
             del runner
             torch.cuda.empty_cache()
             ws = gen.WORKLOADS[wl]
-            runner = Runner(ws, ws.max_M)
+            runner = Runner(ws, ws.max_M, args.dense_weights)
             rows += sweep(runner, list(ws.Ms), args.sweep_reps, stream, flush_buf)
     del flush_buf
 
@@ -639,7 +658,8 @@ def main():
         line["layers"] = {"workload": w.name, "layers": args.layers,
                           "columns": ["M", "tile_sync_us", "row_sync_us", "stream_ordered_us",
                                       "speedup_vs_stream_ordered", "tile_sync_tflops"],
-                          "rows": layers_sweep(w, args.layers, layer_Ms, args.sweep_reps, stream)}
+                          "rows": layers_sweep(w, args.layers, layer_Ms, args.sweep_reps, stream,
+                                               weight_strides(w, args.dense_weights))}
 
     if rows:
         line["sweep_columns"] = list(SUMMARY_COLUMNS)

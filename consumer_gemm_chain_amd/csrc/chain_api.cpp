@@ -95,6 +95,7 @@ struct mlp_chain {
     float* part1;
     float* part2;
     // run state
+    int64_t ldw1, ldw2;         // weight row strides (elements)
     uint32_t spin_limit;
     uint32_t skip_producer;
     uint64_t* trace;            // caller's timeline buffer (debug), or nullptr
@@ -538,6 +539,8 @@ mlpc::ChainArgs make_args(const mlp_chain* h, const void* x, const void* w1, con
     a.trace = h->trace;
     a.ldx = (int)h->H;
     a.ldo = (int)h->H;
+    a.ldw1 = (int)h->ldw1;
+    a.ldw2 = (int)h->ldw2;
     a.layers = h->layers;
     a.ldy = (int)h->ldy;
     a.ys = h->ys;
@@ -555,6 +558,8 @@ void init_handle(mlp_chain* h, int64_t M, int64_t H, int64_t I, int act, int dty
     h->I = I;
     h->ldt = (I + 63) / 64 * 64;
     h->ldy = (H + 63) / 64 * 64;
+    h->ldw1 = (act == MLP_ACT_SWIGLU ? 2 : 1) * I;
+    h->ldw2 = H;
     h->layers = (uint32_t)layers;
     h->ys = nullptr;
     h->act = act;
@@ -788,6 +793,31 @@ int mlp_chain_status(mlp_chain_t h) {
         if (rc != MLP_OK) return rc;
         return fail(MLP_ETIMEOUT, "a consumer tile gave up waiting for its producer (watchdog)");
     }
+    return MLP_OK;
+}
+
+int mlp_chain_weight_ld(int64_t H, int64_t I, int act, int64_t* ldw1, int64_t* ldw2) {
+    if (!ldw1 || !ldw2) return fail(MLP_EINVAL, "mlp_chain_weight_ld needs two output slots");
+    if (H < 8 || I < 8 || H % 8 || I % 8 || act < MLP_ACT_NONE || act > MLP_ACT_SWIGLU)
+        return fail(MLP_EINVAL, "bad sizes H=%lld I=%lld or act %d", (long long)H, (long long)I, act);
+    // the next stride that is an odd number of 128-byte lines (64 mod 128
+    // elements): consecutive rows of a column panel then cycle through all
+    // eight classes of lines ((address / 128) mod 8)
+    auto odd_lines = [](int64_t n) { return n + ((64 - n % 128) + 128) % 128; };
+    *ldw1 = odd_lines((act == MLP_ACT_SWIGLU ? 2 : 1) * I);
+    *ldw2 = odd_lines(H);
+    return MLP_OK;
+}
+
+int mlp_chain_set_weight_ld(mlp_chain_t h, int64_t ldw1, int64_t ldw2) {
+    if (!h) return fail(MLP_EINVAL, "NULL handle");
+    const int64_t g = h->act == MLP_ACT_SWIGLU ? 2 : 1;
+    if (ldw1 < g * h->I || ldw2 < h->H || ldw1 % 8 || ldw2 % 8 || ldw1 > (1 << 24) || ldw2 > (1 << 24))
+        return fail(MLP_EINVAL, "weight row strides must be multiples of 8 elements, ldw1 >= %lld, ldw2 >= %lld "
+                    "and at most 2^24 (got %lld, %lld)", (long long)(g * h->I), (long long)h->H, (long long)ldw1,
+                    (long long)ldw2);
+    h->ldw1 = ldw1;
+    h->ldw2 = ldw2;
     return MLP_OK;
 }
 

@@ -105,6 +105,7 @@ struct ChainArgs {
     int policy;
     int ldx;                // row stride of x (GEMM1's A operand): H, or ldy for a later layer's input
     int ldo;                // row stride of y (GEMM2's output): H, or ldy for a layer's output kept for the next
+    int ldw1, ldw2;         // row strides of every layer's W1 (>= g I) and W2 (>= H), in elements
     // Chains of several MLP layers (layers > 1): layer l computes
     // Y_l = act(Y_{l-1} W1_l) W2_l with Y_{-1} = x; the fields above then
     // describe layer 0, and layer_args() derives any layer's view.
@@ -1287,7 +1288,7 @@ __device__ __forceinline__ TileJob producer_job(const ChainArgs& a, uint32_t mb,
     int ks0, ks1;
     part_range((a.H + BK - 1) / BK, s, a.ksp1, ks0, ks1);
     return TileJob{layer_input(a, l), l == 0 ? a.w1 : a.w1s[l], a.zero, l == 0 ? a.ldx : a.ldy, a.M,
-                   (int)mb * C::BM, (inter ? 2 : 1) * a.I, a.I, (int)nb * producer_width<C>(a), inter ? a.I : 0,
+                   (int)mb * C::BM, a.ldw1, a.I, (int)nb * producer_width<C>(a), inter ? a.I : 0,
                    a.H, ks0, ks1, inter};
 }
 
@@ -1296,7 +1297,7 @@ __device__ __forceinline__ TileJob consumer_job(const ChainArgs& a, uint32_t mb,
                                                 uint32_t l) {
     int ks0, ks1;
     part_range((a.I + BK - 1) / BK, s, a.ksp2, ks0, ks1);
-    return TileJob{layer_t(a, l), l == 0 ? a.w2 : a.w2s[l], a.zero, a.ldt, a.M, (int)mb * C::BM, a.H, a.H,
+    return TileJob{layer_t(a, l), l == 0 ? a.w2 : a.w2s[l], a.zero, a.ldt, a.M, (int)mb * C::BM, a.ldw2, a.H,
                    (int)nb * C::BN, 0, a.I, ks0, ks1, false};
 }
 

@@ -30,7 +30,7 @@ EXPORTS = ("mlp_chain_create", "mlp_chain_run", "mlp_chain_destroy", "mlp_chain_
            "mlp_chain_debug_set_config", "mlp_chain_debug_set_split", "mlp_chain_debug_set_grid",
            "mlp_chain_debug_set_order", "mlp_chain_debug_set_trace", "mlp_chain_debug_read_intermediate",
            "mlp_chain_run_noalloc", "mlp_chain_create_layers", "mlp_chain_run_layers", "mlp_chain_debug_litmus",
-           "mlp_chain_debug_set_epoch")
+           "mlp_chain_debug_set_epoch", "mlp_chain_set_weight_ld", "mlp_chain_weight_ld")
 
 INFO_FIELDS = ("BM", "BN1", "BN2", "BK", "Mt", "N1t", "N2t", "T1", "T2", "grid", "wg_per_cu",
                "threads", "cus", "epoch", "config", "workspace_bytes", "S1", "S2", "ksp1", "ksp2", "layers")
@@ -104,6 +104,10 @@ def _bind(path: str):
     lib.mlp_chain_debug_litmus.restype = ci
     lib.mlp_chain_debug_set_epoch.argtypes = [vp, u32]
     lib.mlp_chain_debug_set_epoch.restype = ci
+    lib.mlp_chain_set_weight_ld.argtypes = [vp, i64, i64]
+    lib.mlp_chain_set_weight_ld.restype = ci
+    lib.mlp_chain_weight_ld.argtypes = [i64, i64, ci, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.mlp_chain_weight_ld.restype = ci
     lib.mlp_chain_create_layers.argtypes = [i64, i64, i64, ci, ci, ci, ci]
     lib.mlp_chain_create_layers.restype = vp
     lib.mlp_chain_run_layers.argtypes = [vp, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp]
@@ -129,6 +133,16 @@ def mlp_chain_create(M: int, H: int, I: int, act: int, dtype: int, policy: int) 
     if not h:
         raise MlpChainError(MLP_EINVAL, mlp_chain_last_error())
     return h
+
+
+def mlp_chain_set_weight_ld(h: int, ldw1: int, ldw2: int) -> int:
+    return _check(load_library().mlp_chain_set_weight_ld(h, int(ldw1), int(ldw2)))
+
+
+def mlp_chain_weight_ld(H: int, I: int, act: int) -> tuple[int, int]:
+    a, b = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(load_library().mlp_chain_weight_ld(int(H), int(I), int(act), ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
 
 
 def mlp_chain_create_layers(M: int, H: int, I: int, act: int, dtype: int, policy: int, layers: int) -> int:
@@ -278,17 +292,25 @@ class MlpChain:
         import torch
         return int(torch.cuda.current_stream().cuda_stream)
 
+    def set_weight_ld(self, ldw1: int, ldw2: int):
+        """Row strides (elements) of the weights later runs read; weight
+        tensors are then 2-D views with those row strides."""
+        mlp_chain_set_weight_ld(self.h, ldw1, ldw2)
+        self.ld = {"w1": int(ldw1), "w2": int(ldw2)}
+
     def _shapes(self, x, w1, w2, out):
         g = 2 if self.act == "swiglu" else 1
         want = {"x": (self.M, self.H), "w1": (self.H, g * self.I), "w2": (self.I, self.H),
                 "out": (self.M, self.H)}
+        ld = getattr(self, "ld", {"w1": g * self.I, "w2": self.H})
         for name, t in (("x", x), ("w1", w1), ("w2", w2), ("out", out)):
             if t is None:
                 continue
             if tuple(t.shape) != want[name]:
                 raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want[name]}")
-            if not t.is_cuda or not t.is_contiguous() or t.element_size() != 2:
-                raise ValueError(f"{name} must be a contiguous 2-byte device tensor")
+            rows = (ld[name], 1) if name in ld else (want[name][1], 1)
+            if not t.is_cuda or tuple(t.stride()) != rows or t.element_size() != 2:
+                raise ValueError(f"{name} must be a 2-byte device tensor with row stride {rows[0]}")
 
     def run(self, x, w1, w2, out, stream=None):
         self._shapes(x, w1, w2, out)

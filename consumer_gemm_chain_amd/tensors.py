@@ -24,3 +24,17 @@ def from_dev(t) -> np.ndarray:
 def empty_dev(shape, dtype: str):
     import torch
     return torch.empty(shape, dtype=torch_dtype(dtype), device="cuda")
+
+
+def to_dev_rows(bits: np.ndarray, dtype: str, ld: int):
+    """A 2-D device tensor of `bits` whose rows lie `ld` elements apart (a
+    view into a zero-filled [rows, ld] allocation), for weights with padded
+    rows (mlp_chain_set_weight_ld)."""
+    import torch
+    rows, cols = bits.shape
+    if ld == cols:
+        return to_dev(bits, dtype)
+    base = torch.zeros((rows, ld), dtype=torch_dtype(dtype), device="cuda")
+    view = base[:, :cols]
+    view.copy_(to_dev(bits, dtype))
+    return view

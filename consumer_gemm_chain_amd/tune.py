@@ -86,6 +86,7 @@ def time_plan(dev, w, M, policy, cfg, split, reps, stream, flush=None):
     from consumer_gemm_chain_amd.mlp_chain import MlpChain
     x, w1, w2, out = dev
     with MlpChain(M, w.H, w.I, w.act, w.dtype, policy) as ch:
+        ch.set_weight_ld(w1.stride(0), w2.stride(0))
         ch.set_config(cfg)
         ch.set_split(*split)
         for _ in range(2):
@@ -152,9 +153,9 @@ def main():
 
     import torch
     from consumer_gemm_chain_amd import gen
-    from consumer_gemm_chain_amd.mlp_chain import load_library
-    from consumer_gemm_chain_amd.tensors import to_dev
-    load_library()
+    from consumer_gemm_chain_amd import mlp_chain as mc
+    from consumer_gemm_chain_amd.tensors import to_dev, to_dev_rows
+    mc.load_library()
     assert torch.cuda.is_available(), "the tuner measures on a GPU"
     props = torch.cuda.get_device_properties(0)
     cus = props.multi_processor_count
@@ -166,7 +167,9 @@ def main():
         w = gen.WORKLOADS[wl]
         w1, w2 = gen.weights(w)
         x = gen.x_rows(w, w.max_M)
-        dev = (to_dev(x, w.dtype), to_dev(w1, w.dtype), to_dev(w2, w.dtype),
+        # the weights in the row strides the library prefers (as the bench lays them out)
+        ld1, ld2 = mc.mlp_chain_weight_ld(w.H, w.I, mc.ACTS[w.act])
+        dev = (to_dev(x, w.dtype), to_dev_rows(w1, w.dtype, ld1), to_dev_rows(w2, w.dtype, ld2),
                torch.empty((w.max_M, w.H), dtype=torch.float16 if w.dtype == "f16" else torch.bfloat16,
                            device="cuda"))
         for M in w.Ms:

@@ -100,6 +100,27 @@ mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype
 int mlp_chain_run(mlp_chain_t h, const void* x, const void* w1, const void* w2, void* out,
                   void* hip_stream);
 
+/* Row strides (in elements) of the weights the handle's runs read: W1
+ * [H, g I] with rows ldw1 >= g I apart, W2 [I, H] with rows ldw2 >= H apart
+ * (g = 2 for SwiGLU, else 1; gate columns 0..I-1 and up columns I..2I-1 of a
+ * W1 row stay where mlp_chain_run describes them; the padding between rows
+ * is never read).  Both multiples of 8 and at most 2^24.  The default is
+ * dense rows (g I and H).  Applies to every later run of the handle, one
+ * layer or several (every layer's weights have these strides).  Returns
+ * MLP_EINVAL for a NULL handle or a stride outside those bounds.
+ * (No page defines a weight layout: this is a deployment choice the library
+ * offers because rows that are a whole number of kilobytes apart put every
+ * row of a column panel on the same class of 128-byte lines, which streams
+ * slower; see mlp_chain_weight_ld.) */
+int mlp_chain_set_weight_ld(mlp_chain_t h, int64_t ldw1, int64_t ldw2);
+
+/* The weight row strides this library streams fastest for these sizes: the
+ * smallest ldw1 >= g I and ldw2 >= H that are an odd number of 128-byte
+ * lines (64 mod 128 elements), so that consecutive rows of a column panel
+ * cycle through all eight classes of lines.  Host-only; returns MLP_EINVAL
+ * for NULL outputs or sizes mlp_chain_create would reject. */
+int mlp_chain_weight_ld(int64_t H, int64_t I, int act, int64_t* ldw1, int64_t* ldw2);
+
 /* A chain of `layers` MLP layers (1..8), 2 x layers dependent GEMMs:
  * layer l computes Y_l = act(Y_{l-1} W1_l) W2_l, with Y_{-1} = x and the last
  * layer's Y written to out; every layer has the sizes of mlp_chain_create

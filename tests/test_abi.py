@@ -59,6 +59,7 @@ def test_null_handle_entry_points():
     assert lib.mlp_chain_debug_set_split(None, 0, 0) == mc.MLP_EINVAL
     assert lib.mlp_chain_debug_set_grid(None, 0) == mc.MLP_EINVAL
     assert lib.mlp_chain_debug_set_order(None, 0) == mc.MLP_EINVAL
+    assert lib.mlp_chain_set_weight_ld(None, 4096, 4096) == mc.MLP_EINVAL
     arr = (ctypes.c_int64 * 16)()
     assert lib.mlp_chain_info(None, arr, 16) == mc.MLP_EINVAL
 
@@ -67,3 +68,27 @@ def test_binding_raises_with_message():
     with pytest.raises(mc.MlpChainError) as e:
         mc.mlp_chain_create(4, 512, 100, mc.MLP_ACT_GELU_TANH, mc.MLP_DTYPE_F16, mc.MLP_POLICY_TILE_SYNC)
     assert "multiples of 8" in str(e.value)
+
+
+@pytest.mark.parametrize("H,I,act", [(12288, 6144, "gelu_tanh"), (8192, 2752, "swiglu"), (8192, 3584, "swiglu"),
+                                     (8192, 8192, "none"), (512, 2048, "gelu_tanh"), (200, 328, "swiglu"),
+                                     (64, 64, "none")])
+def test_preferred_weight_strides_cycle_line_classes(H, I, act):
+    """mlp_chain_weight_ld (host only): the smallest row strides at least as
+    wide as the rows whose byte length is an odd number of 128-byte lines,
+    so the rows of a column panel visit all eight line classes."""
+    g = 2 if act == "swiglu" else 1
+    ld1, ld2 = mc.mlp_chain_weight_ld(H, I, mc.ACTS[act])
+    for ld, n in ((ld1, g * I), (ld2, H)):
+        assert n <= ld < n + 128 and ld % 8 == 0
+        assert (ld * 2) % 256 == 128                      # odd number of 128-byte lines
+        assert sorted({(r * ld * 2 // 128) % 8 for r in range(8)}) == list(range(8))
+        assert all((m * 2) % 256 != 128 for m in range(n, ld, 8))   # the smallest such stride
+
+
+def test_preferred_weight_strides_reject_bad_sizes():
+    lib = mc.load_library()
+    a, b = ctypes.c_int64(0), ctypes.c_int64(0)
+    assert lib.mlp_chain_weight_ld(500, 512, 1, ctypes.byref(a), ctypes.byref(b)) == mc.MLP_EINVAL
+    assert lib.mlp_chain_weight_ld(512, 512, 3, ctypes.byref(a), ctypes.byref(b)) == mc.MLP_EINVAL
+    assert lib.mlp_chain_weight_ld(512, 512, 1, None, ctypes.byref(b)) == mc.MLP_EINVAL
