@@ -152,6 +152,8 @@ def main():
     header = (f"workload: {w.name} (H={w.H}, I={w.I}, {w.act}, {w.dtype}), M={args.M}\n"
               f"policy: {args.policy}, tile {cfgd['tile']}, {plan}; planned stream-ordered pair: "
               f"config {so_plan[0]} split {so_plan[1]},{so_plan[2]}\n"
+              f"weights: rows {cfgd.get('weight_ld', ['dense', 'dense'])[0]} (W1) and "
+              f"{cfgd.get('weight_ld', ['dense', 'dense'])[1]} (W2) elements apart\n"
               f"sources: {sources}\n")
 
     # ---- trace
