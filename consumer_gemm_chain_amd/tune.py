@@ -48,7 +48,7 @@ def log(msg):
 
 def candidate_configs(M):
     if M <= 16:
-        return (0, 4)
+        return (0, 4, 9)
     if M <= 128:
         return (0, 4, 3)
     if M <= 512:

@@ -25,7 +25,7 @@ def _case(M, H, I, act, dtype, seed):
 
 @pytest.mark.parametrize("act", ACTS)
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 7, 8])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 7, 8, 9])
 def test_small_all_policies_match_oracle(oracle_mod, act, dtype, cfg):
     # several tiles in M, N1, N2 and K for every config, ragged everywhere
     M, H, I = 200, 328, 456
