@@ -199,23 +199,30 @@ FULL = [(1, 1), (1, 16), (1, 64), (1, 256), (1, 512), (1, 1024), (1, 2048),
 
 @pytest.mark.parametrize("wl,M", FULL)
 def test_full_size_workloads(oracle_mod, wl, M):
-    """Full-size workloads in the planner's launch configuration: the three
-    policies agree bit for bit on the whole output, and sampled rows agree
-    with the oracle within tolerance.  Each fused handle first runs once on a
-    decoy input (X with its rows reversed), so a consumer that read a stale
-    intermediate would read the decoy's and differ."""
+    """Full-size workloads in the launch configuration the bench times (the
+    planner's plan, the weights in the library's preferred row strides): the
+    three policies agree bit for bit on the whole output, and with the
+    stream-ordered pair on dense weights; sampled rows agree with the oracle
+    within tolerance.  Each fused handle first runs once on a decoy input (X
+    with its rows reversed), so a consumer that read a stale intermediate
+    would read the decoy's and differ."""
     import torch
+    from consumer_gemm_chain_amd import mlp_chain as mc
     from consumer_gemm_chain_amd.mlp_chain import MlpChain
+    from consumer_gemm_chain_amd.tensors import to_dev_rows
     from tests._helpers import empty_dev, from_dev
     w = gen.WORKLOADS[wl]
     print(f"workload {w.name} M={M}", flush=True)
     w1, w2 = gen.weights(w)
     x = gen.x_rows(w, M)
-    dx, dw1, dw2 = to_dev(x, w.dtype), to_dev(w1, w.dtype), to_dev(w2, w.dtype)
+    ld = mc.mlp_chain_weight_ld(w.H, w.I, mc.ACTS[w.act])
+    dx = to_dev(x, w.dtype)
+    dw1, dw2 = to_dev_rows(w1, w.dtype, ld[0]), to_dev_rows(w2, w.dtype, ld[1])
     decoy = torch.flip(dx, dims=[0]).contiguous() if M > 1 else torch.zeros_like(dx)
     outs = {}
     for pol in POLICIES:
         with MlpChain(M, w.H, w.I, w.act, w.dtype, pol) as ch:
+            ch.set_weight_ld(*ld)
             out = empty_dev((M, w.H), w.dtype)
             ch.run(decoy, dw1, dw2, out)
             out.fill_(float("nan"))
@@ -223,10 +230,20 @@ def test_full_size_workloads(oracle_mod, wl, M):
             torch.cuda.synchronize()
             assert ch.status() == 0
             outs[pol] = from_dev(out)
+    del dw1, dw2
+    torch.cuda.empty_cache()
+    dw1, dw2 = to_dev(w1, w.dtype), to_dev(w2, w.dtype)
+    with MlpChain(M, w.H, w.I, w.act, w.dtype, "stream_ordered") as ch:
+        out = empty_dev((M, w.H), w.dtype)
+        ch.run(dx, dw1, dw2, out)
+        torch.cuda.synchronize()
+        assert ch.status() == 0
+        outs["dense"] = from_dev(out)
     del dx, dw1, dw2, decoy
     torch.cuda.empty_cache()
     assert np.array_equal(outs["row_sync"], outs["stream_ordered"])
     assert np.array_equal(outs["tile_sync"], outs["stream_ordered"])
+    assert np.array_equal(outs["dense"], outs["stream_ordered"])
     rows = _sample_rows(M, k=6 if wl != 4 else 32, seed=wl * 10000 + M)
     y_ref = oracle_mod.mlp_chain(x[rows], w1, w2, w.act, w.dtype)
     check_against_oracle(outs["tile_sync"][rows], y_ref, w.dtype, f"{w.name} M={M}")
