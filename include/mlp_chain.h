@@ -96,6 +96,12 @@ mlp_chain_t mlp_chain_create(int64_t M, int64_t H, int64_t I, int act, int dtype
  * they may be captured into a HIP graph and replayed, every policy (the
  * same pointers each replay; replays and direct runs of one handle on one
  * stream may be mixed).
+ * The fused policies' persistent kernel sizes its grid to what the GPU holds
+ * at once and its waits end only once every workgroup is running: a kernel
+ * of another stream that keeps CUs occupied meanwhile can hold consumers in
+ * their waits until the watchdog gives up (MLP_ETIMEOUT, output undefined).
+ * Run the fused policies without concurrent kernels on the same GPU, or use
+ * stream_ordered there.
  * (CuSync README, opening and MLP paragraphs.) */
 int mlp_chain_run(mlp_chain_t h, const void* x, const void* w1, const void* w2, void* out,
                   void* hip_stream);
