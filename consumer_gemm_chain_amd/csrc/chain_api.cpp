@@ -384,17 +384,19 @@ int apply_plan(mlp_chain* h, int cfg) {
         if (occ < 1) return fail(MLP_EHIP, "persistent kernel of config %d does not fit on a CU", cfg);
         h->occ = occ;
         // Persistent workgroups: as many per CU as fit, but no more than the
-        // whole items per CU the run has.  When the run is under two items
-        // per CU (small M), one workgroup per CU runs a producer part and then
-        // a consumer part, so the consumers spread over the CUs the producers
-        // used instead of sharing the CUs their workgroups were placed on at
-        // launch.
-        const uint64_t parts = ((uint64_t)h->T1 * h->S1 + (uint64_t)h->T2 * h->S2) * h->layers;
-        uint64_t per_cu = parts / (uint64_t)h->cus;
+        // whole items per CU one layer has (the layers of a chain run one
+        // after another, so one layer's parts are what can run at once; extra
+        // workgroups would only sit on the next layer's items and wait).
+        // When a layer is under two items per CU (small M), one workgroup per
+        // CU runs a producer part and then a consumer part, so the consumers
+        // spread over the CUs the producers used instead of sharing the CUs
+        // their workgroups were placed on at launch.
+        const uint64_t layer_parts = (uint64_t)h->T1 * h->S1 + (uint64_t)h->T2 * h->S2;
+        uint64_t per_cu = layer_parts / (uint64_t)h->cus;
         if (per_cu < 1) per_cu = 1;
         if (per_cu > (uint64_t)occ) per_cu = (uint64_t)occ;
         uint64_t g = per_cu * (uint64_t)h->cus;
-        if (g > parts) g = parts;
+        if (g > layer_parts * h->layers) g = layer_parts * h->layers;
         // at least one workgroup per tile queue (the kernel's deadlock-freedom
         // argument needs an owner for every queue); extras exit at once
         if (g < 8) g = 8;

@@ -1,7 +1,7 @@
 """Per-shape plan tuner: measures tile configurations x K splits on the GPU
 and writes the table the planner reads (csrc/tuned_plans.inc).
 
-    python -m consumer_gemm_chain_amd.tune [--workloads 0,1,2,3,4] [--out PATH]
+    python -m consumer_gemm_chain_amd.tune [--workloads 0,1,2,3,4] [--M 1,16] [--out PATH]
 
 The pages' system tunes itself per GPU generation (FLUX summary card,
 Interesting ideas: auto-tuned kernels); here each benchmarked shape (the
@@ -148,8 +148,10 @@ def tune_shape(dev, w, M, stream, flush_buf, cus):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--workloads", default="0,1,2,3,4")
+    ap.add_argument("--M", default="", help="only these M of each workload (default: all of its M)")
     ap.add_argument("--out", default=OUT)
     args = ap.parse_args()
+    only_m = {int(v) for v in args.M.split(",") if v.strip()}
 
     import torch
     from consumer_gemm_chain_amd import gen
@@ -173,6 +175,8 @@ def main():
                torch.empty((w.max_M, w.H), dtype=torch.float16 if w.dtype == "f16" else torch.bfloat16,
                            device="cuda"))
         for M in w.Ms:
+            if only_m and M not in only_m:
+                continue
             entry, note = tune_shape(dev, w, M, stream, flush_buf, cus)
             lines.append(f"// {note}\nMLPC_TUNED({', '.join(str(v) for v in entry)})")
         del dev
