@@ -294,7 +294,7 @@ SO_SPLITS = tuple((s1, s2) for s1 in (1, 2, 3, 4) for s2 in (1, 2))
 
 def so_search_configs(M):
     """Tile configurations the best stream-ordered plan is searched over."""
-    return (0, 4, 9) if M <= 16 else (3, 4, 8) if M <= 256 else (3, 7, 8)
+    return (0, 4, 9) if M <= 16 else (3, 4, 8, 10) if M <= 256 else (3, 7, 8, 10) if M <= 512 else (3, 7, 8)
 
 
 def best_stream_ordered(runner, M, stream, reps):

@@ -14,7 +14,8 @@
     X(6, 128, 256, 2, 4, 3, 2, 64)   /* measurements: eight waves of 64x64, 128 x 256 */          \
     X(7, 256, 256, 2, 4, 2, 2, 64)   /* large M once these tiles fill the GPU: eight waves of 128x64 */ \
     X(8, 256, 256, 2, 4, 4, 2, 32)   /* 256 x 256 on a ring of four half slabs: three in flight */ \
-    X(9, 16, 128, 1, 2, 4, 1, 64)    /* M <= 16 SwiGLU: 64 output columns, whole 128-byte lines of T */
+    X(9, 16, 128, 1, 2, 4, 1, 64)    /* M <= 16 SwiGLU: 64 output columns, whole 128-byte lines of T */ \
+    X(10, 128, 128, 2, 4, 4, 1, 64)  /* mid M: eight waves of 64x32, four stages; a quarter of the partials of 256 x 128 */
 
 #define MLPC_COUNT_CFG(id, ...) +1
 constexpr int MLPC_NUM_CONFIGS = 0 MLPC_CONFIGS(MLPC_COUNT_CFG);

@@ -50,9 +50,9 @@ def candidate_configs(M):
     if M <= 16:
         return (0, 4, 9)
     if M <= 128:
-        return (0, 4, 3)
+        return (0, 4, 3, 10)
     if M <= 512:
-        return (4, 3, 8)
+        return (4, 3, 8, 10)
     return (3, 7, 8)
 
 

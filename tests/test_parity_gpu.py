@@ -25,7 +25,7 @@ def _case(M, H, I, act, dtype, seed):
 
 @pytest.mark.parametrize("act", ACTS)
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 7, 8, 9])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 7, 8, 9, 10])
 def test_small_all_policies_match_oracle(oracle_mod, act, dtype, cfg):
     # several tiles in M, N1, N2 and K for every config, ragged everywhere
     M, H, I = 200, 328, 456
@@ -93,7 +93,7 @@ def test_tiny_workload(oracle_mod):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 10])
 def test_exact_integer_pin_on_gpu(oracle_mod, dtype, cfg):
     """Integer inputs whose partial sums are exact in fp32 in any order (also
     inside the matrix cores): every policy, the oracle and exact int64
@@ -151,7 +151,7 @@ def test_linear_in_w2_on_gpu():
         assert np.array_equal(y4[normal], 4 * y1[normal])
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 10])
 def test_repeated_runs_alternating_inputs(cfg):
     """Race check: 40 back-to-back runs of each fused policy on one handle,
     alternating between two inputs, must each equal the stream-ordered output
