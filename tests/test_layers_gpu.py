@@ -190,3 +190,24 @@ def test_layers_entry_points_check_arguments():
         arr = (ctypes.c_void_p * 2)(p, None)
         assert lib.mlp_chain_run_layers(ch.h, p, arr, arr, p, s) == mc.MLP_EINVAL
         assert ch.info()["epoch"] == 0
+
+
+@pytest.mark.parametrize("M,L", [(16, 2), (16, 3), (2048, 2)])
+def test_layers_grid_counts_one_layers_parts(M, L):
+    """The layer-chain kernel launches as many workgroups per CU as one
+    layer's parts fill (layers run one after another), capped by the
+    occupancy, never more than all layers' parts, and at least one per XCD
+    queue; the one-layer handle of the same shape and occupancy gets the same
+    grid."""
+    H, I = 12288, 6144
+    for pol in ("row_sync", "tile_sync"):
+        with mc.MlpChain(M, H, I, "gelu_tanh", "f16", pol, layers=L) as ch, \
+                mc.MlpChain(M, H, I, "gelu_tanh", "f16", pol) as one:
+            info = ch.info()
+            parts = info["T1"] * info["S1"] + info["T2"] * info["S2"]
+            per_cu = min(max(parts // info["cus"], 1), info["wg_per_cu"])
+            want = max(8, min(per_cu * info["cus"], parts * L))
+            assert info["grid"] == want, (M, L, pol, info)
+            o = one.info()
+            if o["wg_per_cu"] == info["wg_per_cu"]:
+                assert o["grid"] == info["grid"], (M, L, pol)
