@@ -36,6 +36,8 @@ def _case(M, H, I, act, dtype, seed):
     (300, 1032, 776, "swiglu", "bf16", 0, None),     # 32-column producer tiles (agent-scope hand-off)
     (40, 2048, 1088, "gelu_tanh", "f16", 4, (3, 2)),
     (600, 1024, 1024, "none", "bf16", 7, (2, 1)),
+    (16, 2048, 1536, "gelu_tanh", "f16", 9, (4, 2)),
+    (256, 1024, 704, "swiglu", "f16", 10, (2, 1)),
 ])
 @pytest.mark.parametrize("policy", ["row_sync", "tile_sync"])
 def test_chaos_repeated_runs(chaos, M, H, I, act, dtype, cfg, split, policy):
